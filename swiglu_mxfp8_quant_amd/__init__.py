@@ -1,0 +1,298 @@
+"""Python binding of libmxq, the MI355X (gfx950) library for the fused
+row-scaled SwiGLU + MXFP8 quantization path and the grouped GEMM over experts.
+
+The functions named mxq_* mirror the C ABI in include/mxq.h one to one: they
+only marshal torch tensors (device memory) into pointers, leading dimensions
+and descriptor structs, and return the mxq_status.  Every computation runs in
+the HIP kernels of libmxq.so; nothing here computes on the host.
+
+The friendlier helpers (splits_to_offsets, swiglu_quantize_fwd, ...) allocate
+the outputs with torch and call the mxq_* functions; they raise MxqError on a
+non-zero status.
+
+Importing this package loads libmxq.so and fails loudly if it is missing (run
+`python -m swiglu_mxfp8_quant_amd.build`).  There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxq.so")
+
+MXQ_OK = 0
+STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_NULL", 2: "MXQ_ERR_SHAPE", 3: "MXQ_ERR_ALIGN",
+          4: "MXQ_ERR_OVERFLOW", 5: "MXQ_ERR_ALIAS", 6: "MXQ_ERR_UNSUPPORTED",
+          7: "MXQ_ERR_HIP", 8: "MXQ_ERR_WORKSPACE"}
+ROWWISE = 1
+COLWISE = 2
+ACT_SWIGLU = 0
+ACT_CLAMPED_SWIGLU = 1
+DTYPE_BF16 = 0
+DTYPE_MXFP8 = 1
+DTYPE_F32 = 2
+GEMM_NT = 0
+GEMM_NN = 1
+GEMM_TN = 2
+
+# every symbol include/mxq.h declares
+EXPORTS = [
+    "mxq_splits_to_offsets", "mxq_swiglu_quantize_fwd", "mxq_swiglu_quantize_bwd_workspace",
+    "mxq_swiglu_quantize_bwd", "mxq_quantize", "mxq_grouped_gemm_workspace", "mxq_grouped_gemm",
+    "mxq_status_string", "mxq_last_error_message", "mxq_version",
+]
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class mxq_act(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("limit", ctypes.c_float)]
+
+
+class mxq_groups(ctypes.Structure):
+    _fields_ = [("G", ctypes.c_int64), ("row_off", ctypes.c_void_p), ("block_off", ctypes.c_void_p)]
+
+
+class mxq_mx_out(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64)]
+
+
+class mxq_operand(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p), ("ld", ctypes.c_int64),
+                ("gstride", ctypes.c_int64), ("scales", ctypes.c_void_p),
+                ("ld_scales", ctypes.c_int64), ("scale_gstride", ctypes.c_int64)]
+
+
+class mxq_gemm_args(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("G", ctypes.c_int64), ("row_off", ctypes.c_void_p),
+                ("block_off", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("rows", ctypes.c_int64), ("A", mxq_operand),
+                ("B", mxq_operand), ("out_dtype", ctypes.c_int32), ("out", ctypes.c_void_p),
+                ("ld_out", ctypes.c_int64), ("out_gstride", ctypes.c_int64),
+                ("accumulate", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libmxq.so not built at {LIB_PATH}; run python -m swiglu_mxfp8_quant_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, U32, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32
+    sig = {
+        "mxq_splits_to_offsets": [P, I64, P, P, P, P],
+        "mxq_swiglu_quantize_fwd": [ctypes.POINTER(mxq_act), I64, I64, P, I64, P, I64, P,
+                                    ctypes.POINTER(mxq_groups), U32, ctypes.POINTER(mxq_mx_out),
+                                    ctypes.POINTER(mxq_mx_out), P],
+        "mxq_swiglu_quantize_bwd_workspace": [I64, I64, U32, ctypes.POINTER(ctypes.c_size_t)],
+        "mxq_swiglu_quantize_bwd": [ctypes.POINTER(mxq_act), I64, I64, P, I64, P, I64, P, I64, P,
+                                    ctypes.POINTER(mxq_groups), P, I64, P, I64, P, U32,
+                                    ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P,
+                                    ctypes.c_size_t, P],
+        "mxq_quantize": [I64, I64, P, I64, ctypes.POINTER(mxq_groups), U32,
+                         ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P],
+        "mxq_grouped_gemm_workspace": [ctypes.POINTER(mxq_gemm_args), ctypes.POINTER(ctypes.c_size_t)],
+        "mxq_grouped_gemm": [ctypes.POINTER(mxq_gemm_args), P, ctypes.c_size_t, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = I32
+    lib.mxq_status_string.argtypes = [I32]
+    lib.mxq_status_string.restype = ctypes.c_char_p
+    lib.mxq_last_error_message.argtypes = []
+    lib.mxq_last_error_message.restype = ctypes.c_char_p
+    lib.mxq_version.argtypes = []
+    lib.mxq_version.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def version() -> str:
+    return lib.mxq_version().decode()
+
+
+def last_error() -> str:
+    return lib.mxq_last_error_message().decode()
+
+
+def check(status: int) -> None:
+    if status != MXQ_OK:
+        raise MxqError(status, last_error())
+
+
+# ------------------------------------------------------------- marshalling ---
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t):
+    """Row pitch (elements) of a 2-D view with unit column stride."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D view with unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1] if t.stride(0) < t.shape[1] else t.stride(0)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+
+
+def make_act(kind=ACT_SWIGLU, limit=7.0):
+    return mxq_act(kind, limit)
+
+
+def make_groups(row_off=None, block_off=None):
+    if row_off is None:
+        return None
+    return mxq_groups(row_off.numel() - 1, row_off.data_ptr(),
+                      None if block_off is None else block_off.data_ptr())
+
+
+def make_mx_out(codes, scales):
+    if codes is None:
+        return None
+    return mxq_mx_out(codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales))
+
+
+def _byref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+# ------------------------------------------------------------ C-ABI mirror ---
+
+def mxq_splits_to_offsets(splits, row_off, block_off=None, err_flag=None, stream=None):
+    return lib.mxq_splits_to_offsets(_ptr(splits), splits.numel(), _ptr(row_off), _ptr(block_off),
+                                     _ptr(err_flag), _stream(stream))
+
+
+def mxq_swiglu_quantize_fwd(act, gate, up, row_scale, groups, dirs, row_out, col_out, stream=None):
+    M, K = gate.shape
+    return lib.mxq_swiglu_quantize_fwd(_byref(act), M, K, _ptr(gate), _ld(gate), _ptr(up), _ld(up),
+                                       _ptr(row_scale), _byref(groups), dirs, _byref(row_out),
+                                       _byref(col_out), _stream(stream))
+
+
+def mxq_swiglu_quantize_bwd_workspace(M, K, dirs):
+    n = ctypes.c_size_t(0)
+    check(lib.mxq_swiglu_quantize_bwd_workspace(M, K, dirs, ctypes.byref(n)))
+    return n.value
+
+
+def mxq_swiglu_quantize_bwd(act, grad, gate, up, row_scale, groups, dgate, dup, dscale, dirs,
+                            row_out, col_out, ws, stream=None):
+    M, K = gate.shape
+    return lib.mxq_swiglu_quantize_bwd(
+        _byref(act), M, K, _ptr(grad), _ld(grad), _ptr(gate), _ld(gate), _ptr(up), _ld(up),
+        _ptr(row_scale), _byref(groups), _ptr(dgate), _ld(dgate) if dgate is not None else 0,
+        _ptr(dup), _ld(dup) if dup is not None else 0, _ptr(dscale), dirs, _byref(row_out),
+        _byref(col_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream))
+
+
+def mxq_quantize(x, groups, dirs, row_out, col_out, stream=None):
+    M, K = x.shape
+    return lib.mxq_quantize(M, K, _ptr(x), _ld(x), _byref(groups), dirs, _byref(row_out),
+                            _byref(col_out), _stream(stream))
+
+
+def mxq_grouped_gemm_workspace(args):
+    n = ctypes.c_size_t(0)
+    check(lib.mxq_grouped_gemm_workspace(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def mxq_grouped_gemm(args, ws=None, stream=None):
+    return lib.mxq_grouped_gemm(ctypes.byref(args), _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+# ---------------------------------------------------------------- helpers ---
+
+def colwise_scale_rows_bound(M, G=0):
+    return (M + 31) // 32 + (G if G else 0)
+
+
+def splits_to_offsets(splits, stream=None):
+    """(row_off, block_off, err_flag) int64 / int32 device tensors."""
+    import torch
+    G = splits.numel()
+    row_off = torch.empty(G + 1, dtype=torch.int64, device=splits.device)
+    block_off = torch.empty(G + 1, dtype=torch.int64, device=splits.device)
+    err = torch.zeros(1, dtype=torch.int32, device=splits.device)
+    check(mxq_splits_to_offsets(splits, row_off, block_off, err, stream))
+    return row_off, block_off, err
+
+
+def _alloc_mx(M, K, dirs, n_col_blocks, device):
+    import torch
+    rc = torch.empty((M, K) if dirs & ROWWISE else (0, 0), dtype=torch.uint8, device=device)
+    rs = torch.empty((M, K // 32) if dirs & ROWWISE else (0, 0), dtype=torch.uint8, device=device)
+    cc = torch.empty((M, K) if dirs & COLWISE else (0, 0), dtype=torch.uint8, device=device)
+    cs = torch.empty((n_col_blocks, K) if dirs & COLWISE else (0, 0), dtype=torch.uint8, device=device)
+    return rc, cc, rs, cs
+
+
+def _outs(rc, cc, rs, cs, dirs):
+    return (make_mx_out(rc, rs) if dirs & ROWWISE else None,
+            make_mx_out(cc, cs) if dirs & COLWISE else None)
+
+
+def swiglu_quantize_fwd(gate, up, scale=None, rowwise=True, colwise=False, row_off=None,
+                        block_off=None, n_col_blocks=None, clamped=False, limit=7.0, stream=None):
+    """Returns (codes_row, codes_col, scales_row, scales_col); a disabled
+    direction comes back zero-sized.  With groups, n_col_blocks must be the
+    number of colwise scale rows (sum of ceil(split/32))."""
+    M, K = gate.shape
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if n_col_blocks is None:
+        n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, gate.device)
+    ro, co = _outs(rc, cc, rs, cs, dirs)
+    act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit)
+    check(mxq_swiglu_quantize_fwd(act, gate, up, scale, make_groups(row_off, block_off), dirs, ro, co, stream))
+    return rc, cc, rs, cs
+
+
+def quantize(x, rowwise=True, colwise=False, row_off=None, block_off=None, n_col_blocks=None, stream=None):
+    M, K = x.shape
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if n_col_blocks is None:
+        n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device)
+    ro, co = _outs(rc, cc, rs, cs, dirs)
+    check(mxq_quantize(x, make_groups(row_off, block_off), dirs, ro, co, stream))
+    return rc, cc, rs, cs
+
+
+def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False, row_off=None,
+                        block_off=None, n_col_blocks=None, clamped=False, limit=7.0, dense=True,
+                        want_dscale=True, stream=None):
+    """Returns (codes_row, codes_col, scales_row, scales_col, dgate_dup, dscale)
+    where the codes cover the (M, 2K) [dgate | dup] matrix and dgate_dup is the
+    packed (M, 2K) bf16 gradient (None when dense=False)."""
+    import torch
+    M, K = gate.shape
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if n_col_blocks is None:
+        n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
+    rc, cc, rs, cs = _alloc_mx(M, 2 * K, dirs, n_col_blocks, gate.device)
+    ro, co = _outs(rc, cc, rs, cs, dirs)
+    dd = torch.empty((M, 2 * K), dtype=torch.bfloat16, device=gate.device) if dense else None
+    ds = torch.empty(M, dtype=torch.float32, device=gate.device) if want_dscale else None
+    nws = mxq_swiglu_quantize_bwd_workspace(M, K, dirs)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=gate.device) if (want_dscale and nws) else None
+    act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit)
+    check(mxq_swiglu_quantize_bwd(act, grad, gate, up, scale, make_groups(row_off, block_off),
+                                  dd[:, :K] if dense else None, dd[:, K:] if dense else None, ds,
+                                  dirs, ro, co, ws, stream))
+    return rc, cc, rs, cs, dd, ds

@@ -1,0 +1,989 @@
+// act_quant.hip -- fused row-scaled SwiGLU + MXFP8 block quantization on gfx950:
+// forward, backward (dgate, dup, dscale and the quantized [dgate | dup]) and the
+// plain quantizer (identity activation).
+//
+// Pages (cited by title; each defines what is computed here):
+//   TAO4743 "[mxfp8 training] Add a fused gated-activation (SwiGLU) + MXFP8
+//           quantization kernel": Summary (gate/up read once, the bf16
+//           activation never stored, 1x32 and/or 32x1 RCEIL scales from one
+//           pass), API (packed [gate | up], backward returns [dGate | dUp]),
+//           Numerics and tests (bitwise match with the unfused definition).
+//   TE3238  "Activation + GroupedLinear Fusion for MOE and other MOE
+//           optimizations": Greptile Summary (per-row-scaled SwiGLU and
+//           ClampedSwiGLU; gradient of the scales).
+//   VEO1340 ByteDance-Seed/VeOmni pull 1340, "What does this PR do?": SiLU is
+//           rounded to the activation dtype before it multiplies up.
+//
+// Design (MI355X-first; the pages' CuTe DSL kernel for GB200 is prior art only):
+//   * A workgroup owns one row tile (a colwise 32-row block, restarting at
+//     every group, or 8 rows for rowwise-only work) and a slab of columns;
+//     each lane owns CPT (8 or 4) consecutive columns and walks the tile's
+//     rows with 16-byte (8-byte) coalesced loads of gate and up.
+//   * Colwise: the lane keeps its CPT x 32 bf16 results in registers, so the
+//     32x1 amax needs neither a second HBM pass nor an LDS round trip.
+//     Rowwise: the 1x32 amax is a DPP max over the 4 (8) lanes of the block.
+//   * amax is an integer max of |bf16| bit patterns (NaN/Inf patterns sort
+//     above every finite value), the scale byte comes straight from the amax
+//     exponent bits, and gfx950's v_cvt_scalef32_pk_fp8_bf16 converts bf16
+//     pairs to E4M3 with the block scale (exact RNE, probed over all bf16
+//     inputs and scale bytes).
+//   * Exactness: SiLU runs on v_exp_f32 / v_rcp_f32; an element whose fp32
+//     result lies within a proven error margin of a bf16 rounding tie (or is
+//     out of the range where the margin was proven) is recomputed in fp64 the
+//     way the definition reads, so results match the exact definition except
+//     within ~1e-15 of a tie.
+#include "mxq_internal.h"
+
+#include <math.h>
+
+namespace mxq {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// fp32 classes {-normal, -zero, +zero, +normal} for v_cmp_class_f32
+constexpr int kNormalOrZero = 0x168;
+
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2_t v;
+    v.x = (__bf16)lo;
+    v.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint32_t umax16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                  __builtin_bit_cast(u16x2_t, b)));
+}
+
+// ------------------------------------------------------------------ fp64 path
+//
+// Used only for the rare elements whose fast fp32 result might round to a
+// different bf16 than the exact value (see silu_risky / product_risky /
+// near_tie below).  Evaluated in the order the definition reads, in fp64.
+
+// double -> bf16 bits, round to nearest even: round to odd into fp32 (24 bits >=
+// 8 + 2, so the second rounding is innocuous), then RNE to bf16.
+__device__ __forceinline__ uint32_t bf16_from_f64(double d) {
+    float f = (float)d;
+    uint32_t b = __float_as_uint(f);
+    if (d != d) return ((b >> 16) & 0x8000u) | 0x7FC0u;
+    if ((double)f != d) {
+        if (fabs((double)f) > fabs(d)) b -= 1u;
+        b |= 1u;
+    }
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ double sigmoid_f64(double g) { return 1.0 / (1.0 + exp(-g)); }
+
+// ------------------------------------------------------------------ fast path
+
+__device__ __forceinline__ float clamp_gate(float g, float L) { return g > L ? L : g; }
+__device__ __forceinline__ float clamp_up(float u, float L) { return u > L ? L : (u < -L ? -L : u); }
+
+// sigma(g) and its complement factor e = e^-g (1 - sigma = e * sigma)
+struct Sig {
+    float e, sig;
+};
+__device__ __forceinline__ Sig sig_fast(float g) {
+    Sig r;
+    r.e = __builtin_amdgcn_exp2f(g * -kLog2e);
+    r.sig = __builtin_amdgcn_rcpf(1.0f + r.e);
+    return r;
+}
+
+// May the fast fp32 silu t of g round to bf16 differently from the exact
+// silu?  For -80 <= g the fast silu's error is below 8 + |g| fp32 ulps (checked
+// over every bf16 g); the margin min(8 + 2|g|, 168) ulps keeps a factor ~2.
+// Outside that range (g < -80, where e^-g overflows, and 0 < |g| < 2^-118,
+// where silu is subnormal-tiny) the element always takes the exact path; for
+// g > 80 the fast value is g itself, which is also the correctly rounded one.
+__device__ __forceinline__ bool silu_risky(float g, float t) {
+    const uint32_t ag = __float_as_uint(g) & 0x7FFFFFFFu;
+    const bool out = (g < -80.0f) || (ag - 1u < 0x04800000u - 1u);
+    const float margin = fminf(fmaf(2.0f, fabsf(g), 8.0f), 168.0f);
+    const int d = (int)(__float_as_uint(t) & 0xFFFFu) - 0x8000;
+    return out || (float)abs(d) <= margin;
+}
+
+// May bf16(hs), hs = fl32(p * s) with p exact, differ from the bf16 rounding of
+// the exact product?  Only if hs sits exactly on a bf16 tie, or p / hs are not
+// normal-or-zero (underflow, overflow, NaN/Inf inputs).
+__device__ __forceinline__ bool product_risky(float p, float hs) {
+    const bool tie = (__float_as_uint(hs) & 0xFFFFu) == 0x8000u;
+    return tie || !__builtin_amdgcn_class(p, kNormalOrZero) || !__builtin_amdgcn_class(hs, kNormalOrZero);
+}
+
+// ------------------------------------------------------------------ quantizer
+
+// E8M0 byte from the largest |bf16| bit pattern m of a block (RCEIL).
+__device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t m) {
+    const int e = (int)((m + 0x1Fu) >> 7) - 8;  // mantissa > 0x60 (i.e. > 1.75) rounds the exponent up
+    return m >= 0x7F80u ? 0xFFu : (e < 0 ? 0u : (uint32_t)e);
+}
+
+__device__ __forceinline__ float scale_operand(uint32_t E) { return __uint_as_float(E << 23); }
+
+// Four bf16 (two packed words) -> four E4M3 codes with one block scale.
+__device__ __forceinline__ uint32_t cvt4_same(uint32_t h01, uint32_t h23, uint32_t E) {
+    const float s = scale_operand(E);
+    short2_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, h01), s, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, h23), s, true);
+    const uint32_t c = __builtin_bit_cast(uint32_t, r);
+    return E == 0xFFu ? 0x7F7F7F7Fu : c;
+}
+
+// Four bf16 of four different columns -> four codes, one scale per column.
+__device__ __forceinline__ uint32_t cvt4_cols(uint32_t h01, uint32_t h23, const float *s,
+                                              uint32_t nanmask) {
+    short2_t x = {0, 0}, y = {0, 0};
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(x, __builtin_bit_cast(bf16x2_t, h01), s[0], false);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(x, __builtin_bit_cast(bf16x2_t, h23), s[2], true);
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(y, __builtin_bit_cast(bf16x2_t, h01), s[1], false);
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(y, __builtin_bit_cast(bf16x2_t, h23), s[3], true);
+    const uint32_t c = (__builtin_bit_cast(uint32_t, y) & 0xFF00FF00u) |
+                       (__builtin_bit_cast(uint32_t, x) & 0x00FF00FFu);
+    return (c & ~nanmask) | (0x7F7F7F7Fu & nanmask);
+}
+
+// max over the LPB lanes that share a 1x32 block (LPB = 32 / CPT, aligned groups)
+template <int LPB>
+__device__ __forceinline__ uint32_t block_max(uint32_t m) {
+    m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, true));  // lane ^ 1
+    m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, true));  // lane ^ 2
+    // quads now hold their max; mirroring within each 8-lane half row pairs quad 0 with quad 1
+    if (LPB == 8) m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x141, 0xF, 0xF, true));
+    return m;
+}
+
+// ------------------------------------------------------------------ loads
+
+template <int CPT>
+struct Vec;
+template <>
+struct Vec<8> {
+    uint32_t w[4];
+};
+template <>
+struct Vec<4> {
+    uint32_t w[2];
+};
+
+template <int CPT>
+__device__ __forceinline__ Vec<CPT> load_vec(const uint16_t *p) {
+    Vec<CPT> v;
+    if constexpr (CPT == 8) {
+        const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+        v.w[0] = q.x; v.w[1] = q.y; v.w[2] = q.z; v.w[3] = q.w;
+    } else {
+        const u32x2_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+        v.w[0] = q.x; v.w[1] = q.y;
+    }
+    return v;
+}
+
+template <int CPT>
+__device__ __forceinline__ Vec<CPT> zero_vec() {
+    Vec<CPT> v;
+#pragma unroll
+    for (int k = 0; k < CPT / 2; k++) v.w[k] = 0u;
+    return v;
+}
+
+// CPT/4 code dwords -> memory
+template <int CPT>
+__device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t *c) {
+    if constexpr (CPT == 8) *reinterpret_cast<uint2 *>(p) = make_uint2(c[0], c[1]);
+    else *reinterpret_cast<uint32_t *>(p) = c[0];
+}
+
+template <int CPT>
+__device__ __forceinline__ void store_bf16(uint16_t *p, const uint32_t *w) {
+    if constexpr (CPT == 8) *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    else *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+}
+
+// ------------------------------------------------------------------ tiles
+
+struct Tile {
+    int64_t r0;    // first row
+    int n;         // rows present (0 => nothing to do)
+    int64_t srow;  // colwise scale row
+};
+
+// Row tile `t`: with groups, colwise tile t is global 32-row block t, found by a
+// binary search of block_off (uniform, scalar loads); otherwise rows t*ROWS...
+template <int ROWS>
+__device__ __forceinline__ Tile tile_rows(int64_t t, int64_t M, const Groups &gr, bool grouped) {
+    Tile T;
+    T.srow = t;
+    if (!grouped) {
+        T.r0 = t * ROWS;
+        const int64_t rem = M - T.r0;
+        T.n = rem <= 0 ? 0 : (rem < ROWS ? (int)rem : ROWS);
+        return T;
+    }
+    T.n = 0;
+    T.r0 = 0;
+    const int64_t G = gr.G;
+    if (t >= gr.block_off[G] || t < 0) return T;
+    int64_t lo = 0, hi = G;  // largest g with block_off[g] <= t
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (gr.block_off[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    const int64_t r0 = gr.row_off[lo] + (t - gr.block_off[lo]) * 32;
+    int64_t end = gr.row_off[lo + 1];
+    if (end > M) end = M;
+    const int64_t rem = end - r0;
+    if (r0 < 0 || rem <= 0) return T;
+    T.r0 = r0;
+    T.n = rem < 32 ? (int)rem : 32;
+    return T;
+}
+
+// ------------------------------------------------------------------ fix-up queue
+//
+// Pass 1 of every kernel below computes a whole row tile on the fast path and
+// marks the elements that need the exact path in a per-lane bit mask (bit
+// i * CPT + k for row i, column k).  The fix-up then walks the set bits in
+// order, kFixQ at a time: it records their indices in a per-lane LDS queue,
+// recomputes each one in fp64 (one copy of that code per kernel, in a rolled
+// loop, re-reading the element's inputs from memory), and merges the results
+// back into the register tile with a static pass over the tile.
+
+constexpr int kFixQ = 4;
+
+template <int ROWS, int CPT>
+constexpr int risk_words() { return (ROWS * CPT + 31) / 32; }
+
+template <int CPT>
+__device__ __forceinline__ uint32_t row_bits(const uint32_t *risk, int i) {
+    return (risk[(i * CPT) / 32] >> ((i * CPT) % 32)) & ((1u << CPT) - 1u);
+}
+
+// Gather the element indices of the set bits of rank [base, base + kFixQ).
+template <int NW>
+__device__ __forceinline__ int fix_gather(const uint32_t *risk, int base, uint32_t *q) {
+    int rank = 0, nq = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        uint32_t bits = risk[w];
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            if (rank >= base && nq < kFixQ) q[nq++] = (uint32_t)(w * 32 + b);
+            rank++;
+        }
+    }
+    return nq;
+}
+
+__device__ __forceinline__ uint32_t set_half(uint32_t w, int hi, uint32_t v) {
+    return hi ? ((w & 0x0000FFFFu) | (v << 16)) : ((w & 0xFFFF0000u) | v);
+}
+
+__device__ __forceinline__ float bf16_at(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+
+// ------------------------------------------------------------------ forward
+
+// One element pair of the forward: packed gate / up words -> packed h word.
+// Returns a 2-bit mask of the elements that need the exact path.
+template <int ACT>
+__device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, float L, uint32_t &hw) {
+    if constexpr (ACT == ACT_IDENTITY) {
+        hw = gw;
+        return 0u;
+    } else {
+        float g0 = lo_f(gw), g1 = hi_f(gw), u0 = lo_f(uw), u1 = hi_f(uw);
+        if constexpr (ACT == ACT_CLAMPED) {
+            g0 = clamp_gate(g0, L); g1 = clamp_gate(g1, L);
+            u0 = clamp_up(u0, L);   u1 = clamp_up(u1, L);
+        }
+        const Sig s0 = sig_fast(g0), s1 = sig_fast(g1);
+        const float t0 = g0 * s0.sig, t1 = g1 * s1.sig;
+        const uint32_t aw = pack_bf16(t0, t1);
+        const float p0 = lo_f(aw) * u0, p1 = hi_f(aw) * u1;
+        const float h0 = p0 * s, h1 = p1 * s;
+        hw = pack_bf16(h0, h1);
+        uint32_t risky = 0u;
+        if (silu_risky(g0, t0) || product_risky(p0, h0)) risky |= 1u;
+        if (silu_risky(g1, t1) || product_risky(p1, h1)) risky |= 2u;
+        return risky;
+    }
+}
+
+// h = bf16( bf16(silu(g)) * u * s ) in fp64 (the product is exact in fp64)
+__device__ __forceinline__ uint32_t fwd_elem_f64(float g, float u, float s, float L, int act) {
+    if (act == ACT_CLAMPED) {
+        g = clamp_gate(g, L);
+        u = clamp_up(u, L);
+    }
+    const double gd = (double)g;
+    const float a = __uint_as_float(bf16_from_f64(gd * sigmoid_f64(gd)) << 16);
+    return bf16_from_f64((double)a * (double)u * (double)s);
+}
+
+template <int ACT, int CPT, int ROWS>
+__device__ __forceinline__ void fwd_fix(const FwdArgs &a, const Tile &T, int c0,
+                                        const uint32_t *risk, uint32_t (&h)[ROWS][CPT / 2], uint32_t *q) {
+    constexpr int NW = risk_words<ROWS, CPT>();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) total += __builtin_popcount(risk[w]);
+    for (int base = 0; base < total; base += kFixQ) {
+        const int nq = fix_gather<NW>(risk, base, q);
+#pragma unroll 1
+        for (int j = 0; j < nq; j++) {
+            const int idx = (int)q[j];
+            const int64_t r = T.r0 + idx / CPT, c = c0 + idx % CPT;
+            const float g = bf16_at(a.gate + r * a.ld_gate + c);
+            const float u = bf16_at(a.up + r * a.ld_up + c);
+            const float s = a.row_scale != nullptr ? a.row_scale[r] : 1.0f;
+            q[j] = fwd_elem_f64(g, u, s, a.limit, ACT);
+        }
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < ROWS; i++) {
+            const uint32_t rb = row_bits<CPT>(risk, i);
+            if (rb) {
+#pragma unroll
+                for (int k = 0; k < CPT; k++) {
+                    if (rb & (1u << k)) {
+                        if (rank >= base && rank < base + nq) h[i][k >> 1] = set_half(h[i][k >> 1], k & 1, q[rank - base]);
+                        rank++;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Is the row scale s safe for the fast product path (finite, normal or zero)?
+__device__ __forceinline__ bool scale_ok(float s) { return __builtin_amdgcn_class(s, kNormalOrZero); }
+
+template <int ACT, int DIRS, int CPT, int ROWS>
+__global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a, int64_t nslabs) {
+    constexpr int LPB = 32 / CPT;
+    constexpr int NW = risk_words<ROWS, CPT>();
+    constexpr int PF = 4;  // rows of loads kept in flight
+    __shared__ uint32_t fixq[256 * kFixQ];
+    const int64_t bid = blockIdx.x;
+    const int64_t t = bid / nslabs;
+    const int64_t slab = bid - t * nslabs;
+    const int tid = threadIdx.x;
+    const int co = (int)((slab * (int64_t)blockDim.x + tid) * CPT);  // this lane's first column (K < 2^30)
+    const bool active = co < a.K;
+    const Tile T = tile_rows<ROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
+    if (T.n == 0) return;  // uniform over the workgroup
+    // uniform row bases; lanes add their 32-bit column offset
+    const uint16_t *gate0 = a.gate + T.r0 * a.ld_gate;
+    const uint16_t *up0 = a.up + T.r0 * a.ld_up;
+
+    // pass 1: the tile on the fast path
+    uint32_t h[ROWS][CPT / 2];
+    uint32_t risk[NW];
+#pragma unroll
+    for (int w = 0; w < NW; w++) risk[w] = 0u;
+    Vec<CPT> gb[PF], ub[PF];
+#pragma unroll
+    for (int i = 0; i < PF; i++) {
+        gb[i] = zero_vec<CPT>();
+        ub[i] = zero_vec<CPT>();
+        if (i < ROWS && i < T.n && active) {
+            gb[i] = load_vec<CPT>(gate0 + i * a.ld_gate + co);
+            if constexpr (ACT != ACT_IDENTITY) ub[i] = load_vec<CPT>(up0 + i * a.ld_up + co);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < ROWS; i++) {
+        if (i < T.n) {
+            const Vec<CPT> gv = gb[i % PF], uv = ub[i % PF];
+            if (i + PF < ROWS && i + PF < T.n && active) {
+                gb[i % PF] = load_vec<CPT>(gate0 + (i + PF) * a.ld_gate + co);
+                if constexpr (ACT != ACT_IDENTITY) ub[i % PF] = load_vec<CPT>(up0 + (i + PF) * a.ld_up + co);
+            }
+            float s = 1.0f;
+            if constexpr (ACT != ACT_IDENTITY)
+                if (a.row_scale != nullptr) s = a.row_scale[T.r0 + i];
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int k = 0; k < CPT / 2; k++) bits |= fwd_pair<ACT>(gv.w[k], uv.w[k], s, a.limit, h[i][k]) << (2 * k);
+            if constexpr (ACT != ACT_IDENTITY) {
+                if (!scale_ok(s)) bits = (1u << CPT) - 1u;
+                if (!active) bits = 0u;
+                risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < CPT / 2; k++) h[i][k] = 0u;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // the rare exact-path elements
+    if constexpr (ACT != ACT_IDENTITY) fwd_fix<ACT, CPT, ROWS>(a, T, co, risk, h, fixq + tid * kFixQ);
+
+    // pass 2: rowwise outputs and column maxima (lanes past K hold zeros and
+    // form whole 32-column groups of their own, so they never mix in)
+    uint32_t colmax[CPT / 2];
+#pragma unroll
+    for (int k = 0; k < CPT / 2; k++) colmax[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < ROWS; i++) {
+        if (i < T.n) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int k = 0; k < CPT / 2; k++) {
+                const uint32_t mag = h[i][k] & 0x7FFF7FFFu;
+                if constexpr (DIRS & 2) colmax[k] = umax16x2(colmax[k], mag);
+                m = umax16x2(m, mag);
+            }
+            if constexpr (DIRS & 1) {
+                m = block_max<LPB>(max(m & 0xFFFFu, m >> 16));
+                const uint32_t E = e8m0_from_amax_bits(m);
+                uint32_t c[CPT / 4];
+#pragma unroll
+                for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_same(h[i][2 * q], h[i][2 * q + 1], E);
+                if (active) {
+                    const int64_t r = T.r0 + i;
+                    store_codes<CPT>(a.row.codes + r * a.row.ld_codes + co, c);
+                    if ((tid & (LPB - 1)) == 0) a.row.scales[r * a.row.ld_scales + co / 32] = (uint8_t)E;
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // pass 3: colwise outputs
+    if constexpr (DIRS & 2) {
+        if (!active) return;
+        float sc[CPT];
+        uint32_t nan[CPT / 4];
+        uint32_t Eb[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT / 2; k++) {
+            Eb[2 * k] = e8m0_from_amax_bits(colmax[k] & 0xFFFFu);
+            Eb[2 * k + 1] = e8m0_from_amax_bits(colmax[k] >> 16);
+        }
+#pragma unroll
+        for (int k = 0; k < CPT; k++) sc[k] = scale_operand(Eb[k]);
+#pragma unroll
+        for (int q = 0; q < CPT / 4; q++) {
+            nan[q] = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; j++) nan[q] |= (Eb[4 * q + j] == 0xFFu ? 0xFFu : 0u) << (8 * j);
+        }
+        uint8_t *colc = a.col.codes + T.r0 * a.col.ld_codes;
+#pragma unroll
+        for (int i = 0; i < ROWS; i++) {
+            if (i < T.n) {
+                uint32_t c[CPT / 4];
+#pragma unroll
+                for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_cols(h[i][2 * q], h[i][2 * q + 1], sc + 4 * q, nan[q]);
+                store_codes<CPT>(colc + i * a.col.ld_codes + co, c);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        uint32_t sb[CPT / 4];
+#pragma unroll
+        for (int q = 0; q < CPT / 4; q++)
+            sb[q] = Eb[4 * q] | (Eb[4 * q + 1] << 8) | (Eb[4 * q + 2] << 16) | (Eb[4 * q + 3] << 24);
+        store_codes<CPT>(a.col.scales + T.srow * a.col.ld_scales + co, sb);
+    }
+}
+
+// ------------------------------------------------------------------ backward
+
+struct BwdPair {
+    uint32_t dg, du;     // packed bf16 dgate / dup
+    float dsum;          // dh*a*u of both elements
+    uint32_t risky;      // 2-bit mask
+};
+
+// Error bound of the fast silu'(g) = sig * (1 + g * e * sig) for g >= -80, as
+// an absolute value: e carries up to 1 + |g| ulps (v_exp_f32 plus the
+// rounding of its argument), sig up to 3; both are amplified by |g| * (1 - sig)
+// in the cancellation of 1 + g * (1 - sig); the rest is relative to silu'.
+// Taken with a factor ~2 of slack.
+__device__ __forceinline__ float dsilu_err(float g, float sig, float one_minus) {
+    const float ag = fabsf(g);
+    return sig * (ag * one_minus * (2.0f * ag + 20.0f) + 16.0f) * 0x1p-24f;
+}
+
+// Could an error of at most `bound` move t across a bf16 rounding tie?  The
+// tie of t's own bf16 interval is tested directly; a bound that is not small
+// against the bf16 quantum (2^-8 relative) is treated as risky outright, which
+// covers the ties of the neighbouring intervals.
+__device__ __forceinline__ bool near_tie(float t, float bound) {
+    const float tie = __uint_as_float((__float_as_uint(t) & 0xFFFF0000u) | 0x8000u);
+    return fabsf(t - tie) <= bound || bound > fabsf(t) * 0x1p-10f;
+}
+
+template <int ACT>
+__device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t uw, float s, float L) {
+    float g[2] = {lo_f(gw), hi_f(gw)}, u[2] = {lo_f(uw), hi_f(uw)};
+    const float dh[2] = {lo_f(dw), hi_f(dw)};
+    float mg[2] = {1.0f, 1.0f}, mu[2] = {1.0f, 1.0f};
+    if constexpr (ACT == ACT_CLAMPED) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            mg[j] = g[j] > L ? 0.0f : 1.0f;
+            mu[j] = (u[j] > L || u[j] < -L) ? 0.0f : 1.0f;
+            g[j] = clamp_gate(g[j], L);
+            u[j] = clamp_up(u[j], L);
+        }
+    }
+    BwdPair out;
+    float t[2], sg[2], om[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const Sig z = sig_fast(g[j]);
+        sg[j] = z.sig;
+        om[j] = z.e * z.sig;           // 1 - sigma without cancellation
+        t[j] = g[j] * z.sig;
+    }
+    const uint32_t aw = pack_bf16(t[0], t[1]);
+    const float av[2] = {lo_f(aw), hi_f(aw)};
+    float vdg[2], vdu[2];
+    out.risky = 0u;
+    out.dsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const float q = dh[j] * av[j];          // exact (8 x 8 bits)
+        const float qs = q * s;
+        vdu[j] = qs * mu[j];
+        out.dsum += q * u[j];                   // exact (24 bits) unless it underflows
+        const float du_ = dh[j] * u[j];         // exact
+        const float P = du_ * s;                // one rounding
+        const float ds = sg[j] * (1.0f + g[j] * om[j]);
+        const float tdg = P * ds * mg[j];
+        vdg[j] = tdg;
+        bool r = silu_risky(g[j], t[j]) || product_risky(q, qs);
+        r = r || !__builtin_amdgcn_class(du_, kNormalOrZero) || !__builtin_amdgcn_class(P, kNormalOrZero) ||
+            !__builtin_amdgcn_class(tdg, kNormalOrZero);
+        r = r || (mg[j] != 0.0f && near_tie(tdg, fabsf(P) * dsilu_err(g[j], sg[j], om[j]) + fabsf(tdg) * 0x1p-21f));
+        if (r) out.risky |= 1u << j;
+    }
+    out.dg = pack_bf16(vdg[0], vdg[1]);
+    out.du = pack_bf16(vdu[0], vdu[1]);
+    return out;
+}
+
+// fp64 recomputation of one backward element, in the definition's order.
+// Returns dgate | dup << 16, and in *corr the change of dh*a*u caused by the
+// exact a (the fast pass summed dh*a_fast*u into dscale).
+template <int ACT>
+__device__ __forceinline__ uint32_t bwd_elem_f64(float dhf, float gf, float uf, float s, float L, float *corr) {
+    double g = gf, u = uf;
+    const double dh = dhf;
+    double mg = 1.0, mu = 1.0;
+    if (ACT == ACT_CLAMPED) {
+        if (g > L) { mg = 0.0; g = L; }
+        if (u > L || u < -L) { mu = 0.0; u = u > L ? (double)L : -(double)L; }
+    }
+    const double sg = sigmoid_f64(g);
+    const uint32_t ab = bf16_from_f64(g * sg);
+    const double a = (double)__uint_as_float(ab << 16);
+    const double dsilu = sg * (1.0 + g * (1.0 - sg));
+    const double sd = s;
+    const uint32_t dgb = bf16_from_f64(dh * sd * u * dsilu * mg);
+    const uint32_t dub = bf16_from_f64(dh * sd * a * mu);
+    // the fast pass's a, recomputed with the same instructions
+    const float gc = (float)g;
+    const Sig z = sig_fast(gc);
+    const float af = lo_f(pack_bf16(gc * z.sig, 0.0f));
+    *corr = (dhf * (float)u) * ((float)a - af);
+    return dgb | (dub << 16);
+}
+
+template <int ACT, int CPT, int ROWS>
+__device__ __forceinline__ void bwd_fix(const BwdArgs &a, const Tile &T, int c0, const uint32_t *risk,
+                                        uint32_t (&hg)[ROWS][CPT / 2], uint32_t (&hu)[ROWS][CPT / 2],
+                                        uint32_t *q, float *qc, float (*red)[257], int tid) {
+    constexpr int NW = risk_words<ROWS, CPT>();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) total += __builtin_popcount(risk[w]);
+    for (int base = 0; base < total; base += kFixQ) {
+        const int nq = fix_gather<NW>(risk, base, q);
+#pragma unroll 1
+        for (int j = 0; j < nq; j++) {
+            const int idx = (int)q[j];
+            const int64_t r = T.r0 + idx / CPT, c = c0 + idx % CPT;
+            const float d = bf16_at(a.grad + r * a.ld_grad + c);
+            const float g = bf16_at(a.gate + r * a.ld_gate + c);
+            const float u = bf16_at(a.up + r * a.ld_up + c);
+            const float s = a.row_scale != nullptr ? a.row_scale[r] : 1.0f;
+            float corr;
+            q[j] = bwd_elem_f64<ACT>(d, g, u, s, a.limit, &corr);
+            qc[j] = corr;
+        }
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < ROWS; i++) {
+            const uint32_t rb = row_bits<CPT>(risk, i);
+            if (rb) {
+                float corr = 0.0f;
+#pragma unroll
+                for (int k = 0; k < CPT; k++) {
+                    if (rb & (1u << k)) {
+                        if (rank >= base && rank < base + nq) {
+                            const uint32_t v = q[rank - base];
+                            hg[i][k >> 1] = set_half(hg[i][k >> 1], k & 1, v & 0xFFFFu);
+                            hu[i][k >> 1] = set_half(hu[i][k >> 1], k & 1, v >> 16);
+                            corr += qc[rank - base];
+                        }
+                        rank++;
+                    }
+                }
+                if (red != nullptr) red[i][tid] += corr;
+            }
+        }
+    }
+}
+
+// Backward over one row tile x column slab.  Each lane owns CPT columns j of
+// gate/up/grad; it produces dgate (columns j of [dgate | dup]) and dup
+// (columns K + j).  dscale partials of the workgroup are reduced through LDS
+// in a fixed order (deterministic) and written per (row, slab).
+template <int ACT, int DIRS, int CPT, int ROWS>
+__global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a, int64_t nslabs) {
+    constexpr int LPB = 32 / CPT;
+    constexpr int NW = risk_words<ROWS, CPT>();
+    constexpr int PF = 4;  // rows of loads kept in flight
+    __shared__ float red[ROWS][257];
+    __shared__ float red2[ROWS][9];
+    __shared__ uint32_t fixq[256 * kFixQ];
+    __shared__ float fixc[256 * kFixQ];
+    const int64_t bid = blockIdx.x;
+    const int64_t t = bid / nslabs;
+    const int64_t slab = bid - t * nslabs;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int co = (int)((slab * (int64_t)nthr + tid) * CPT);
+    const bool active = co < a.K;
+    const Tile T = tile_rows<ROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
+    if (T.n == 0) return;
+    const float L = a.limit;
+    const int K = (int)a.K;
+    const bool dense = a.dgate != nullptr;
+    const bool want_ds = a.dscale != nullptr;
+    const uint16_t *grad0 = a.grad + T.r0 * a.ld_grad;
+    const uint16_t *gate0 = a.gate + T.r0 * a.ld_gate;
+    const uint16_t *up0 = a.up + T.r0 * a.ld_up;
+
+    // pass 1: the tile on the fast path
+    uint32_t hg[ROWS][CPT / 2], hu[ROWS][CPT / 2];
+    uint32_t risk[NW];
+#pragma unroll
+    for (int w = 0; w < NW; w++) risk[w] = 0u;
+    Vec<CPT> db[PF], gb[PF], ub[PF];
+#pragma unroll
+    for (int i = 0; i < PF; i++) {
+        db[i] = gb[i] = ub[i] = zero_vec<CPT>();
+        if (i < ROWS && i < T.n && active) {
+            db[i] = load_vec<CPT>(grad0 + i * a.ld_grad + co);
+            gb[i] = load_vec<CPT>(gate0 + i * a.ld_gate + co);
+            ub[i] = load_vec<CPT>(up0 + i * a.ld_up + co);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < ROWS; i++) {
+        if (i < T.n) {
+            const Vec<CPT> dv = db[i % PF], gv = gb[i % PF], uv = ub[i % PF];
+            if (i + PF < ROWS && i + PF < T.n && active) {
+                db[i % PF] = load_vec<CPT>(grad0 + (i + PF) * a.ld_grad + co);
+                gb[i % PF] = load_vec<CPT>(gate0 + (i + PF) * a.ld_gate + co);
+                ub[i % PF] = load_vec<CPT>(up0 + (i + PF) * a.ld_up + co);
+            }
+            const float s = a.row_scale != nullptr ? a.row_scale[T.r0 + i] : 1.0f;
+            uint32_t bits = 0u;
+            float dsum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CPT / 2; k++) {
+                const BwdPair p = bwd_pair<ACT>(dv.w[k], gv.w[k], uv.w[k], s, L);
+                hg[i][k] = p.dg;
+                hu[i][k] = p.du;
+                dsum += p.dsum;
+                bits |= p.risky << (2 * k);
+            }
+            if (!scale_ok(s)) bits = (1u << CPT) - 1u;
+            if (!active) {
+                bits = 0u;
+                dsum = 0.0f;
+            }
+            risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
+            if (want_ds) red[i][tid] = dsum;
+        } else {
+#pragma unroll
+            for (int k = 0; k < CPT / 2; k++) hg[i][k] = hu[i][k] = 0u;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    bwd_fix<ACT, CPT, ROWS>(a, T, co, risk, hg, hu, fixq + tid * kFixQ, fixc + tid * kFixQ,
+                            want_ds ? red : nullptr, tid);
+
+    // pass 2: dense outputs, rowwise outputs, column maxima
+    uint32_t cmg[CPT / 2], cmu[CPT / 2];
+#pragma unroll
+    for (int k = 0; k < CPT / 2; k++) cmg[k] = cmu[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < ROWS; i++) {
+        if (i < T.n) {
+            const int64_t r = T.r0 + i;
+            if (dense && active) {
+                store_bf16<CPT>(a.dgate + r * a.ld_dgate + co, hg[i]);
+                store_bf16<CPT>(a.dup + r * a.ld_dup + co, hu[i]);
+            }
+            uint32_t mg = 0u, mu = 0u;
+#pragma unroll
+            for (int k = 0; k < CPT / 2; k++) {
+                const uint32_t ag = hg[i][k] & 0x7FFF7FFFu;
+                const uint32_t au = hu[i][k] & 0x7FFF7FFFu;
+                if constexpr (DIRS & 2) {
+                    cmg[k] = umax16x2(cmg[k], ag);
+                    cmu[k] = umax16x2(cmu[k], au);
+                }
+                mg = umax16x2(mg, ag);
+                mu = umax16x2(mu, au);
+            }
+            if constexpr (DIRS & 1) {
+                mg = block_max<LPB>(max(mg & 0xFFFFu, mg >> 16));
+                mu = block_max<LPB>(max(mu & 0xFFFFu, mu >> 16));
+                const uint32_t Eg = e8m0_from_amax_bits(mg), Eu = e8m0_from_amax_bits(mu);
+                uint32_t cg[CPT / 4], cu[CPT / 4];
+#pragma unroll
+                for (int q = 0; q < CPT / 4; q++) {
+                    cg[q] = cvt4_same(hg[i][2 * q], hg[i][2 * q + 1], Eg);
+                    cu[q] = cvt4_same(hu[i][2 * q], hu[i][2 * q + 1], Eu);
+                }
+                if (active) {
+                    uint8_t *rowc = a.row.codes + r * a.row.ld_codes;
+                    store_codes<CPT>(rowc + co, cg);
+                    store_codes<CPT>(rowc + K + co, cu);
+                    if ((tid & (LPB - 1)) == 0) {
+                        uint8_t *rs = a.row.scales + r * a.row.ld_scales;
+                        rs[co / 32] = (uint8_t)Eg;
+                        rs[(K + co) / 32] = (uint8_t)Eu;
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // pass 3: colwise outputs
+    if constexpr (DIRS & 2) {
+        if (active) {
+            uint32_t Eg[CPT], Eu[CPT];
+            float sg[CPT], su[CPT];
+#pragma unroll
+            for (int k = 0; k < CPT / 2; k++) {
+                Eg[2 * k] = e8m0_from_amax_bits(cmg[k] & 0xFFFFu);
+                Eg[2 * k + 1] = e8m0_from_amax_bits(cmg[k] >> 16);
+                Eu[2 * k] = e8m0_from_amax_bits(cmu[k] & 0xFFFFu);
+                Eu[2 * k + 1] = e8m0_from_amax_bits(cmu[k] >> 16);
+            }
+            uint32_t ng[CPT / 4], nu[CPT / 4];
+#pragma unroll
+            for (int k = 0; k < CPT; k++) {
+                sg[k] = scale_operand(Eg[k]);
+                su[k] = scale_operand(Eu[k]);
+            }
+#pragma unroll
+            for (int q = 0; q < CPT / 4; q++) {
+                ng[q] = nu[q] = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    ng[q] |= (Eg[4 * q + j] == 0xFFu ? 0xFFu : 0u) << (8 * j);
+                    nu[q] |= (Eu[4 * q + j] == 0xFFu ? 0xFFu : 0u) << (8 * j);
+                }
+            }
+            uint8_t *colc = a.col.codes + T.r0 * a.col.ld_codes;
+#pragma unroll
+            for (int i = 0; i < ROWS; i++) {
+                if (i < T.n) {
+                    uint32_t cg[CPT / 4], cu[CPT / 4];
+#pragma unroll
+                    for (int q = 0; q < CPT / 4; q++) {
+                        cg[q] = cvt4_cols(hg[i][2 * q], hg[i][2 * q + 1], sg + 4 * q, ng[q]);
+                        cu[q] = cvt4_cols(hu[i][2 * q], hu[i][2 * q + 1], su + 4 * q, nu[q]);
+                    }
+                    store_codes<CPT>(colc + i * a.col.ld_codes + co, cg);
+                    store_codes<CPT>(colc + i * a.col.ld_codes + K + co, cu);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            uint32_t sbg[CPT / 4], sbu[CPT / 4];
+#pragma unroll
+            for (int q = 0; q < CPT / 4; q++) {
+                sbg[q] = Eg[4 * q] | (Eg[4 * q + 1] << 8) | (Eg[4 * q + 2] << 16) | (Eg[4 * q + 3] << 24);
+                sbu[q] = Eu[4 * q] | (Eu[4 * q + 1] << 8) | (Eu[4 * q + 2] << 16) | (Eu[4 * q + 3] << 24);
+            }
+            uint8_t *cs = a.col.scales + T.srow * a.col.ld_scales;
+            store_codes<CPT>(cs + co, sbg);
+            store_codes<CPT>(cs + K + co, sbu);
+        }
+    }
+
+    if (want_ds) {
+        // deterministic reduction of the workgroup's dscale partials per row:
+        // segment sums of 32 lanes in lane order, then segments in order
+        __syncthreads();
+        const int nseg = (nthr + 31) / 32;
+        for (int w = tid; w < ROWS * nseg; w += nthr) {
+            const int row = w % ROWS, seg = w / ROWS;
+            float acc = 0.0f;
+            const int j1 = min(nthr, seg * 32 + 32);
+            for (int j = seg * 32; j < j1; j++) acc += red[row][j];
+            red2[row][seg] = acc;
+        }
+        __syncthreads();
+        if (tid < T.n) {
+            float acc = 0.0f;
+            for (int seg = 0; seg < nseg; seg++) acc += red2[tid][seg];
+            const int64_t r = T.r0 + tid;
+            if (nslabs == 1) a.dscale[r] = acc;
+            else a.partials[r * nslabs + slab] = acc;
+        }
+    }
+}
+
+// dscale[r] = sum over slabs of the partials, in slab order
+__global__ void dscale_finish_kernel(const float *partials, int64_t nslabs, int64_t M, float *dscale) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= M) return;
+    float acc = 0.0f;
+    for (int64_t j = 0; j < nslabs; j++) acc += partials[r * nslabs + j];
+    dscale[r] = acc;
+}
+
+// ------------------------------------------------------------------ launch config
+
+struct Cfg {
+    int threads;
+    int64_t nslabs;
+};
+
+// Workgroup width (lanes) for `chunks` column chunks per row: the widest of
+// 256/192/128/64 lanes that leaves the fewest lanes idle.
+Cfg choose_cfg(int64_t chunks) {
+    Cfg best{64, (chunks + 63) / 64};
+    double best_util = -1.0;
+    for (int th : {256, 192, 128, 64}) {
+        const int64_t ns = (chunks + th - 1) / th;
+        const double util = (double)chunks / (double)(ns * th);
+        if (util > best_util + 1e-9) {
+            best_util = util;
+            best = Cfg{th, ns};
+        }
+    }
+    return best;
+}
+
+template <int ACT, int DIRS>
+hipError_t fwd_dispatch_dirs(const FwdArgs &a, hipStream_t stream) {
+    // rowwise-only: 8 rows x 8 columns per lane; colwise / both: 32 rows x 4 columns
+    constexpr int CPT = (DIRS == 1) ? 8 : 4;
+    constexpr int ROWS = (DIRS == 1) ? 8 : 32;
+    const Cfg c = choose_cfg(a.K / CPT);
+    const bool grouped = (DIRS & 2) && a.groups.G > 0;
+    const int64_t ntiles = grouped ? colwise_block_bound(a.M, a.groups.G) : (a.M + ROWS - 1) / ROWS;
+    const int64_t nblocks = ntiles * c.nslabs;
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_kernel<ACT, DIRS, CPT, ROWS>), dim3((unsigned)nblocks), dim3(c.threads), 0,
+                       stream, a, c.nslabs);
+    return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t fwd_dispatch(const FwdArgs &a, hipStream_t stream) {
+    switch (a.dirs) {
+        case 1: return fwd_dispatch_dirs<ACT, 1>(a, stream);
+        case 2: return fwd_dispatch_dirs<ACT, 2>(a, stream);
+        default: return fwd_dispatch_dirs<ACT, 3>(a, stream);
+    }
+}
+
+template <int DIRS>
+constexpr int bwd_cpt() { return (DIRS & 2) ? 4 : 8; }
+template <int DIRS>
+constexpr int bwd_rows() { return (DIRS & 2) ? 32 : 8; }
+
+Cfg bwd_cfg(int64_t K, unsigned dirs) {
+    const int cpt = (dirs & 2) ? 4 : 8;
+    return choose_cfg(K / cpt);
+}
+
+template <int ACT, int DIRS>
+hipError_t bwd_dispatch_dirs(const BwdArgs &a, hipStream_t stream) {
+    constexpr int CPT = bwd_cpt<DIRS>();
+    constexpr int ROWS = bwd_rows<DIRS>();
+    const Cfg c = bwd_cfg(a.K, DIRS);
+    const bool grouped = (DIRS & 2) && a.groups.G > 0;
+    const int64_t ntiles = grouped ? colwise_block_bound(a.M, a.groups.G) : (a.M + ROWS - 1) / ROWS;
+    const int64_t nblocks = ntiles * c.nslabs;
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_kernel<ACT, DIRS, CPT, ROWS>), dim3((unsigned)nblocks), dim3(c.threads), 0,
+                       stream, a, c.nslabs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.dscale != nullptr && c.nslabs > 1) {
+        const int64_t nb = (a.M + 255) / 256;
+        hipLaunchKernelGGL(dscale_finish_kernel, dim3((unsigned)nb), dim3(256), 0, stream,
+                           (const float *)a.partials, c.nslabs, a.M, a.dscale);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template <int ACT>
+hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t stream) {
+    switch (a.dirs) {
+        case 0: return bwd_dispatch_dirs<ACT, 0>(a, stream);
+        case 1: return bwd_dispatch_dirs<ACT, 1>(a, stream);
+        case 2: return bwd_dispatch_dirs<ACT, 2>(a, stream);
+        default: return bwd_dispatch_dirs<ACT, 3>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_act_quant_fwd(const FwdArgs &a, hipStream_t stream) {
+    switch (a.act) {
+        case ACT_SWIGLU: return fwd_dispatch<ACT_SWIGLU>(a, stream);
+        case ACT_CLAMPED: return fwd_dispatch<ACT_CLAMPED>(a, stream);
+        default: return fwd_dispatch<ACT_IDENTITY>(a, stream);
+    }
+}
+
+hipError_t launch_act_quant_bwd(const BwdArgs &a, hipStream_t stream) {
+    if (a.act == ACT_CLAMPED) return bwd_dispatch<ACT_CLAMPED>(a, stream);
+    return bwd_dispatch<ACT_SWIGLU>(a, stream);
+}
+
+size_t bwd_workspace_bytes(int64_t M, int64_t K) {
+    // the largest slab count over the direction choices
+    int64_t ns = 1;
+    for (unsigned d : {0u, 1u, 2u, 3u}) {
+        const Cfg c = bwd_cfg(K, d);
+        if (c.nslabs > ns) ns = c.nslabs;
+    }
+    return ns > 1 ? (size_t)M * (size_t)ns * sizeof(float) : 0;
+}
+
+}  // namespace mxq

@@ -1,0 +1,399 @@
+// api.cpp -- the C ABI of libmxq (declared in include/mxq.h): argument
+// validation, error reporting and dispatch to the HIP launchers.  Nothing here
+// touches device memory; every launch is asynchronous on the caller's stream.
+#include "mxq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gemm_internal.h"
+#include "mxq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mxq_status fail(mxq_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+mxq_status ok() {
+    g_last_error.clear();
+    return MXQ_OK;
+}
+
+mxq_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(MXQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxExtent = int64_t(1) << 62;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte footprint of a strided 2-D array (rows x cols elements of esize bytes,
+// row pitch ld elements): the interval [lo, hi) plus the pitch and row width,
+// so that interleaved arrays with one pitch (e.g. the two halves of a packed
+// [dgate | dup]) are not mistaken for overlapping ones.
+struct Range {
+    uintptr_t lo = 0, hi = 0;
+    uintptr_t pitch = 0, width = 0;
+    const char *name = "";
+};
+
+Range range2d(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t esize, const char *name) {
+    Range r;
+    r.name = name;
+    if (p == nullptr || rows <= 0 || cols <= 0) return r;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + cols) * esize);
+    r.pitch = rows > 1 ? (uintptr_t)(ld * esize) : 0;
+    r.width = (uintptr_t)(cols * esize);
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+    if (!(a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi)) return false;
+    if (a.pitch != 0 && a.pitch == b.pitch) {
+        // same pitch: disjoint iff the row segments never meet modulo the pitch
+        const uintptr_t d = (b.lo >= a.lo) ? (b.lo - a.lo) % a.pitch : (a.pitch - (a.lo - b.lo) % a.pitch) % a.pitch;
+        if (d >= a.width && d + b.width <= a.pitch) return false;
+    }
+    return true;
+}
+
+// every output against every input and every other output
+mxq_status check_alias(const std::vector<Range> &in, const std::vector<Range> &out) {
+    for (size_t i = 0; i < out.size(); i++) {
+        for (const Range &r : in)
+            if (overlap(out[i], r)) return fail(MXQ_ERR_ALIAS, "output %s overlaps input %s", out[i].name, r.name);
+        for (size_t j = i + 1; j < out.size(); j++)
+            if (overlap(out[i], out[j]))
+                return fail(MXQ_ERR_ALIAS, "output %s overlaps output %s", out[i].name, out[j].name);
+    }
+    return MXQ_OK;
+}
+
+// extent of rows x ld elements must stay far below 2^62 bytes
+bool extent_ok(int64_t rows, int64_t ld, int64_t esize) {
+    if (rows <= 0) return true;
+    if (ld > kMaxExtent / esize) return false;
+    return rows <= kMaxExtent / (ld * esize);
+}
+
+// Validate one MXFP8 output of `rows x cols` with `srows` scale rows.
+mxq_status check_mx_out(const mxq_mx_out *o, bool rowwise, int64_t rows, int64_t cols, int64_t srows,
+                        const char *name, std::vector<Range> &outs) {
+    if (o == nullptr || o->codes == nullptr || o->scales == nullptr)
+        return fail(MXQ_ERR_NULL, "%s output (codes and scales) is required for this direction", name);
+    if (o->ld_codes < cols) return fail(MXQ_ERR_SHAPE, "%s ld_codes %lld < %lld", name, (long long)o->ld_codes, (long long)cols);
+    const int64_t scols = rowwise ? cols / 32 : cols;
+    if (o->ld_scales < scols)
+        return fail(MXQ_ERR_SHAPE, "%s ld_scales %lld < %lld", name, (long long)o->ld_scales, (long long)scols);
+    if (!aligned(o->codes, 16) || o->ld_codes % 16 != 0)
+        return fail(MXQ_ERR_ALIGN, "%s codes pointer and ld_codes must be multiples of 16 bytes", name);
+    if (!rowwise && (!aligned(o->scales, 8) || o->ld_scales % 8 != 0))
+        return fail(MXQ_ERR_ALIGN, "%s colwise scales pointer and ld_scales must be multiples of 8 bytes", name);
+    if (!extent_ok(rows, o->ld_codes, 1) || !extent_ok(srows, o->ld_scales, 1))
+        return fail(MXQ_ERR_OVERFLOW, "%s output extent too large", name);
+    outs.push_back(range2d(o->codes, rows, cols, o->ld_codes, 1, rowwise ? "row codes" : "col codes"));
+    outs.push_back(range2d(o->scales, srows, scols, o->ld_scales, 1, rowwise ? "row scales" : "col scales"));
+    return MXQ_OK;
+}
+
+mxq_status check_bf16_in(const uint16_t *p, int64_t M, int64_t K, int64_t ld, const char *name,
+                         std::vector<Range> &ins) {
+    if (p == nullptr) return fail(MXQ_ERR_NULL, "%s is NULL", name);
+    if (ld < K) return fail(MXQ_ERR_SHAPE, "%s ld %lld < K %lld", name, (long long)ld, (long long)K);
+    if (!aligned(p, 16) || ld % 8 != 0)
+        return fail(MXQ_ERR_ALIGN, "%s pointer and row pitch must be multiples of 16 bytes", name);
+    if (!extent_ok(M, ld, 2)) return fail(MXQ_ERR_OVERFLOW, "%s extent too large", name);
+    ins.push_back(range2d(p, M, K, ld, 2, name));
+    return MXQ_OK;
+}
+
+struct GroupsOut {
+    mxq::Groups g{0, nullptr, nullptr};
+};
+
+mxq_status check_groups(const mxq_groups *groups, bool need_blocks, GroupsOut &out, std::vector<Range> &ins) {
+    if (groups == nullptr) return MXQ_OK;
+    if (groups->G < 1 || groups->G > (int64_t(1) << 24))
+        return fail(MXQ_ERR_SHAPE, "groups->G = %lld must be in [1, 2^24]", (long long)groups->G);
+    if (groups->row_off == nullptr || (need_blocks && groups->block_off == nullptr))
+        return fail(MXQ_ERR_NULL, "groups->row_off%s is NULL", need_blocks ? " or groups->block_off" : "");
+    if (!aligned(groups->row_off, 8) || (groups->block_off && !aligned(groups->block_off, 8)))
+        return fail(MXQ_ERR_ALIGN, "group offset arrays must be 8-byte aligned");
+    out.g = mxq::Groups{groups->G, groups->row_off, groups->block_off};
+    ins.push_back(range2d(groups->row_off, 1, groups->G + 1, groups->G + 1, 8, "row_off"));
+    if (groups->block_off) ins.push_back(range2d(groups->block_off, 1, groups->G + 1, groups->G + 1, 8, "block_off"));
+    return MXQ_OK;
+}
+
+// Validate and pack the shared part of fwd / quantize.
+mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, int64_t K, const uint16_t *gate,
+                       int64_t ld_gate, const uint16_t *up, int64_t ld_up, const float *row_scale,
+                       const mxq_groups *groups, uint32_t dirs, const mxq_mx_out *row_out,
+                       const mxq_mx_out *col_out, bool *noop) {
+    *noop = false;
+    if (M < 0 || K < 0) return fail(MXQ_ERR_SHAPE, "M = %lld and K = %lld must be >= 0", (long long)M, (long long)K);
+    if (K % 32 != 0) return fail(MXQ_ERR_SHAPE, "K = %lld must be a multiple of 32", (long long)K);
+    if (dirs < 1 || dirs > 3) return fail(MXQ_ERR_SHAPE, "dirs = %u must be ROWWISE, COLWISE or both", dirs);
+    if (act_kind == mxq::ACT_CLAMPED && !(limit > 0.0f))
+        return fail(MXQ_ERR_SHAPE, "clamped SwiGLU needs a limit > 0");
+    if (act_kind != mxq::ACT_IDENTITY && row_scale != nullptr && !aligned(row_scale, 4))
+        return fail(MXQ_ERR_ALIGN, "row_scale must be 4-byte aligned");
+    std::vector<Range> ins, outs;
+    GroupsOut go;
+    mxq_status s = check_groups(groups, (dirs & 2) != 0, go, ins);
+    if (s != MXQ_OK) return s;
+    if (M == 0 || K == 0) {
+        *noop = true;
+        return MXQ_OK;
+    }
+    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 30))
+        return fail(MXQ_ERR_OVERFLOW, "M or K beyond the supported range");
+    s = check_bf16_in(gate, M, K, ld_gate, act_kind == mxq::ACT_IDENTITY ? "x" : "gate", ins);
+    if (s != MXQ_OK) return s;
+    if (act_kind != mxq::ACT_IDENTITY) {
+        s = check_bf16_in(up, M, K, ld_up, "up", ins);
+        if (s != MXQ_OK) return s;
+        if (row_scale) ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
+    }
+    const int64_t G = go.g.G;
+    const int64_t nsrows_bound = mxq::colwise_block_bound(M, G);
+    if (dirs & 1) {
+        s = check_mx_out(row_out, true, M, K, M, "rowwise", outs);
+        if (s != MXQ_OK) return s;
+    } else if (row_out != nullptr && row_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");
+    }
+    if (dirs & 2) {
+        // exact scale-row count is known only on the device; alias checks use the bound
+        s = check_mx_out(col_out, false, M, K, G > 0 ? nsrows_bound : (M + 31) / 32, "colwise", outs);
+        if (s != MXQ_OK) return s;
+    } else if (col_out != nullptr && col_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
+    }
+    // grid bound: tiles x slabs must fit a 31-bit grid
+    if (nsrows_bound * ((K / 8 + 63) / 64) >= (int64_t(1) << 31) || (M / 8 + 1) * ((K / 8 + 63) / 64) >= (int64_t(1) << 31))
+        return fail(MXQ_ERR_OVERFLOW, "launch grid beyond 2^31 workgroups");
+    s = check_alias(ins, outs);
+    if (s != MXQ_OK) return s;
+    a.act = act_kind;
+    a.limit = limit;
+    a.M = M;
+    a.K = K;
+    a.gate = gate;
+    a.ld_gate = ld_gate;
+    a.up = up;
+    a.ld_up = ld_up;
+    a.row_scale = act_kind == mxq::ACT_IDENTITY ? nullptr : row_scale;
+    a.groups = go.g;
+    a.dirs = dirs;
+    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    return MXQ_OK;
+}
+
+int act_from(const mxq_act *act, float *limit) {
+    *limit = 7.0f;
+    if (act == nullptr) return mxq::ACT_SWIGLU;
+    *limit = act->limit;
+    return act->kind == MXQ_ACT_CLAMPED_SWIGLU ? mxq::ACT_CLAMPED : (act->kind == MXQ_ACT_SWIGLU ? mxq::ACT_SWIGLU : -1);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mxq_version(void) { return "mxq 0.1.0 (gfx950)"; }
+
+const char *mxq_last_error_message(void) { return g_last_error.c_str(); }
+
+const char *mxq_status_string(mxq_status s) {
+    switch (s) {
+        case MXQ_OK: return "MXQ_OK";
+        case MXQ_ERR_NULL: return "MXQ_ERR_NULL";
+        case MXQ_ERR_SHAPE: return "MXQ_ERR_SHAPE";
+        case MXQ_ERR_ALIGN: return "MXQ_ERR_ALIGN";
+        case MXQ_ERR_OVERFLOW: return "MXQ_ERR_OVERFLOW";
+        case MXQ_ERR_ALIAS: return "MXQ_ERR_ALIAS";
+        case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
+        case MXQ_ERR_HIP: return "MXQ_ERR_HIP";
+        case MXQ_ERR_WORKSPACE: return "MXQ_ERR_WORKSPACE";
+    }
+    return "unknown mxq_status";
+}
+
+mxq_status mxq_splits_to_offsets(const int64_t *splits, int64_t G, int64_t *row_off, int64_t *block_off,
+                                 int32_t *err_flag, void *stream) {
+    if (splits == nullptr || row_off == nullptr) return fail(MXQ_ERR_NULL, "splits and row_off are required");
+    if (G < 1 || G > (int64_t(1) << 20)) return fail(MXQ_ERR_SHAPE, "G = %lld must be in [1, 2^20]", (long long)G);
+    if (!aligned(splits, 8) || !aligned(row_off, 8) || (block_off && !aligned(block_off, 8)) ||
+        (err_flag && !aligned(err_flag, 4)))
+        return fail(MXQ_ERR_ALIGN, "offset arrays must be 8-byte aligned (err_flag 4-byte)");
+    std::vector<Range> ins{range2d(splits, 1, G, G, 8, "splits")};
+    std::vector<Range> outs{range2d(row_off, 1, G + 1, G + 1, 8, "row_off")};
+    if (block_off) outs.push_back(range2d(block_off, 1, G + 1, G + 1, 8, "block_off"));
+    if (err_flag) outs.push_back(range2d(err_flag, 1, 1, 1, 4, "err_flag"));
+    mxq_status s = check_alias(ins, outs);
+    if (s != MXQ_OK) return s;
+    return hip_status(mxq::launch_splits_to_offsets(splits, G, row_off, block_off, err_flag, (hipStream_t)stream),
+                      "mxq_splits_to_offsets launch");
+}
+
+mxq_status mxq_swiglu_quantize_fwd(const mxq_act *act, int64_t M, int64_t K, const uint16_t *gate, int64_t ld_gate,
+                                   const uint16_t *up, int64_t ld_up, const float *row_scale,
+                                   const mxq_groups *groups, uint32_t dirs, const mxq_mx_out *row_out,
+                                   const mxq_mx_out *col_out, void *stream) {
+    float limit;
+    const int kind = act_from(act, &limit);
+    if (kind < 0) return fail(MXQ_ERR_UNSUPPORTED, "unknown activation kind %d", act->kind);
+    mxq::FwdArgs a{};
+    bool noop;
+    mxq_status s = prepare_fwd(a, kind, limit, M, K, gate, ld_gate, up, ld_up, row_scale, groups, dirs, row_out,
+                               col_out, &noop);
+    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
+    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_fwd launch");
+}
+
+mxq_status mxq_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, const mxq_groups *groups,
+                        uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *stream) {
+    mxq::FwdArgs a{};
+    bool noop;
+    mxq_status s = prepare_fwd(a, mxq::ACT_IDENTITY, 0.0f, M, K, x, ld_x, nullptr, 0, nullptr, groups, dirs, row_out,
+                               col_out, &noop);
+    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
+    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_quantize launch");
+}
+
+mxq_status mxq_swiglu_quantize_bwd_workspace(int64_t M, int64_t K, uint32_t dirs, size_t *bytes) {
+    (void)dirs;
+    if (bytes == nullptr) return fail(MXQ_ERR_NULL, "bytes is NULL");
+    if (M < 0 || K < 0 || K % 32 != 0) return fail(MXQ_ERR_SHAPE, "M, K must be >= 0 and K % 32 == 0");
+    *bytes = (M == 0 || K == 0) ? 0 : mxq::bwd_workspace_bytes(M, K);
+    return ok();
+}
+
+mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, const uint16_t *grad, int64_t ld_grad,
+                                   const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
+                                   const float *row_scale, const mxq_groups *groups, uint16_t *dgate,
+                                   int64_t ld_dgate, uint16_t *dup, int64_t ld_dup, float *dscale, uint32_t dirs,
+                                   const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *ws,
+                                   size_t ws_bytes, void *stream) {
+    float limit;
+    const int kind = act_from(act, &limit);
+    if (kind < 0) return fail(MXQ_ERR_UNSUPPORTED, "unknown activation kind %d", act->kind);
+    if (M < 0 || K < 0) return fail(MXQ_ERR_SHAPE, "M = %lld and K = %lld must be >= 0", (long long)M, (long long)K);
+    if (K % 32 != 0) return fail(MXQ_ERR_SHAPE, "K = %lld must be a multiple of 32", (long long)K);
+    if (dirs > 3) return fail(MXQ_ERR_SHAPE, "dirs = %u must be 0, ROWWISE, COLWISE or both", dirs);
+    if ((dgate == nullptr) != (dup == nullptr)) return fail(MXQ_ERR_NULL, "dgate and dup must both be given or both NULL");
+    if (dirs == 0 && dgate == nullptr && dscale == nullptr)
+        return fail(MXQ_ERR_SHAPE, "nothing requested: dirs = 0 with no dense output and no dscale");
+    if (kind == mxq::ACT_CLAMPED && !(limit > 0.0f)) return fail(MXQ_ERR_SHAPE, "clamped SwiGLU needs a limit > 0");
+    std::vector<Range> ins, outs;
+    GroupsOut go;
+    mxq_status s = check_groups(groups, (dirs & 2) != 0, go, ins);
+    if (s != MXQ_OK) return s;
+    if (M == 0 || K == 0) return ok();
+    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 30))
+        return fail(MXQ_ERR_OVERFLOW, "M or K beyond the supported range");
+    if ((s = check_bf16_in(grad, M, K, ld_grad, "grad", ins)) != MXQ_OK) return s;
+    if ((s = check_bf16_in(gate, M, K, ld_gate, "gate", ins)) != MXQ_OK) return s;
+    if ((s = check_bf16_in(up, M, K, ld_up, "up", ins)) != MXQ_OK) return s;
+    if (row_scale) {
+        if (!aligned(row_scale, 4)) return fail(MXQ_ERR_ALIGN, "row_scale must be 4-byte aligned");
+        ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
+    }
+    if (dgate) {
+        if (ld_dgate < K || ld_dup < K) return fail(MXQ_ERR_SHAPE, "ld_dgate / ld_dup must be >= K");
+        if (!aligned(dgate, 16) || !aligned(dup, 16) || ld_dgate % 8 != 0 || ld_dup % 8 != 0)
+            return fail(MXQ_ERR_ALIGN, "dgate / dup pointers and pitches must be multiples of 16 bytes");
+        if (!extent_ok(M, ld_dgate, 2) || !extent_ok(M, ld_dup, 2))
+            return fail(MXQ_ERR_OVERFLOW, "dgate / dup extent too large");
+        outs.push_back(range2d(dgate, M, K, ld_dgate, 2, "dgate"));
+        outs.push_back(range2d(dup, M, K, ld_dup, 2, "dup"));
+    }
+    if (dscale) {
+        if (!aligned(dscale, 4)) return fail(MXQ_ERR_ALIGN, "dscale must be 4-byte aligned");
+        outs.push_back(range2d(dscale, 1, M, M, 4, "dscale"));
+        const size_t need = mxq::bwd_workspace_bytes(M, K);
+        if (need > 0) {
+            if (ws == nullptr || ws_bytes < need)
+                return fail(MXQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? (size_t)0 : ws_bytes);
+            if (!aligned(ws, 4)) return fail(MXQ_ERR_ALIGN, "workspace must be 4-byte aligned");
+            outs.push_back(range2d(ws, 1, (int64_t)need, (int64_t)need, 1, "workspace"));
+        }
+    }
+    const int64_t G = go.g.G;
+    const int64_t nsrows_bound = mxq::colwise_block_bound(M, G);
+    if (dirs & 1) {
+        if ((s = check_mx_out(row_out, true, M, 2 * K, M, "rowwise", outs)) != MXQ_OK) return s;
+    } else if (row_out != nullptr && row_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");
+    }
+    if (dirs & 2) {
+        if ((s = check_mx_out(col_out, false, M, 2 * K, G > 0 ? nsrows_bound : (M + 31) / 32, "colwise", outs)) != MXQ_OK)
+            return s;
+    } else if (col_out != nullptr && col_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
+    }
+    if (nsrows_bound * ((K / 4 + 63) / 64) >= (int64_t(1) << 31) || (M / 8 + 1) * ((K / 8 + 63) / 64) >= (int64_t(1) << 31))
+        return fail(MXQ_ERR_OVERFLOW, "launch grid beyond 2^31 workgroups");
+    if ((s = check_alias(ins, outs)) != MXQ_OK) return s;
+
+    mxq::BwdArgs a{};
+    a.act = kind;
+    a.limit = limit;
+    a.M = M;
+    a.K = K;
+    a.grad = grad; a.ld_grad = ld_grad;
+    a.gate = gate; a.ld_gate = ld_gate;
+    a.up = up; a.ld_up = ld_up;
+    a.row_scale = row_scale;
+    a.groups = go.g;
+    a.dgate = dgate; a.ld_dgate = ld_dgate;
+    a.dup = dup; a.ld_dup = ld_dup;
+    a.dscale = dscale;
+    a.dirs = dirs;
+    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.partials = static_cast<float *>(ws);
+    return hip_status(mxq::launch_act_quant_bwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_bwd launch");
+}
+
+mxq_status mxq_grouped_gemm_workspace(const mxq_gemm_args *args, size_t *bytes) {
+    if (args == nullptr || bytes == nullptr) return fail(MXQ_ERR_NULL, "args and bytes are required");
+    *bytes = 0;
+    return ok();
+}
+
+mxq_status mxq_grouped_gemm(const mxq_gemm_args *args, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (args == nullptr) return fail(MXQ_ERR_NULL, "args is NULL");
+    mxq::GemmArgs g{};
+    std::string err;
+    const int st = mxq::gemm_prepare(*args, g, err);
+    if (st != MXQ_OK) return fail((mxq_status)st, "%s", err.c_str());
+    if (g.noop) return ok();
+    return hip_status(mxq::launch_grouped_gemm(g, (hipStream_t)stream), "mxq_grouped_gemm launch");
+}
+
+}  // extern "C"

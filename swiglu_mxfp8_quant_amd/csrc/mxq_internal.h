@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI front end (api.cpp) and the HIP kernel
+// translation units.  Not installed; the public interface is include/mxq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace mxq {
+
+// One direction of an MXFP8 output (device pointers, pitches in bytes).
+struct MxOut {
+    uint8_t *codes;
+    int64_t ld_codes;
+    uint8_t *scales;
+    int64_t ld_scales;
+};
+
+// Row groups as seen by the kernels.  G == 0 means one implicit group of M rows.
+struct Groups {
+    int64_t G;
+    const int64_t *row_off;
+    const int64_t *block_off;
+};
+
+enum Act { ACT_SWIGLU = 0, ACT_CLAMPED = 1, ACT_IDENTITY = 2 };
+
+struct FwdArgs {
+    int act;            // Act
+    float limit;
+    int64_t M, K;
+    const uint16_t *gate; int64_t ld_gate;   // x for ACT_IDENTITY
+    const uint16_t *up; int64_t ld_up;       // unused for ACT_IDENTITY
+    const float *row_scale;                  // NULL => 1
+    Groups groups;
+    unsigned dirs;
+    MxOut row, col;
+};
+
+struct BwdArgs {
+    int act;
+    float limit;
+    int64_t M, K;
+    const uint16_t *grad; int64_t ld_grad;
+    const uint16_t *gate; int64_t ld_gate;
+    const uint16_t *up; int64_t ld_up;
+    const float *row_scale;
+    Groups groups;
+    uint16_t *dgate; int64_t ld_dgate;
+    uint16_t *dup; int64_t ld_dup;
+    float *dscale;
+    unsigned dirs;
+    MxOut row, col;
+    float *partials;    // workspace: per-row partial sums of dscale
+};
+
+// Host launchers (asynchronous on `stream`; return the hipGetLastError code).
+hipError_t launch_splits_to_offsets(const int64_t *splits, int64_t G, int64_t *row_off,
+                                    int64_t *block_off, int32_t *err_flag, hipStream_t stream);
+hipError_t launch_act_quant_fwd(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_act_quant_bwd(const BwdArgs &a, hipStream_t stream);
+size_t bwd_workspace_bytes(int64_t M, int64_t K);
+
+// Upper bound of the number of colwise scale rows: sum_g ceil(m_g/32) <= ceil(M/32) + G.
+inline int64_t colwise_block_bound(int64_t M, int64_t G) {
+    return (M + 31) / 32 + (G > 0 ? G : 0);
+}
+
+}  // namespace mxq

@@ -1,0 +1,403 @@
+"""GPU parity of the fused SwiGLU + MXFP8 forward / backward, the plain
+quantizer and the splits->offsets scan, through the C ABI, against the CPU
+oracle on identical seeded inputs.
+
+Pages: "[mxfp8 training] Add a fused gated-activation (SwiGLU) + MXFP8
+quantization kernel" (Summary, API, Numerics and tests); "Activation +
+GroupedLinear Fusion for MOE and other MOE optimizations" (Greptile Summary);
+ByteDance-Seed/VeOmni pull 1340 ("What does this PR do?", Test).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity import compare_bf16, compare_mx, rowblock_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mxq():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    import swiglu_mxfp8_quant_amd as m
+    return m
+
+
+def bits(t):
+    return W.bf16_bits(t)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def np_u8(t):
+    return t.cpu().numpy()
+
+
+def dirs_of(d):
+    return {"row": 1, "col": 2, "both": 3}[d]
+
+
+def run_fwd_and_compare(m, gu, sc, K, dirs, clamped, splits=None, report=None):
+    report = {} if report is None else report
+    M = gu.shape[0]
+    g_np, u_np = bits(gu[:, :K]), bits(gu[:, K:])
+    sc_np = None if sc is None else sc.cpu().numpy()
+    row_off = block_off = None
+    ro_np = None
+    if splits is not None:
+        row_off, block_off, _ = m.splits_to_offsets(torch.tensor(splits, dtype=torch.int64, device="cuda"))
+        ro_np, _ = O.splits_to_offsets(splits)
+    kind = O.CLAMPED_SWIGLU if clamped else O.SWIGLU
+    rc, cc, rs, cs, h, close = O.swiglu_quantize_fwd(g_np, u_np, sc_np, dirs, ro_np, kind, 7.0, want_close=True)
+    gud = gu.cuda()
+    ncb = cs.shape[0] if dirs & 2 else None
+    out = m.swiglu_quantize_fwd(gud[:, :K], gud[:, K:], None if sc is None else sc.cuda(),
+                                rowwise=bool(dirs & 1), colwise=bool(dirs & 2), row_off=row_off,
+                                block_off=block_off, n_col_blocks=ncb, clamped=clamped)
+    torch.cuda.synchronize()
+    gc_r, gc_c, gs_r, gs_c = (np_u8(x) for x in out)
+    closeh = close != 0
+    if dirs & 1:
+        compare_mx("fwd.row", gc_r, gs_r, rc, rs, closeh, True, report=report)
+    if dirs & 2:
+        compare_mx("fwd.col", gc_c, gs_c, cc, cs, closeh, False, rowblock_of(M, ro_np), report=report)
+    return report
+
+
+# ------------------------------------------------------------------ offsets
+
+@pytest.mark.parametrize("G", [1, 4, 128, 3000])
+def test_splits_to_offsets(mxq, G):
+    rng = np.random.default_rng(G)
+    s = rng.integers(0, 300, G)
+    s[rng.integers(0, G, max(1, G // 5))] = 0
+    splits = torch.tensor(s, dtype=torch.int64, device="cuda")
+    ro, bo, err = mxq.splits_to_offsets(splits)
+    rref, bref = O.splits_to_offsets(s)
+    assert np.array_equal(ro.cpu().numpy(), rref)
+    assert np.array_equal(bo.cpu().numpy(), bref)
+    assert int(err.item()) == 0
+
+
+def test_splits_negative_sets_flag(mxq):
+    splits = torch.tensor([3, -1, 5], dtype=torch.int64, device="cuda")
+    ro, bo, err = mxq.splits_to_offsets(splits)
+    assert int(err.item()) == 1
+    assert ro.cpu().tolist() == [0, 3, 2, 7]
+
+
+# ------------------------------------------------------------------ forward
+
+def test_c1_forward_both_seed0(mxq):
+    """(128,128) both directions, seed 0: codes (128,128) + scales (128,4) and (4,128)."""
+    gu = W.packed_gate_up(128, 128, seed=0)
+    sc = W.row_scale(128, seed=0)
+    rep = run_fwd_and_compare(mxq, gu, sc, 128, 3, False)
+    say("C1 mismatches:", rep)
+
+
+FWD_SHAPES = [(96, 64), (100, 64), (33, 32), (1, 32), (64, 2048), (40, 7168), (256, 768)]
+
+
+@pytest.mark.parametrize("shape", FWD_SHAPES)
+@pytest.mark.parametrize("d", ["row", "col", "both"])
+def test_forward(mxq, shape, d):
+    M, K = shape
+    gu = W.packed_gate_up(M, K, seed=M + K)
+    sc = W.row_scale(M, seed=M + K)
+    say("fwd", shape, d)
+    run_fwd_and_compare(mxq, gu, sc, K, dirs_of(d), False)
+
+
+@pytest.mark.parametrize("d", ["row", "col", "both"])
+def test_forward_clamped(mxq, d):
+    """Gate/up ~N(0, 4): about 8 % of values beyond +-7."""
+    gu = W.packed_gate_up(96, 256, seed=5, std=4.0)
+    sc = W.row_scale(96, seed=5)
+    run_fwd_and_compare(mxq, gu, sc, 256, dirs_of(d), True)
+
+
+def test_forward_no_scale(mxq):
+    gu = W.packed_gate_up(64, 128, seed=6)
+    run_fwd_and_compare(mxq, gu, None, 128, 3, False)
+
+
+@pytest.mark.parametrize("d", ["col", "both"])
+def test_forward_grouped(mxq, d):
+    splits = [31, 0, 33, 1, 64, 7, 0, 32]
+    M = sum(splits)
+    gu = W.packed_gate_up(M, 96, seed=7)
+    sc = W.row_scale(M, seed=7)
+    run_fwd_and_compare(mxq, gu, sc, 96, dirs_of(d), False, splits=splits)
+
+
+def test_forward_large_magnitudes(mxq):
+    """|g| up to ~100 exercises the g-dependent margin and the exact path."""
+    gu = W.packed_gate_up(64, 256, seed=8, std=30.0)
+    sc = W.row_scale(64, seed=8)
+    run_fwd_and_compare(mxq, gu, sc, 256, 3, False)
+
+
+def test_forward_stress_regimes(mxq):
+    """Zero blocks, outliers (~N(0, 1e3)), NaN and Inf blocks, subnormal-tiny
+    blocks and -0 in the inputs."""
+    M, K = 128, 256
+    gu, sc, _ = W.stress_inputs(M, K, seed=9, frac=0.02)
+    gu[3, 40] = float("nan")
+    gu[70, K + 100] = float("inf")
+    gu[10:12, 64:96] = 1e-39           # bf16 subnormals in gate
+    gu[90, K:K + 32] = -0.0
+    gu[5, 0:32] = 0.0
+    run_fwd_and_compare(mxq, gu, sc, K, 3, False)
+
+
+def test_forward_empty(mxq):
+    gu = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    out = mxq.swiglu_quantize_fwd(gu[:, :32], gu[:, 32:], rowwise=True, colwise=True)
+    assert all(x.numel() == 0 for x in out)
+
+
+def test_forward_input_not_mutated(mxq):
+    gu = W.packed_gate_up(64, 128, seed=10).cuda()
+    before = gu.clone()
+    mxq.swiglu_quantize_fwd(gu[:, :128], gu[:, 128:], rowwise=True, colwise=True)
+    torch.cuda.synchronize()
+    assert torch.equal(gu.view(torch.int16), before.view(torch.int16))
+
+
+def test_both_equals_row_union_col(mxq):
+    gu = W.packed_gate_up(96, 512, seed=11).cuda()
+    sc = W.row_scale(96, seed=11).cuda()
+    b = mxq.swiglu_quantize_fwd(gu[:, :512], gu[:, 512:], sc, rowwise=True, colwise=True)
+    r = mxq.swiglu_quantize_fwd(gu[:, :512], gu[:, 512:], sc, rowwise=True, colwise=False)
+    c = mxq.swiglu_quantize_fwd(gu[:, :512], gu[:, 512:], sc, rowwise=False, colwise=True)
+    assert torch.equal(b[0], r[0]) and torch.equal(b[2], r[2])
+    assert torch.equal(b[1], c[1]) and torch.equal(b[3], c[3])
+
+
+# ------------------------------------------------------------------ quantizer
+
+def test_quantize_special_blocks(mxq):
+    M, K = 96, 128
+    rng = np.random.default_rng(12)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16)
+    x[0, :32] = 0.0
+    x[1, 3] = float("nan")
+    x[2, 40] = float("-inf")
+    x[3, :32] = 1e-39
+    x[4, 5] = 448.0
+    x[5, 6] = 450.0
+    x[6, :32] = -0.0
+    x[40:72, 7] = 0.0
+    x[33, 9] = float("nan")
+    xb = bits(x)
+    rc, cc, rs, cs = O.mx_quantize(xb, 3)
+    g = [np_u8(t) for t in mxq.quantize(x.cuda(), rowwise=True, colwise=True)]
+    rep = {}
+    zero = np.zeros((M, K), bool)
+    compare_mx("q.row", g[0], g[2], rc, rs, zero, True, report=rep)
+    compare_mx("q.col", g[1], g[3], cc, cs, zero, False, rowblock_of(M), report=rep)
+
+
+def test_quantize_grouped_colwise(mxq):
+    splits = [5, 0, 40, 33, 0, 1]
+    M = sum(splits)
+    rng = np.random.default_rng(13)
+    x = torch.from_numpy(rng.standard_normal((M, 64)).astype(np.float32)).to(torch.bfloat16)
+    ro_np, bo_np = O.splits_to_offsets(splits)
+    rc, cc, rs, cs = O.mx_quantize(bits(x), 2, ro_np)
+    ro, bo, _ = mxq.splits_to_offsets(torch.tensor(splits, dtype=torch.int64, device="cuda"))
+    g = [np_u8(t) for t in mxq.quantize(x.cuda(), rowwise=False, colwise=True, row_off=ro, block_off=bo,
+                                        n_col_blocks=int(bo_np[-1]))]
+    assert np.array_equal(g[1], cc) and np.array_equal(g[3], cs)
+
+
+def test_encoder_sweep_all_bf16_all_scales(mxq):
+    """Every finite bf16 value quantized under every reachable scale byte:
+    each 32-block holds an amax of 448 * 2^(E-127) (scale byte E) and 31 bf16
+    patterns no larger than it, so the sweep covers E = 1..246 x all
+    magnitudes, subnormals included."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = (allb.astype(np.uint32) << 16).view(np.float32)
+    fin = np.isfinite(vals)
+    pats = allb[fin]
+    mags = np.abs(vals[fin])
+    rows = []
+    for E in range(1, 247, 5):
+        amax = np.float32(448.0 * 2.0 ** (E - 127))
+        cand = pats[mags <= amax]
+        step = max(1, len(cand) // (31 * 64))
+        cand = cand[::step][: 31 * 64]
+        n = len(cand) // 31
+        blk = np.empty((n, 32), np.uint16)
+        blk[:, 0] = (np.array([amax], np.float32).view(np.uint32) >> 16).astype(np.uint16)[0]
+        blk[:, 1:] = cand[: n * 31].reshape(n, 31)
+        rows.append(blk)
+    x = np.concatenate(rows, 0).reshape(-1, 128)
+    rc, _, rs, _ = O.mx_quantize(x, 1)
+    xt = W.from_bits(x, "cuda")
+    g = mxq.quantize(xt, rowwise=True, colwise=False)
+    assert np.array_equal(np_u8(g[2]), rs)
+    assert np.array_equal(np_u8(g[0]), rc)
+
+
+# ------------------------------------------------------------------ backward
+
+def run_bwd_and_compare(m, gu, sc, dy, K, dirs, clamped, splits=None, dense=True, want_ds=True):
+    M = gu.shape[0]
+    g_np, u_np, d_np = bits(gu[:, :K]), bits(gu[:, K:]), bits(dy)
+    sc_np = None if sc is None else sc.cpu().numpy()
+    row_off = block_off = None
+    ro_np = None
+    if splits is not None:
+        row_off, block_off, _ = m.splits_to_offsets(torch.tensor(splits, dtype=torch.int64, device="cuda"))
+        ro_np, _ = O.splits_to_offsets(splits)
+    kind = O.CLAMPED_SWIGLU if clamped else O.SWIGLU
+    rc, cc, rs, cs, dg, du, ds, close, tol = O.swiglu_quantize_bwd(d_np, g_np, u_np, sc_np, dirs, ro_np, kind,
+                                                                    7.0, want_close=True)
+    gud = gu.cuda()
+    ncb = cs.shape[0] if dirs & 2 else None
+    out = m.swiglu_quantize_bwd(dy.cuda(), gud[:, :K], gud[:, K:], None if sc is None else sc.cuda(),
+                                rowwise=bool(dirs & 1), colwise=bool(dirs & 2), row_off=row_off,
+                                block_off=block_off, n_col_blocks=ncb, clamped=clamped, dense=dense,
+                                want_dscale=want_ds)
+    torch.cuda.synchronize()
+    rep = {}
+    closeb = close != 0
+    if dirs & 1:
+        compare_mx("bwd.row", np_u8(out[0]), np_u8(out[2]), rc, rs, closeb, True, report=rep)
+    if dirs & 2:
+        compare_mx("bwd.col", np_u8(out[1]), np_u8(out[3]), cc, cs, closeb, False, rowblock_of(M, ro_np), report=rep)
+    if dense:
+        dd = bits(out[4])
+        compare_bf16("dgate", dd[:, :K], dg, closeb[:, :K], rep)
+        compare_bf16("dup", dd[:, K:], du, closeb[:, K:], rep)
+    if want_ds:
+        gds = out[5].cpu().numpy().astype(np.float64)
+        err = np.abs(gds - ds.astype(np.float64))
+        assert np.all(err <= tol + 1e-30), f"dscale off by {err.max()} (tol {tol[np.argmax(err)]})"
+        rep["dscale.maxerr"] = float(err.max())
+    return rep
+
+
+BWD_SHAPES = [(96, 64), (100, 64), (33, 32), (64, 2048), (40, 7168), (256, 768)]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES)
+@pytest.mark.parametrize("d", ["none", "row", "col", "both"])
+def test_backward(mxq, shape, d):
+    M, K = shape
+    gu = W.packed_gate_up(M, K, seed=2 * M + K)
+    sc = W.row_scale(M, seed=2 * M + K)
+    dy = W.grad_out(M, K, seed=2 * M + K)
+    say("bwd", shape, d)
+    dirs = {"none": 0, "row": 1, "col": 2, "both": 3}[d]
+    rep = run_bwd_and_compare(mxq, gu, sc, dy, K, dirs, False)
+    say("  ", rep)
+
+
+@pytest.mark.parametrize("d", ["row", "both"])
+def test_backward_clamped(mxq, d):
+    gu = W.packed_gate_up(128, 256, seed=14, std=4.0)
+    sc = W.row_scale(128, seed=14)
+    dy = W.grad_out(128, 256, seed=14)
+    run_bwd_and_compare(mxq, gu, sc, dy, 256, dirs_of(d), True)
+
+
+def test_backward_grouped_both(mxq):
+    splits = [33, 0, 31, 1, 64, 0, 7]
+    M = sum(splits)
+    gu = W.packed_gate_up(M, 128, seed=15)
+    sc = W.row_scale(M, seed=15)
+    dy = W.grad_out(M, 128, seed=15)
+    run_bwd_and_compare(mxq, gu, sc, dy, 128, 3, False, splits=splits)
+
+
+def test_backward_dscale_only_and_quant_only(mxq):
+    gu = W.packed_gate_up(64, 128, seed=16)
+    sc = W.row_scale(64, seed=16)
+    dy = W.grad_out(64, 128, seed=16)
+    run_bwd_and_compare(mxq, gu, sc, dy, 128, 0, False, dense=False, want_ds=True)
+    run_bwd_and_compare(mxq, gu, sc, dy, 128, 3, False, dense=False, want_ds=False)
+
+
+def test_backward_large_magnitudes(mxq):
+    gu = W.packed_gate_up(64, 256, seed=17, std=20.0)
+    sc = W.row_scale(64, seed=17)
+    dy = W.grad_out(64, 256, seed=17)
+    run_bwd_and_compare(mxq, gu, sc, dy, 256, 3, False)
+
+
+def test_silu_exhaustive_through_dup(mxq):
+    """dup = bf16(dh * s * a) with dh = s = 1 is a = bf16(silu(g)) itself: all
+    65,280 finite bf16 gate values, bit-exact against the oracle."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = (allb.astype(np.uint32) << 16).view(np.float32)
+    g = allb[np.isfinite(vals)].reshape(-1, 32)
+    M = g.shape[0]
+    u = np.full_like(g, 0x3F80)
+    dh = np.full_like(g, 0x3F80)
+    a = O.swiglu_fwd(g, u)
+    gg, uu, dd = (W.from_bits(x, "cuda") for x in (g, u, dh))
+    out = mxq.swiglu_quantize_bwd(dd, gg, uu, None, rowwise=False, colwise=False, dense=True, want_dscale=False)
+    torch.cuda.synchronize()
+    dup = bits(out[4])[:, 32:]
+    nan = ((dup & 0x7FFF) > 0x7F80) & ((a & 0x7FFF) > 0x7F80)
+    mism = (dup != a) & ~nan
+    assert not mism.any(), f"{int(mism.sum())} silu mismatches, e.g. g bits {g[mism][:5]}"
+
+
+def test_backward_deterministic(mxq):
+    gu = W.packed_gate_up(512, 7168, seed=18).cuda()
+    sc = W.row_scale(512, seed=18).cuda()
+    dy = W.grad_out(512, 7168, seed=18).cuda()
+    K = 7168
+    a = mxq.swiglu_quantize_bwd(dy, gu[:, :K], gu[:, K:], sc, rowwise=True, colwise=True)
+    b = mxq.swiglu_quantize_bwd(dy, gu[:, :K], gu[:, K:], sc, rowwise=True, colwise=True)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
+                           y.view(torch.uint8) if y.dtype != torch.uint8 else y)
+
+
+# ------------------------------------------------------------------ full sizes (sampled)
+
+@pytest.mark.parametrize("shape", [(4096, 2048), (4096, 7168), (16384, 7168)])
+def test_full_size_sampled_stripes(mxq, shape):
+    """The benchmark's shapes in the benchmark's launch configuration (both
+    directions, packed [gate | up]); the oracle checks 3 sampled 32-row
+    stripes of every output."""
+    M, K = shape
+    say("full", shape)
+    gu = W.packed_gate_up(M, K, seed=0, device="cuda")
+    sc = W.row_scale(M, seed=0, device="cuda")
+    dy = W.grad_out(M, K, seed=0, device="cuda")
+    f = mxq.swiglu_quantize_fwd(gu[:, :K], gu[:, K:], sc, rowwise=True, colwise=True)
+    b = mxq.swiglu_quantize_bwd(dy, gu[:, :K], gu[:, K:], sc, rowwise=True, colwise=True)
+    torch.cuda.synchronize()
+    for stripe in (0, M // 64, M // 32 - 1):
+        r0, r1 = 32 * stripe, 32 * stripe + 32
+        g_np, u_np, d_np = bits(gu[r0:r1, :K]), bits(gu[r0:r1, K:]), bits(dy[r0:r1])
+        s_np = sc[r0:r1].cpu().numpy()
+        rc, cc, rs, cs, h, close = O.swiglu_quantize_fwd(g_np, u_np, s_np, 3, want_close=True)
+        rep = {}
+        compare_mx("fwd.row", np_u8(f[0][r0:r1]), np_u8(f[2][r0:r1]), rc, rs, close != 0, True, report=rep)
+        compare_mx("fwd.col", np_u8(f[1][r0:r1]), np_u8(f[3][stripe:stripe + 1]), cc, cs, close != 0, False,
+                   rowblock_of(32), report=rep)
+        o = O.swiglu_quantize_bwd(d_np, g_np, u_np, s_np, 3, want_close=True)
+        closeb = o[7] != 0
+        compare_mx("bwd.row", np_u8(b[0][r0:r1]), np_u8(b[2][r0:r1]), o[0], o[2], closeb, True, report=rep)
+        compare_mx("bwd.col", np_u8(b[1][r0:r1]), np_u8(b[3][stripe:stripe + 1]), o[1], o[3], closeb, False,
+                   rowblock_of(32), report=rep)
+        dd = bits(b[4][r0:r1])
+        compare_bf16("dgate", dd[:, :K], o[4], closeb[:, :K], rep)
+        compare_bf16("dup", dd[:, K:], o[5], closeb[:, K:], rep)
+        err = np.abs(b[5][r0:r1].cpu().numpy().astype(np.float64) - o[6].astype(np.float64))
+        assert np.all(err <= o[8] + 1e-30)
+        say("  stripe", stripe, rep)
