@@ -180,8 +180,9 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, in
         return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");
     }
     if (dirs & 2) {
-        // exact scale-row count is known only on the device; alias checks use the bound
-        s = check_mx_out(col_out, false, M, K, G > 0 ? nsrows_bound : (M + 31) / 32, "colwise", outs);
+        // the exact scale-row count sum_g ceil(m_g/32) is known only on the
+        // device; the alias check covers the ceil(M/32) rows that always exist
+        s = check_mx_out(col_out, false, M, K, (M + 31) / 32, "colwise", outs);
         if (s != MXQ_OK) return s;
     } else if (col_out != nullptr && col_out->codes != nullptr) {
         return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
@@ -347,7 +348,7 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, con
         return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");
     }
     if (dirs & 2) {
-        if ((s = check_mx_out(col_out, false, M, 2 * K, G > 0 ? nsrows_bound : (M + 31) / 32, "colwise", outs)) != MXQ_OK)
+        if ((s = check_mx_out(col_out, false, M, 2 * K, (M + 31) / 32, "colwise", outs)) != MXQ_OK)
             return s;
     } else if (col_out != nullptr && col_out->codes != nullptr) {
         return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
