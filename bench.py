@@ -1,0 +1,216 @@
+"""Benchmark of the fused SwiGLU + MXFP8 path (and, when built, the grouped GEMM)
+on one MI355X.
+
+One step = every cell of the fused-activation workload once: forward and
+backward, each rowwise / colwise / both, at gate/up shapes (4096, 2048),
+(4096, 7168) and (16384, 7168) (bf16 ~N(0,1) gate/up as views of one packed
+[gate | up] buffer, fp32 row scale ~U(0.5,1.5), bf16 grad ~N(0,1e-2)); the
+shapes are interleaved so that consecutive cells never reuse cached inputs.
+value = algorithmic bytes of the step / step time, in GB/s (inputs read once,
+outputs written once; forward 4 + n_dir*(1 + 1/32) B per element + 4 B per
+row, backward 10 + 2*n_dir*(1 + 1/32) B per element + 8 B per row, the
+backward writing the bf16 dgate/dup and the fp32 dscale too).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+SHAPES = [(4096, 2048), (4096, 7168), (16384, 7168)]
+DIRS = [("row", 1), ("col", 2), ("both", 3)]
+HBM_PEAK_GBS = 8000.0
+DOMINANT = ("bwd", "both", (16384, 7168))
+
+
+def fwd_bytes(M, K, nd):
+    return M * K * (4 + nd * (1 + 1 / 32)) + 4 * M
+
+
+def bwd_bytes(M, K, nd):
+    return M * K * (10 + 2 * nd * (1 + 1 / 32)) + 8 * M
+
+
+def ndir(d):
+    return (d & 1) + ((d >> 1) & 1)
+
+
+class Cell:
+    """One (pass, direction, shape) call with its outputs preallocated."""
+
+    def __init__(self, m, torch, data, kind, dname, dirs, shape):
+        M, K = shape
+        self.kind, self.dname, self.dirs, self.shape = kind, dname, dirs, shape
+        gu, sc, dy = data[shape]
+        g, u = gu[:, :K], gu[:, K:]
+        act = m.make_act()
+        if kind == "fwd":
+            rc, cc, rs, cs = m._alloc_mx(M, K, dirs, (M + 31) // 32, "cuda")
+            ro, co = m._outs(rc, cc, rs, cs, dirs)
+            self.keep = (rc, cc, rs, cs, ro, co, act)
+            self.fn = lambda: m.mxq_swiglu_quantize_fwd(act, g, u, sc, None, dirs, ro, co)
+            self.bytes = fwd_bytes(M, K, ndir(dirs))
+        else:
+            rc, cc, rs, cs = m._alloc_mx(M, 2 * K, dirs, (M + 31) // 32, "cuda")
+            ro, co = m._outs(rc, cc, rs, cs, dirs)
+            dd = torch.empty((M, 2 * K), dtype=torch.bfloat16, device="cuda")
+            ds = torch.empty(M, dtype=torch.float32, device="cuda")
+            nws = m.mxq_swiglu_quantize_bwd_workspace(M, K, dirs)
+            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+            self.keep = (rc, cc, rs, cs, ro, co, dd, ds, ws, act)
+            self.fn = lambda: m.mxq_swiglu_quantize_bwd(act, dy, g, u, sc, None, dd[:, :K], dd[:, K:], ds,
+                                                        dirs, ro, co, ws)
+            self.bytes = bwd_bytes(M, K, ndir(dirs))
+
+    def key(self):
+        return (self.kind, self.dname, self.shape)
+
+
+def build_cells(m, torch, W):
+    data = {}
+    for (M, K) in SHAPES:
+        data[(M, K)] = (W.packed_gate_up(M, K, seed=0, device="cuda"), W.row_scale(M, seed=0, device="cuda"),
+                        W.grad_out(M, K, seed=0, device="cuda"))
+    cells = []
+    for kind in ("fwd", "bwd"):
+        for dname, d in DIRS:
+            for shape in SHAPES:
+                cells.append(Cell(m, torch, data, kind, dname, d, shape))
+    return cells, data
+
+
+def cpu_baseline(rows=256):
+    """The CPU oracle (single-threaded C, fp64) over a bounded sample: the
+    first `rows` rows of every cell of the step (same byte model)."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    total_bytes = 0.0
+    t0 = time.perf_counter()
+    for (M, K) in SHAPES:
+        gu = W.packed_gate_up(rows, K, seed=0)
+        sc = W.row_scale(rows, seed=0).numpy()
+        dy = W.bf16_bits(W.grad_out(rows, K, seed=0))
+        g, u = W.bf16_bits(gu[:, :K]), W.bf16_bits(gu[:, K:])
+        for _, d in DIRS:
+            O.swiglu_quantize_fwd(g, u, sc, d)
+            O.swiglu_quantize_bwd(dy, g, u, sc, d)
+            total_bytes += fwd_bytes(rows, K, ndir(d)) + bwd_bytes(rows, K, ndir(d))
+    dt = time.perf_counter() - t0
+    _ = np
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} rows of each of the 18 fused fwd/bwd cells "
+                      f"({total_bytes / 1e6:.1f} MB algorithmic), {dt:.1f} s on 1 host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the fused path shards by rows with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import swiglu_mxfp8_quant_amd as m
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cells, _data = build_cells(m, torch, W)
+    stream = torch.cuda.current_stream()
+    dom = [c for c in cells if c.key() == DOMINANT][0]
+
+    def step(ev=None):
+        for c in cells:
+            if c is dom and ev is not None:
+                ev[0].record(stream)
+                m.check(c.fn())
+                ev[1].record(stream)
+            else:
+                m.check(c.fn())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # the timed region: exactly `steps` steps, synchronized on both sides;
+    # the dominant kernel is bracketed by events on its own stream
+    dom_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(dom_ev[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dom_us = sum(a.elapsed_time(b) for a, b in dom_ev) / args.steps * 1e3
+
+    step_bytes = sum(c.bytes for c in cells)
+    ms_per_step = dt / args.steps * 1e3
+    value = step_bytes / (dt / args.steps) / 1e9
+
+    # per-cell device times (outside the timed region, for the record)
+    per_cell = {}
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for c in cells:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(3):
+            flush.zero_()   # evict the 256 MB Infinity Cache and the L2s
+            e0.record(stream)
+            m.check(c.fn())
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = sorted(ts)[1]
+        per_cell[f"{c.kind}.{c.dname}.{c.shape[0]}x{c.shape[1]}"] = {
+            "us": round(us, 2), "GBps": round(c.bytes / us / 1e3, 1)}
+
+    achieved = dom.bytes / dom_us / 1e3
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tf):
+        try:
+            traffic = json.load(open(tf)).get("bwd_both_16384x7168")
+        except Exception:
+            traffic = None
+    out = {
+        "metric": "fused SwiGLU+MXFP8 quant GB/s (% HBM peak); grouped GEMM TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fused row-scaled SwiGLU + MXFP8 fwd and bwd, rowwise/colwise/both, "
+                               "gate/up (4096,2048), (4096,7168), (16384,7168), packed [gate|up]",
+                   "cells": len(cells), "step_bytes": int(step_bytes),
+                   "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 1)},
+        "roofline": {"kernel": "mxq_swiglu_quantize_bwd both (16384,7168)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": int(dom.bytes), "avg_launch_us": round(dom_us, 2)},
+        "per_cell": per_cell,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

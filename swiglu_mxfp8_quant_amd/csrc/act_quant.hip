@@ -110,10 +110,10 @@ __device__ __forceinline__ Sig sig_fast(float g) {
 // g > 80 the fast value is g itself, which is also the correctly rounded one.
 __device__ __forceinline__ bool silu_risky(float g, float t) {
     const uint32_t ag = __float_as_uint(g) & 0x7FFFFFFFu;
-    const bool out = (g < -80.0f) || (ag - 1u < 0x04800000u - 1u);
+    const bool out = (bool)((int)(g < -80.0f) | (int)(ag - 1u < 0x04800000u - 1u));
     const float margin = fminf(fmaf(2.0f, fabsf(g), 8.0f), 168.0f);
     const int d = (int)(__float_as_uint(t) & 0xFFFFu) - 0x8000;
-    return out || (float)abs(d) <= margin;
+    return (bool)((int)out | (int)((float)abs(d) <= margin));
 }
 
 // May bf16(hs), hs = fl32(p * s) with p exact, differ from the bf16 rounding of
@@ -121,7 +121,7 @@ __device__ __forceinline__ bool silu_risky(float g, float t) {
 // normal-or-zero (underflow, overflow, NaN/Inf inputs).
 __device__ __forceinline__ bool product_risky(float p, float hs) {
     const bool tie = (__float_as_uint(hs) & 0xFFFFu) == 0x8000u;
-    return tie || !__builtin_amdgcn_class(p, kNormalOrZero) || !__builtin_amdgcn_class(hs, kNormalOrZero);
+    return (bool)((int)tie | (int)!__builtin_amdgcn_class(p, kNormalOrZero) | (int)!__builtin_amdgcn_class(hs, kNormalOrZero));
 }
 
 // ------------------------------------------------------------------ quantizer
@@ -297,7 +297,22 @@ __device__ __forceinline__ uint32_t set_half(uint32_t w, int hi, uint32_t v) {
 
 __device__ __forceinline__ float bf16_at(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
 
+
 // ------------------------------------------------------------------ forward
+//
+// Work split: a workgroup of 4 waves owns one colwise block of up to 32 rows
+// (restarting at every group) and a slab of 512 columns; wave w owns rows
+// 8w..8w+7 of the block and each lane 8 consecutive columns (16-byte loads).
+// All 8 rows' loads are issued before any arithmetic, so a wave keeps 16 KB
+// in flight.  The 1x32 amax is a DPP max over 4 lanes; the 32x1 amax is the
+// max of the 4 waves' 8-row partial maxima, exchanged through LDS.
+
+constexpr int CPT = 8;      // columns per lane
+constexpr int RPW = 8;      // rows per wave
+constexpr int NWAVE = 4;    // waves per workgroup
+constexpr int TROWS = RPW * NWAVE;  // rows per tile (one colwise block)
+constexpr int SLAB = 64 * CPT;      // columns per workgroup
+constexpr int NWORDS = RPW * CPT / 32;  // risk mask words per lane
 
 // One element pair of the forward: packed gate / up words -> packed h word.
 // Returns a 2-bit mask of the elements that need the exact path.
@@ -319,8 +334,8 @@ __device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, 
         const float h0 = p0 * s, h1 = p1 * s;
         hw = pack_bf16(h0, h1);
         uint32_t risky = 0u;
-        if (silu_risky(g0, t0) || product_risky(p0, h0)) risky |= 1u;
-        if (silu_risky(g1, t1) || product_risky(p1, h1)) risky |= 2u;
+        risky |= (uint32_t)silu_risky(g0, t0) | (uint32_t)product_risky(p0, h0);
+        risky |= ((uint32_t)silu_risky(g1, t1) | (uint32_t)product_risky(p1, h1)) << 1;
         return risky;
     }
 }
@@ -336,19 +351,18 @@ __device__ __forceinline__ uint32_t fwd_elem_f64(float g, float u, float s, floa
     return bf16_from_f64((double)a * (double)u * (double)s);
 }
 
-template <int ACT, int CPT, int ROWS>
-__device__ __forceinline__ void fwd_fix(const FwdArgs &a, const Tile &T, int c0,
-                                        const uint32_t *risk, uint32_t (&h)[ROWS][CPT / 2], uint32_t *q) {
-    constexpr int NW = risk_words<ROWS, CPT>();
+template <int ACT>
+__device__ __forceinline__ void fwd_fix(const FwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
+                                        uint32_t (&h)[RPW][CPT / 2], uint32_t *q) {
     int total = 0;
 #pragma unroll
-    for (int w = 0; w < NW; w++) total += __builtin_popcount(risk[w]);
+    for (int w = 0; w < NWORDS; w++) total += __builtin_popcount(risk[w]);
     for (int base = 0; base < total; base += kFixQ) {
-        const int nq = fix_gather<NW>(risk, base, q);
+        const int nq = fix_gather<NWORDS>(risk, base, q);
 #pragma unroll 1
         for (int j = 0; j < nq; j++) {
             const int idx = (int)q[j];
-            const int64_t r = T.r0 + idx / CPT, c = c0 + idx % CPT;
+            const int64_t r = rbase + idx / CPT, c = c0 + idx % CPT;
             const float g = bf16_at(a.gate + r * a.ld_gate + c);
             const float u = bf16_at(a.up + r * a.ld_up + c);
             const float s = a.row_scale != nullptr ? a.row_scale[r] : 1.0f;
@@ -356,7 +370,7 @@ __device__ __forceinline__ void fwd_fix(const FwdArgs &a, const Tile &T, int c0,
         }
         int rank = 0;
 #pragma unroll
-        for (int i = 0; i < ROWS; i++) {
+        for (int i = 0; i < RPW; i++) {
             const uint32_t rb = row_bits<CPT>(risk, i);
             if (rb) {
 #pragma unroll
@@ -374,134 +388,151 @@ __device__ __forceinline__ void fwd_fix(const FwdArgs &a, const Tile &T, int c0,
 // Is the row scale s safe for the fast product path (finite, normal or zero)?
 __device__ __forceinline__ bool scale_ok(float s) { return __builtin_amdgcn_class(s, kNormalOrZero); }
 
-template <int ACT, int DIRS, int CPT, int ROWS>
+// Scale bytes and NaN masks of CPT columns from their packed |bf16| maxima.
+struct ColScales {
+    uint32_t E[CPT];
+    float s[CPT];
+    uint32_t nan[CPT / 4];
+};
+__device__ __forceinline__ ColScales col_scales(const uint32_t *cm) {
+    ColScales c;
+#pragma unroll
+    for (int k = 0; k < CPT / 2; k++) {
+        c.E[2 * k] = e8m0_from_amax_bits(cm[k] & 0xFFFFu);
+        c.E[2 * k + 1] = e8m0_from_amax_bits(cm[k] >> 16);
+    }
+#pragma unroll
+    for (int k = 0; k < CPT; k++) c.s[k] = scale_operand(c.E[k]);
+#pragma unroll
+    for (int q = 0; q < CPT / 4; q++) {
+        c.nan[q] = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; j++) c.nan[q] |= (c.E[4 * q + j] == 0xFFu ? 0xFFu : 0u) << (8 * j);
+    }
+    return c;
+}
+
+__device__ __forceinline__ void store_scale_bytes(uint8_t *p, const uint32_t *E) {
+    uint32_t sb[CPT / 4];
+#pragma unroll
+    for (int q = 0; q < CPT / 4; q++)
+        sb[q] = E[4 * q] | (E[4 * q + 1] << 8) | (E[4 * q + 2] << 16) | (E[4 * q + 3] << 24);
+    store_codes<CPT>(p, sb);
+}
+
+// combine the 4 waves' partial column maxima (cmx[wave][lane][k]) for one lane
+__device__ __forceinline__ void colmax_exchange(uint32_t (*cmx)[64][CPT / 2], int wave, int lane, uint32_t *cm) {
+#pragma unroll
+    for (int k = 0; k < CPT / 2; k++) cmx[wave][lane][k] = cm[k];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CPT / 2; k++) {
+        uint32_t v = cmx[0][lane][k];
+#pragma unroll
+        for (int w = 1; w < NWAVE; w++) v = umax16x2(v, cmx[w][lane][k]);
+        cm[k] = v;
+    }
+}
+
+template <int ACT, int DIRS>
 __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a, int64_t nslabs) {
-    constexpr int LPB = 32 / CPT;
-    constexpr int NW = risk_words<ROWS, CPT>();
-    constexpr int PF = 4;  // rows of loads kept in flight
     __shared__ uint32_t fixq[256 * kFixQ];
+    __shared__ uint32_t cmx[NWAVE][64][CPT / 2];
     const int64_t bid = blockIdx.x;
     const int64_t t = bid / nslabs;
     const int64_t slab = bid - t * nslabs;
     const int tid = threadIdx.x;
-    const int co = (int)((slab * (int64_t)blockDim.x + tid) * CPT);  // this lane's first column (K < 2^30)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
+    const int co = (int)(slab * SLAB) + lane * CPT;
     const bool active = co < a.K;
-    const Tile T = tile_rows<ROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
+    const Tile T = tile_rows<TROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
     if (T.n == 0) return;  // uniform over the workgroup
-    // uniform row bases; lanes add their 32-bit column offset
-    const uint16_t *gate0 = a.gate + T.r0 * a.ld_gate;
-    const uint16_t *up0 = a.up + T.r0 * a.ld_up;
+    const int nrow = min(max(T.n - wave * RPW, 0), RPW);  // rows of this wave (uniform per wave)
+    const int64_t rbase = T.r0 + wave * RPW;
+    const uint16_t *gate0 = a.gate + rbase * a.ld_gate;
+    const uint16_t *up0 = a.up + rbase * a.ld_up;
 
-    // pass 1: the tile on the fast path
-    uint32_t h[ROWS][CPT / 2];
-    uint32_t risk[NW];
+    // pass 1: all loads of the wave's rows, then the fast path
+    Vec<CPT> gv[RPW], uv[RPW];
 #pragma unroll
-    for (int w = 0; w < NW; w++) risk[w] = 0u;
-    Vec<CPT> gb[PF], ub[PF];
-#pragma unroll
-    for (int i = 0; i < PF; i++) {
-        gb[i] = zero_vec<CPT>();
-        ub[i] = zero_vec<CPT>();
-        if (i < ROWS && i < T.n && active) {
-            gb[i] = load_vec<CPT>(gate0 + i * a.ld_gate + co);
-            if constexpr (ACT != ACT_IDENTITY) ub[i] = load_vec<CPT>(up0 + i * a.ld_up + co);
+    for (int i = 0; i < RPW; i++) {
+        gv[i] = zero_vec<CPT>();
+        uv[i] = zero_vec<CPT>();
+        if (i < nrow && active) {
+            gv[i] = load_vec<CPT>(gate0 + i * a.ld_gate + co);
+            if constexpr (ACT != ACT_IDENTITY) uv[i] = load_vec<CPT>(up0 + i * a.ld_up + co);
         }
     }
+    uint32_t h[RPW][CPT / 2];
+    uint32_t risk[NWORDS];
 #pragma unroll
-    for (int i = 0; i < ROWS; i++) {
-        if (i < T.n) {
-            const Vec<CPT> gv = gb[i % PF], uv = ub[i % PF];
-            if (i + PF < ROWS && i + PF < T.n && active) {
-                gb[i % PF] = load_vec<CPT>(gate0 + (i + PF) * a.ld_gate + co);
-                if constexpr (ACT != ACT_IDENTITY) ub[i % PF] = load_vec<CPT>(up0 + (i + PF) * a.ld_up + co);
-            }
-            float s = 1.0f;
-            if constexpr (ACT != ACT_IDENTITY)
-                if (a.row_scale != nullptr) s = a.row_scale[T.r0 + i];
-            uint32_t bits = 0u;
+    for (int w = 0; w < NWORDS; w++) risk[w] = 0u;
 #pragma unroll
-            for (int k = 0; k < CPT / 2; k++) bits |= fwd_pair<ACT>(gv.w[k], uv.w[k], s, a.limit, h[i][k]) << (2 * k);
-            if constexpr (ACT != ACT_IDENTITY) {
-                if (!scale_ok(s)) bits = (1u << CPT) - 1u;
-                if (!active) bits = 0u;
-                risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
-            }
-        } else {
+    for (int i = 0; i < RPW; i++) {
+        float s = 1.0f;
+        if constexpr (ACT != ACT_IDENTITY)
+            if (a.row_scale != nullptr && i < nrow) s = a.row_scale[rbase + i];
+        uint32_t bits = 0u;
 #pragma unroll
-            for (int k = 0; k < CPT / 2; k++) h[i][k] = 0u;
+        for (int k = 0; k < CPT / 2; k++) bits |= fwd_pair<ACT>(gv[i].w[k], uv[i].w[k], s, a.limit, h[i][k]) << (2 * k);
+        if constexpr (ACT != ACT_IDENTITY) {
+            if (!scale_ok(s)) bits = (1u << CPT) - 1u;
+            if (!active || i >= nrow) bits = 0u;
+            risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 
     // the rare exact-path elements
-    if constexpr (ACT != ACT_IDENTITY) fwd_fix<ACT, CPT, ROWS>(a, T, co, risk, h, fixq + tid * kFixQ);
+    if constexpr (ACT != ACT_IDENTITY) fwd_fix<ACT>(a, rbase, co, risk, h, fixq + tid * kFixQ);
 
-    // pass 2: rowwise outputs and column maxima (lanes past K hold zeros and
-    // form whole 32-column groups of their own, so they never mix in)
-    uint32_t colmax[CPT / 2];
+    // pass 2: rowwise outputs and the wave's column maxima (rows past the
+    // tile and lanes past K hold zeros; the latter form whole 32-column
+    // groups of their own, so they never mix in)
+    uint32_t cm[CPT / 2];
 #pragma unroll
-    for (int k = 0; k < CPT / 2; k++) colmax[k] = 0u;
+    for (int k = 0; k < CPT / 2; k++) cm[k] = 0u;
 #pragma unroll
-    for (int i = 0; i < ROWS; i++) {
-        if (i < T.n) {
-            uint32_t m = 0u;
+    for (int i = 0; i < RPW; i++) {
+        uint32_t m = 0u;
 #pragma unroll
-            for (int k = 0; k < CPT / 2; k++) {
-                const uint32_t mag = h[i][k] & 0x7FFF7FFFu;
-                if constexpr (DIRS & 2) colmax[k] = umax16x2(colmax[k], mag);
-                m = umax16x2(m, mag);
-            }
-            if constexpr (DIRS & 1) {
-                m = block_max<LPB>(max(m & 0xFFFFu, m >> 16));
+        for (int k = 0; k < CPT / 2; k++) {
+            const uint32_t mag = i < nrow ? (h[i][k] & 0x7FFF7FFFu) : 0u;
+            if constexpr (DIRS & 2) cm[k] = umax16x2(cm[k], mag);
+            m = umax16x2(m, mag);
+        }
+        if constexpr (DIRS & 1) {
+            if (i < nrow) {
+                m = block_max<4>(max(m & 0xFFFFu, m >> 16));
                 const uint32_t E = e8m0_from_amax_bits(m);
                 uint32_t c[CPT / 4];
 #pragma unroll
                 for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_same(h[i][2 * q], h[i][2 * q + 1], E);
                 if (active) {
-                    const int64_t r = T.r0 + i;
+                    const int64_t r = rbase + i;
                     store_codes<CPT>(a.row.codes + r * a.row.ld_codes + co, c);
-                    if ((tid & (LPB - 1)) == 0) a.row.scales[r * a.row.ld_scales + co / 32] = (uint8_t)E;
+                    if ((lane & 3) == 0) a.row.scales[r * a.row.ld_scales + co / 32] = (uint8_t)E;
                 }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 
     // pass 3: colwise outputs
     if constexpr (DIRS & 2) {
+        colmax_exchange(cmx, wave, lane, cm);
         if (!active) return;
-        float sc[CPT];
-        uint32_t nan[CPT / 4];
-        uint32_t Eb[CPT];
+        const ColScales cs = col_scales(cm);
+        uint8_t *colc = a.col.codes + rbase * a.col.ld_codes;
 #pragma unroll
-        for (int k = 0; k < CPT / 2; k++) {
-            Eb[2 * k] = e8m0_from_amax_bits(colmax[k] & 0xFFFFu);
-            Eb[2 * k + 1] = e8m0_from_amax_bits(colmax[k] >> 16);
-        }
-#pragma unroll
-        for (int k = 0; k < CPT; k++) sc[k] = scale_operand(Eb[k]);
-#pragma unroll
-        for (int q = 0; q < CPT / 4; q++) {
-            nan[q] = 0u;
-#pragma unroll
-            for (int j = 0; j < 4; j++) nan[q] |= (Eb[4 * q + j] == 0xFFu ? 0xFFu : 0u) << (8 * j);
-        }
-        uint8_t *colc = a.col.codes + T.r0 * a.col.ld_codes;
-#pragma unroll
-        for (int i = 0; i < ROWS; i++) {
-            if (i < T.n) {
+        for (int i = 0; i < RPW; i++) {
+            if (i < nrow) {
                 uint32_t c[CPT / 4];
 #pragma unroll
-                for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_cols(h[i][2 * q], h[i][2 * q + 1], sc + 4 * q, nan[q]);
+                for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_cols(h[i][2 * q], h[i][2 * q + 1], cs.s + 4 * q, cs.nan[q]);
                 store_codes<CPT>(colc + i * a.col.ld_codes + co, c);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
-        uint32_t sb[CPT / 4];
-#pragma unroll
-        for (int q = 0; q < CPT / 4; q++)
-            sb[q] = Eb[4 * q] | (Eb[4 * q + 1] << 8) | (Eb[4 * q + 2] << 16) | (Eb[4 * q + 3] << 24);
-        store_codes<CPT>(a.col.scales + T.srow * a.col.ld_scales + co, sb);
+        if (wave == 0) store_scale_bytes(a.col.scales + T.srow * a.col.ld_scales + co, cs.E);
     }
 }
 
@@ -529,7 +560,7 @@ __device__ __forceinline__ float dsilu_err(float g, float sig, float one_minus) 
 // covers the ties of the neighbouring intervals.
 __device__ __forceinline__ bool near_tie(float t, float bound) {
     const float tie = __uint_as_float((__float_as_uint(t) & 0xFFFF0000u) | 0x8000u);
-    return fabsf(t - tie) <= bound || bound > fabsf(t) * 0x1p-10f;
+    return (bool)((int)(fabsf(t - tie) <= bound) | (int)(bound > fabsf(t) * 0x1p-10f));
 }
 
 template <int ACT>
@@ -571,11 +602,11 @@ __device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t u
         const float ds = sg[j] * (1.0f + g[j] * om[j]);
         const float tdg = P * ds * mg[j];
         vdg[j] = tdg;
-        bool r = silu_risky(g[j], t[j]) || product_risky(q, qs);
-        r = r || !__builtin_amdgcn_class(du_, kNormalOrZero) || !__builtin_amdgcn_class(P, kNormalOrZero) ||
-            !__builtin_amdgcn_class(tdg, kNormalOrZero);
-        r = r || (mg[j] != 0.0f && near_tie(tdg, fabsf(P) * dsilu_err(g[j], sg[j], om[j]) + fabsf(tdg) * 0x1p-21f));
-        if (r) out.risky |= 1u << j;
+        uint32_t r = (uint32_t)silu_risky(g[j], t[j]) | (uint32_t)product_risky(q, qs);
+        r |= (uint32_t)!__builtin_amdgcn_class(du_, kNormalOrZero) | (uint32_t)!__builtin_amdgcn_class(P, kNormalOrZero) |
+             (uint32_t)!__builtin_amdgcn_class(tdg, kNormalOrZero);
+        r |= (uint32_t)(mg[j] != 0.0f) & (uint32_t)near_tie(tdg, fabsf(P) * dsilu_err(g[j], sg[j], om[j]) + fabsf(tdg) * 0x1p-21f);
+        out.risky |= r << j;
     }
     out.dg = pack_bf16(vdg[0], vdg[1]);
     out.du = pack_bf16(vdu[0], vdu[1]);
@@ -609,20 +640,26 @@ __device__ __forceinline__ uint32_t bwd_elem_f64(float dhf, float gf, float uf, 
     return dgb | (dub << 16);
 }
 
-template <int ACT, int CPT, int ROWS>
-__device__ __forceinline__ void bwd_fix(const BwdArgs &a, const Tile &T, int c0, const uint32_t *risk,
-                                        uint32_t (&hg)[ROWS][CPT / 2], uint32_t (&hu)[ROWS][CPT / 2],
-                                        uint32_t *q, float *qc, float (*red)[257], int tid) {
-    constexpr int NW = risk_words<ROWS, CPT>();
+// The backward splits a 32-row block over 8 waves of 4 rows (512 lanes): its
+// per-element work is about twice the forward's, and 4 rows per wave keep it
+// at ~100 VGPRs (4 waves per SIMD).
+constexpr int BRPW = 4;
+constexpr int BNWAVE = 8;
+constexpr int BNWORDS = BRPW * CPT / 32;
+
+template <int ACT>
+__device__ __forceinline__ void bwd_fix(const BwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
+                                        uint32_t (&hg)[BRPW][CPT / 2], uint32_t (&hu)[BRPW][CPT / 2],
+                                        uint32_t *q, float *qc, float (&dsum)[BRPW]) {
     int total = 0;
 #pragma unroll
-    for (int w = 0; w < NW; w++) total += __builtin_popcount(risk[w]);
+    for (int w = 0; w < BNWORDS; w++) total += __builtin_popcount(risk[w]);
     for (int base = 0; base < total; base += kFixQ) {
-        const int nq = fix_gather<NW>(risk, base, q);
+        const int nq = fix_gather<BNWORDS>(risk, base, q);
 #pragma unroll 1
         for (int j = 0; j < nq; j++) {
             const int idx = (int)q[j];
-            const int64_t r = T.r0 + idx / CPT, c = c0 + idx % CPT;
+            const int64_t r = rbase + idx / CPT, c = c0 + idx % CPT;
             const float d = bf16_at(a.grad + r * a.ld_grad + c);
             const float g = bf16_at(a.gate + r * a.ld_gate + c);
             const float u = bf16_at(a.up + r * a.ld_up + c);
@@ -633,10 +670,9 @@ __device__ __forceinline__ void bwd_fix(const BwdArgs &a, const Tile &T, int c0,
         }
         int rank = 0;
 #pragma unroll
-        for (int i = 0; i < ROWS; i++) {
+        for (int i = 0; i < BRPW; i++) {
             const uint32_t rb = row_bits<CPT>(risk, i);
             if (rb) {
-                float corr = 0.0f;
 #pragma unroll
                 for (int k = 0; k < CPT; k++) {
                     if (rb & (1u << k)) {
@@ -644,126 +680,125 @@ __device__ __forceinline__ void bwd_fix(const BwdArgs &a, const Tile &T, int c0,
                             const uint32_t v = q[rank - base];
                             hg[i][k >> 1] = set_half(hg[i][k >> 1], k & 1, v & 0xFFFFu);
                             hu[i][k >> 1] = set_half(hu[i][k >> 1], k & 1, v >> 16);
-                            corr += qc[rank - base];
+                            dsum[i] += qc[rank - base];
                         }
                         rank++;
                     }
                 }
-                if (red != nullptr) red[i][tid] += corr;
             }
         }
     }
 }
 
-// Backward over one row tile x column slab.  Each lane owns CPT columns j of
-// gate/up/grad; it produces dgate (columns j of [dgate | dup]) and dup
-// (columns K + j).  dscale partials of the workgroup are reduced through LDS
-// in a fixed order (deterministic) and written per (row, slab).
-template <int ACT, int DIRS, int CPT, int ROWS>
-__global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a, int64_t nslabs) {
-    constexpr int LPB = 32 / CPT;
-    constexpr int NW = risk_words<ROWS, CPT>();
-    constexpr int PF = 4;  // rows of loads kept in flight
-    __shared__ float red[ROWS][257];
-    __shared__ float red2[ROWS][9];
-    __shared__ uint32_t fixq[256 * kFixQ];
-    __shared__ float fixc[256 * kFixQ];
+// Backward over one tile x slab (8 waves of 4 rows, else as the forward).  Each lane
+// owns 8 columns j of gate/up/grad and produces dgate (columns j of
+// [dgate | dup]) and dup (columns K + j).  dscale partials are reduced
+// through LDS in a fixed order (deterministic) and written per (row, slab).
+template <int ACT, int DIRS>
+__global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a, int64_t nslabs) {
+    __shared__ uint32_t fixq[512 * kFixQ];
+    __shared__ float fixc[512 * kFixQ];
+    __shared__ uint32_t cmx[2][BNWAVE][64][CPT / 2];
+    __shared__ float red[TROWS][65];
+    __shared__ float red2[TROWS][9];
     const int64_t bid = blockIdx.x;
     const int64_t t = bid / nslabs;
     const int64_t slab = bid - t * nslabs;
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int co = (int)((slab * (int64_t)nthr + tid) * CPT);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
+    const int co = (int)(slab * SLAB) + lane * CPT;
     const bool active = co < a.K;
-    const Tile T = tile_rows<ROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
+    const Tile T = tile_rows<TROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
     if (T.n == 0) return;
+    const int nrow = min(max(T.n - wave * BRPW, 0), BRPW);
+    const int64_t rbase = T.r0 + wave * BRPW;
     const float L = a.limit;
     const int K = (int)a.K;
     const bool dense = a.dgate != nullptr;
     const bool want_ds = a.dscale != nullptr;
-    const uint16_t *grad0 = a.grad + T.r0 * a.ld_grad;
-    const uint16_t *gate0 = a.gate + T.r0 * a.ld_gate;
-    const uint16_t *up0 = a.up + T.r0 * a.ld_up;
 
-    // pass 1: the tile on the fast path
-    uint32_t hg[ROWS][CPT / 2], hu[ROWS][CPT / 2];
-    uint32_t risk[NW];
-#pragma unroll
-    for (int w = 0; w < NW; w++) risk[w] = 0u;
+    // pass 1: the fast path, PF rows of loads kept in flight
+    constexpr int PF = 4;
     Vec<CPT> db[PF], gb[PF], ub[PF];
 #pragma unroll
     for (int i = 0; i < PF; i++) {
         db[i] = gb[i] = ub[i] = zero_vec<CPT>();
-        if (i < ROWS && i < T.n && active) {
-            db[i] = load_vec<CPT>(grad0 + i * a.ld_grad + co);
-            gb[i] = load_vec<CPT>(gate0 + i * a.ld_gate + co);
-            ub[i] = load_vec<CPT>(up0 + i * a.ld_up + co);
+        if (i < nrow && active) {
+            const int64_t r = rbase + i;
+            db[i] = load_vec<CPT>(a.grad + r * a.ld_grad + co);
+            gb[i] = load_vec<CPT>(a.gate + r * a.ld_gate + co);
+            ub[i] = load_vec<CPT>(a.up + r * a.ld_up + co);
         }
     }
+    uint32_t hg[BRPW][CPT / 2], hu[BRPW][CPT / 2];
+    uint32_t risk[BNWORDS];
+    float dsum[BRPW];
 #pragma unroll
-    for (int i = 0; i < ROWS; i++) {
-        if (i < T.n) {
-            const Vec<CPT> dv = db[i % PF], gv = gb[i % PF], uv = ub[i % PF];
-            if (i + PF < ROWS && i + PF < T.n && active) {
-                db[i % PF] = load_vec<CPT>(grad0 + (i + PF) * a.ld_grad + co);
-                gb[i % PF] = load_vec<CPT>(gate0 + (i + PF) * a.ld_gate + co);
-                ub[i % PF] = load_vec<CPT>(up0 + (i + PF) * a.ld_up + co);
-            }
-            const float s = a.row_scale != nullptr ? a.row_scale[T.r0 + i] : 1.0f;
-            uint32_t bits = 0u;
-            float dsum = 0.0f;
+    for (int w = 0; w < BNWORDS; w++) risk[w] = 0u;
 #pragma unroll
-            for (int k = 0; k < CPT / 2; k++) {
-                const BwdPair p = bwd_pair<ACT>(dv.w[k], gv.w[k], uv.w[k], s, L);
-                hg[i][k] = p.dg;
-                hu[i][k] = p.du;
-                dsum += p.dsum;
-                bits |= p.risky << (2 * k);
-            }
-            if (!scale_ok(s)) bits = (1u << CPT) - 1u;
-            if (!active) {
-                bits = 0u;
-                dsum = 0.0f;
-            }
-            risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
-            if (want_ds) red[i][tid] = dsum;
-        } else {
-#pragma unroll
-            for (int k = 0; k < CPT / 2; k++) hg[i][k] = hu[i][k] = 0u;
+    for (int i = 0; i < BRPW; i++) {
+        const Vec<CPT> dv = db[i % PF], gv = gb[i % PF], uv = ub[i % PF];
+        if (i + PF < BRPW && i + PF < nrow && active) {
+            const int64_t r = rbase + i + PF;
+            db[i % PF] = load_vec<CPT>(a.grad + r * a.ld_grad + co);
+            gb[i % PF] = load_vec<CPT>(a.gate + r * a.ld_gate + co);
+            ub[i % PF] = load_vec<CPT>(a.up + r * a.ld_up + co);
         }
+        const float s = (a.row_scale != nullptr && i < nrow) ? a.row_scale[rbase + i] : 1.0f;
+        uint32_t bits = 0u;
+        float ds = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPT / 2; k++) {
+            const BwdPair p = bwd_pair<ACT>(dv.w[k], gv.w[k], uv.w[k], s, L);
+            hg[i][k] = p.dg;
+            hu[i][k] = p.du;
+            ds += p.dsum;
+            bits |= p.risky << (2 * k);
+        }
+        if (!scale_ok(s)) bits = (1u << CPT) - 1u;
+        if (!active || i >= nrow) {
+            bits = 0u;
+            ds = 0.0f;
+        }
+        risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
+        dsum[i] = ds;
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    bwd_fix<ACT, CPT, ROWS>(a, T, co, risk, hg, hu, fixq + tid * kFixQ, fixc + tid * kFixQ,
-                            want_ds ? red : nullptr, tid);
+    bwd_fix<ACT>(a, rbase, co, risk, hg, hu, fixq + tid * kFixQ, fixc + tid * kFixQ, dsum);
+    if (want_ds) {
+        // this lane's dscale partials (corrected by the fix-up) for the reduction
+#pragma unroll
+        for (int i = 0; i < BRPW; i++) red[wave * BRPW + i][lane] = dsum[i];
+    }
 
-    // pass 2: dense outputs, rowwise outputs, column maxima
+    // pass 2: dense outputs, rowwise outputs, the wave's column maxima
     uint32_t cmg[CPT / 2], cmu[CPT / 2];
 #pragma unroll
     for (int k = 0; k < CPT / 2; k++) cmg[k] = cmu[k] = 0u;
 #pragma unroll
-    for (int i = 0; i < ROWS; i++) {
-        if (i < T.n) {
-            const int64_t r = T.r0 + i;
-            if (dense && active) {
-                store_bf16<CPT>(a.dgate + r * a.ld_dgate + co, hg[i]);
-                store_bf16<CPT>(a.dup + r * a.ld_dup + co, hu[i]);
-            }
-            uint32_t mg = 0u, mu = 0u;
+    for (int i = 0; i < BRPW; i++) {
+        const int64_t r = rbase + i;
+        if (dense && active && i < nrow) {
+            store_bf16<CPT>(a.dgate + r * a.ld_dgate + co, hg[i]);
+            store_bf16<CPT>(a.dup + r * a.ld_dup + co, hu[i]);
+        }
+        uint32_t mg = 0u, mu = 0u;
 #pragma unroll
-            for (int k = 0; k < CPT / 2; k++) {
-                const uint32_t ag = hg[i][k] & 0x7FFF7FFFu;
-                const uint32_t au = hu[i][k] & 0x7FFF7FFFu;
-                if constexpr (DIRS & 2) {
-                    cmg[k] = umax16x2(cmg[k], ag);
-                    cmu[k] = umax16x2(cmu[k], au);
-                }
-                mg = umax16x2(mg, ag);
-                mu = umax16x2(mu, au);
+        for (int k = 0; k < CPT / 2; k++) {
+            const uint32_t ag = i < nrow ? (hg[i][k] & 0x7FFF7FFFu) : 0u;
+            const uint32_t au = i < nrow ? (hu[i][k] & 0x7FFF7FFFu) : 0u;
+            if constexpr (DIRS & 2) {
+                cmg[k] = umax16x2(cmg[k], ag);
+                cmu[k] = umax16x2(cmu[k], au);
             }
-            if constexpr (DIRS & 1) {
-                mg = block_max<LPB>(max(mg & 0xFFFFu, mg >> 16));
-                mu = block_max<LPB>(max(mu & 0xFFFFu, mu >> 16));
+            mg = umax16x2(mg, ag);
+            mu = umax16x2(mu, au);
+        }
+        if constexpr (DIRS & 1) {
+            if (i < nrow) {
+                mg = block_max<4>(max(mg & 0xFFFFu, mg >> 16));
+                mu = block_max<4>(max(mu & 0xFFFFu, mu >> 16));
                 const uint32_t Eg = e8m0_from_amax_bits(mg), Eu = e8m0_from_amax_bits(mu);
                 uint32_t cg[CPT / 4], cu[CPT / 4];
 #pragma unroll
@@ -775,7 +810,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a, int64_t nslabs) {
                     uint8_t *rowc = a.row.codes + r * a.row.ld_codes;
                     store_codes<CPT>(rowc + co, cg);
                     store_codes<CPT>(rowc + K + co, cu);
-                    if ((tid & (LPB - 1)) == 0) {
+                    if ((lane & 3) == 0) {
                         uint8_t *rs = a.row.scales + r * a.row.ld_scales;
                         rs[co / 32] = (uint8_t)Eg;
                         rs[(K + co) / 32] = (uint8_t)Eu;
@@ -783,79 +818,67 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a, int64_t nslabs) {
                 }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 
     // pass 3: colwise outputs
     if constexpr (DIRS & 2) {
+#pragma unroll
+        for (int k = 0; k < CPT / 2; k++) {
+            cmx[0][wave][lane][k] = cmg[k];
+            cmx[1][wave][lane][k] = cmu[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < CPT / 2; k++) {
+            uint32_t vg = cmx[0][0][lane][k], vu = cmx[1][0][lane][k];
+#pragma unroll
+            for (int w = 1; w < BNWAVE; w++) {
+                vg = umax16x2(vg, cmx[0][w][lane][k]);
+                vu = umax16x2(vu, cmx[1][w][lane][k]);
+            }
+            cmg[k] = vg;
+            cmu[k] = vu;
+        }
         if (active) {
-            uint32_t Eg[CPT], Eu[CPT];
-            float sg[CPT], su[CPT];
+            const ColScales sg = col_scales(cmg), su = col_scales(cmu);
+            uint8_t *colc = a.col.codes + rbase * a.col.ld_codes;
 #pragma unroll
-            for (int k = 0; k < CPT / 2; k++) {
-                Eg[2 * k] = e8m0_from_amax_bits(cmg[k] & 0xFFFFu);
-                Eg[2 * k + 1] = e8m0_from_amax_bits(cmg[k] >> 16);
-                Eu[2 * k] = e8m0_from_amax_bits(cmu[k] & 0xFFFFu);
-                Eu[2 * k + 1] = e8m0_from_amax_bits(cmu[k] >> 16);
-            }
-            uint32_t ng[CPT / 4], nu[CPT / 4];
-#pragma unroll
-            for (int k = 0; k < CPT; k++) {
-                sg[k] = scale_operand(Eg[k]);
-                su[k] = scale_operand(Eu[k]);
-            }
-#pragma unroll
-            for (int q = 0; q < CPT / 4; q++) {
-                ng[q] = nu[q] = 0u;
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    ng[q] |= (Eg[4 * q + j] == 0xFFu ? 0xFFu : 0u) << (8 * j);
-                    nu[q] |= (Eu[4 * q + j] == 0xFFu ? 0xFFu : 0u) << (8 * j);
-                }
-            }
-            uint8_t *colc = a.col.codes + T.r0 * a.col.ld_codes;
-#pragma unroll
-            for (int i = 0; i < ROWS; i++) {
-                if (i < T.n) {
+            for (int i = 0; i < BRPW; i++) {
+                if (i < nrow) {
                     uint32_t cg[CPT / 4], cu[CPT / 4];
 #pragma unroll
                     for (int q = 0; q < CPT / 4; q++) {
-                        cg[q] = cvt4_cols(hg[i][2 * q], hg[i][2 * q + 1], sg + 4 * q, ng[q]);
-                        cu[q] = cvt4_cols(hu[i][2 * q], hu[i][2 * q + 1], su + 4 * q, nu[q]);
+                        cg[q] = cvt4_cols(hg[i][2 * q], hg[i][2 * q + 1], sg.s + 4 * q, sg.nan[q]);
+                        cu[q] = cvt4_cols(hu[i][2 * q], hu[i][2 * q + 1], su.s + 4 * q, su.nan[q]);
                     }
                     store_codes<CPT>(colc + i * a.col.ld_codes + co, cg);
                     store_codes<CPT>(colc + i * a.col.ld_codes + K + co, cu);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
-            uint32_t sbg[CPT / 4], sbu[CPT / 4];
-#pragma unroll
-            for (int q = 0; q < CPT / 4; q++) {
-                sbg[q] = Eg[4 * q] | (Eg[4 * q + 1] << 8) | (Eg[4 * q + 2] << 16) | (Eg[4 * q + 3] << 24);
-                sbu[q] = Eu[4 * q] | (Eu[4 * q + 1] << 8) | (Eu[4 * q + 2] << 16) | (Eu[4 * q + 3] << 24);
+            if (wave == 0) {
+                uint8_t *cs = a.col.scales + T.srow * a.col.ld_scales;
+                store_scale_bytes(cs + co, sg.E);
+                store_scale_bytes(cs + K + co, su.E);
             }
-            uint8_t *cs = a.col.scales + T.srow * a.col.ld_scales;
-            store_codes<CPT>(cs + co, sbg);
-            store_codes<CPT>(cs + K + co, sbu);
         }
     }
 
     if (want_ds) {
         // deterministic reduction of the workgroup's dscale partials per row:
-        // segment sums of 32 lanes in lane order, then segments in order
+        // 8-lane segment sums in lane order, then the 8 segments in order
         __syncthreads();
-        const int nseg = (nthr + 31) / 32;
-        for (int w = tid; w < ROWS * nseg; w += nthr) {
-            const int row = w % ROWS, seg = w / ROWS;
+        if (tid < 256) {
+            const int row = tid >> 3, seg = tid & 7;
             float acc = 0.0f;
-            const int j1 = min(nthr, seg * 32 + 32);
-            for (int j = seg * 32; j < j1; j++) acc += red[row][j];
+#pragma unroll
+            for (int j = 0; j < 8; j++) acc += red[row][seg * 8 + j];
             red2[row][seg] = acc;
         }
         __syncthreads();
         if (tid < T.n) {
             float acc = 0.0f;
-            for (int seg = 0; seg < nseg; seg++) acc += red2[tid][seg];
+#pragma unroll
+            for (int seg = 0; seg < 8; seg++) acc += red2[tid][seg];
             const int64_t r = T.r0 + tid;
             if (nslabs == 1) a.dscale[r] = acc;
             else a.partials[r * nslabs + slab] = acc;
@@ -872,80 +895,45 @@ __global__ void dscale_finish_kernel(const float *partials, int64_t nslabs, int6
     dscale[r] = acc;
 }
 
-// ------------------------------------------------------------------ launch config
+// ------------------------------------------------------------------ launch
 
-struct Cfg {
-    int threads;
-    int64_t nslabs;
-};
+int64_t slabs_of(int64_t K) { return (K + SLAB - 1) / SLAB; }
 
-// Workgroup width (lanes) for `chunks` column chunks per row: the widest of
-// 256/192/128/64 lanes that leaves the fewest lanes idle.
-Cfg choose_cfg(int64_t chunks) {
-    Cfg best{64, (chunks + 63) / 64};
-    double best_util = -1.0;
-    for (int th : {256, 192, 128, 64}) {
-        const int64_t ns = (chunks + th - 1) / th;
-        const double util = (double)chunks / (double)(ns * th);
-        if (util > best_util + 1e-9) {
-            best_util = util;
-            best = Cfg{th, ns};
-        }
-    }
-    return best;
+int64_t tiles_of(int64_t M, const Groups &g, unsigned dirs) {
+    const bool grouped = (dirs & 2) && g.G > 0;
+    return grouped ? colwise_block_bound(M, g.G) : (M + TROWS - 1) / TROWS;
 }
 
 template <int ACT, int DIRS>
-hipError_t fwd_dispatch_dirs(const FwdArgs &a, hipStream_t stream) {
-    // rowwise-only: 8 rows x 8 columns per lane; colwise / both: 32 rows x 4 columns
-    constexpr int CPT = (DIRS == 1) ? 8 : 4;
-    constexpr int ROWS = (DIRS == 1) ? 8 : 32;
-    const Cfg c = choose_cfg(a.K / CPT);
-    const bool grouped = (DIRS & 2) && a.groups.G > 0;
-    const int64_t ntiles = grouped ? colwise_block_bound(a.M, a.groups.G) : (a.M + ROWS - 1) / ROWS;
-    const int64_t nblocks = ntiles * c.nslabs;
+hipError_t fwd_launch(const FwdArgs &a, hipStream_t stream) {
+    const int64_t ns = slabs_of(a.K);
+    const int64_t nblocks = tiles_of(a.M, a.groups, DIRS) * ns;
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_kernel<ACT, DIRS, CPT, ROWS>), dim3((unsigned)nblocks), dim3(c.threads), 0,
-                       stream, a, c.nslabs);
+    hipLaunchKernelGGL((fwd_kernel<ACT, DIRS>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, ns);
     return hipGetLastError();
 }
 
 template <int ACT>
 hipError_t fwd_dispatch(const FwdArgs &a, hipStream_t stream) {
     switch (a.dirs) {
-        case 1: return fwd_dispatch_dirs<ACT, 1>(a, stream);
-        case 2: return fwd_dispatch_dirs<ACT, 2>(a, stream);
-        default: return fwd_dispatch_dirs<ACT, 3>(a, stream);
+        case 1: return fwd_launch<ACT, 1>(a, stream);
+        case 2: return fwd_launch<ACT, 2>(a, stream);
+        default: return fwd_launch<ACT, 3>(a, stream);
     }
 }
 
-template <int DIRS>
-constexpr int bwd_cpt() { return (DIRS & 2) ? 4 : 8; }
-template <int DIRS>
-constexpr int bwd_rows() { return (DIRS & 2) ? 32 : 8; }
-
-Cfg bwd_cfg(int64_t K, unsigned dirs) {
-    const int cpt = (dirs & 2) ? 4 : 8;
-    return choose_cfg(K / cpt);
-}
-
 template <int ACT, int DIRS>
-hipError_t bwd_dispatch_dirs(const BwdArgs &a, hipStream_t stream) {
-    constexpr int CPT = bwd_cpt<DIRS>();
-    constexpr int ROWS = bwd_rows<DIRS>();
-    const Cfg c = bwd_cfg(a.K, DIRS);
-    const bool grouped = (DIRS & 2) && a.groups.G > 0;
-    const int64_t ntiles = grouped ? colwise_block_bound(a.M, a.groups.G) : (a.M + ROWS - 1) / ROWS;
-    const int64_t nblocks = ntiles * c.nslabs;
+hipError_t bwd_launch(const BwdArgs &a, hipStream_t stream) {
+    const int64_t ns = slabs_of(a.K);
+    const int64_t nblocks = tiles_of(a.M, a.groups, DIRS) * ns;
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_kernel<ACT, DIRS, CPT, ROWS>), dim3((unsigned)nblocks), dim3(c.threads), 0,
-                       stream, a, c.nslabs);
+    hipLaunchKernelGGL((bwd_kernel<ACT, DIRS>), dim3((unsigned)nblocks), dim3(512), 0, stream, a, ns);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.dscale != nullptr && c.nslabs > 1) {
+    if (a.dscale != nullptr && ns > 1) {
         const int64_t nb = (a.M + 255) / 256;
         hipLaunchKernelGGL(dscale_finish_kernel, dim3((unsigned)nb), dim3(256), 0, stream,
-                           (const float *)a.partials, c.nslabs, a.M, a.dscale);
+                           (const float *)a.partials, ns, a.M, a.dscale);
         e = hipGetLastError();
     }
     return e;
@@ -954,10 +942,10 @@ hipError_t bwd_dispatch_dirs(const BwdArgs &a, hipStream_t stream) {
 template <int ACT>
 hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t stream) {
     switch (a.dirs) {
-        case 0: return bwd_dispatch_dirs<ACT, 0>(a, stream);
-        case 1: return bwd_dispatch_dirs<ACT, 1>(a, stream);
-        case 2: return bwd_dispatch_dirs<ACT, 2>(a, stream);
-        default: return bwd_dispatch_dirs<ACT, 3>(a, stream);
+        case 0: return bwd_launch<ACT, 0>(a, stream);
+        case 1: return bwd_launch<ACT, 1>(a, stream);
+        case 2: return bwd_launch<ACT, 2>(a, stream);
+        default: return bwd_launch<ACT, 3>(a, stream);
     }
 }
 
@@ -977,12 +965,7 @@ hipError_t launch_act_quant_bwd(const BwdArgs &a, hipStream_t stream) {
 }
 
 size_t bwd_workspace_bytes(int64_t M, int64_t K) {
-    // the largest slab count over the direction choices
-    int64_t ns = 1;
-    for (unsigned d : {0u, 1u, 2u, 3u}) {
-        const Cfg c = bwd_cfg(K, d);
-        if (c.nslabs > ns) ns = c.nslabs;
-    }
+    const int64_t ns = slabs_of(K);
     return ns > 1 ? (size_t)M * (size_t)ns * sizeof(float) : 0;
 }
 
