@@ -296,3 +296,53 @@ def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False,
                                   dd[:, :K] if dense else None, dd[:, K:] if dense else None, ds,
                                   dirs, ro, co, ws, stream))
     return rc, cc, rs, cs, dd, ds
+
+
+def _operand(data, scales=None, group_dim=False):
+    """mxq_operand from a data tensor (2-D, or 3-D stacked per group) and its
+    E8M0 scale tensor (same rank)."""
+    f8 = data.dtype == _torch().uint8
+    if group_dim:
+        ld = data.stride(1)
+        gs = data.stride(0)
+    else:
+        ld = data.stride(0)
+        gs = 0
+    op = mxq_operand(DTYPE_MXFP8 if f8 else DTYPE_BF16, data.data_ptr(), ld, gs, None, 0, 0)
+    if scales is not None:
+        op.scales = scales.data_ptr()
+        op.ld_scales = scales.stride(1) if group_dim else scales.stride(0)
+        op.scale_gstride = scales.stride(0) if group_dim else 0
+    return op
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def grouped_gemm(mode, row_off, A, B, out, A_scales=None, B_scales=None, block_off=None,
+                 accumulate=False, stream=None):
+    """Run the grouped GEMM.  Shapes (bf16 tensors or uint8 E4M3 codes):
+      NT: A (R, K), B (G, N, K), out (R, N); MXFP8 scales (R, K/32), (G, N, K/32)
+      NN: A (R, K), B (G, K, N), out (R, N); MXFP8 scales (R, K/32), (G, K/32, N)
+      TN: A (R, M), B (R, N), out (G, M, N); MXFP8 scales (n_blocks, M), (n_blocks, N)
+    """
+    G = row_off.numel() - 1
+    if mode == GEMM_TN:
+        R, M = A.shape
+        N = B.shape[1]
+        K = 0
+        args = mxq_gemm_args(mode, G, row_off.data_ptr(), None if block_off is None else block_off.data_ptr(),
+                             M, N, K, R, _operand(A, A_scales), _operand(B, B_scales),
+                             DTYPE_F32 if out.dtype == _torch().float32 else DTYPE_BF16, out.data_ptr(),
+                             out.stride(1), out.stride(0), int(accumulate))
+    else:
+        R, K = A.shape
+        N = B.shape[1] if mode == GEMM_NT else B.shape[2]
+        args = mxq_gemm_args(mode, G, row_off.data_ptr(), None if block_off is None else block_off.data_ptr(),
+                             R, N, K, R, _operand(A, A_scales), _operand(B, B_scales, group_dim=True),
+                             DTYPE_F32 if out.dtype == _torch().float32 else DTYPE_BF16, out.data_ptr(),
+                             out.stride(0), 0, int(accumulate))
+    check(mxq_grouped_gemm(args, None, stream))
+    return out
