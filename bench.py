@@ -85,6 +85,22 @@ def build_cells(m, torch, W):
     return cells, data
 
 
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (profiles/traffic.json), or None when the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    tf = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(tf))["bwd_both_16384x7168"]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(rows=256):
     """The CPU oracle (single-threaded C, fp64) over a bounded sample: the
     first `rows` rows of every cell of the step (same byte model)."""
@@ -115,7 +131,10 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run the dominant call 3 times and a 1 GiB device copy 3 times "
+                         "(for the HBM byte counters of rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
@@ -129,6 +148,17 @@ def main():
     cells, _data = build_cells(m, torch, W)
     stream = torch.cuda.current_stream()
     dom = [c for c in cells if c.key() == DOMINANT][0]
+    if args.traffic_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            m.check(dom.fn())
+        for _ in range(3):
+            dst.copy_(src)   # reference kernel: reads 1 GiB and writes 1 GiB
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "dominant_bytes": int(dom.bytes), "copy_bytes_each_way": 1 << 30}))
+        return
 
     def step(ev=None):
         for c in cells:
@@ -177,13 +207,7 @@ def main():
             "us": round(us, 2), "GBps": round(c.bytes / us / 1e3, 1)}
 
     achieved = dom.bytes / dom_us / 1e3
-    traffic = None
-    tf = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tf):
-        try:
-            traffic = json.load(open(tf)).get("bwd_both_16384x7168")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic()
     out = {
         "metric": "fused SwiGLU+MXFP8 quant GB/s (% HBM peak); grouped GEMM TFLOP/s",
         "value": round(value, 1),
