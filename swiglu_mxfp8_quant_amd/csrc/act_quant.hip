@@ -49,6 +49,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // fp32 classes {-normal, -zero, +zero, +normal} for v_cmp_class_f32
 constexpr int kNormalOrZero = 0x168;
 
+__device__ __forceinline__ bool normal_or_zero(float x) { return __builtin_amdgcn_classf(x, kNormalOrZero); }
+
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -59,6 +61,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     v.y = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
 }
+
+// Materialize x here: keeps the compiler from sinking the packing of a result
+// word past later code (which would keep two fp32 values live instead of one word).
+__device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ uint32_t umax16x2(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
@@ -103,17 +110,22 @@ __device__ __forceinline__ Sig sig_fast(float g) {
 }
 
 // May the fast fp32 silu t of g round to bf16 differently from the exact
-// silu?  For -80 <= g the fast silu's error is below 8 + |g| fp32 ulps (checked
-// over every bf16 g); the margin min(8 + 2|g|, 168) ulps keeps a factor ~2.
-// Outside that range (g < -80, where e^-g overflows, and 0 < |g| < 2^-118,
-// where silu is subnormal-tiny) the element always takes the exact path; for
-// g > 80 the fast value is g itself, which is also the correctly rounded one.
+// silu?  Measured against the exact silu for every bf16 g >= -80, the fast
+// value is within 2.03 fp32 ulps for g >= 0 and within 2.25 + 0.7|g| ulps for
+// g < 0 (the relative error of e^-g, which grows with |g|, reaches sigma only
+// when e^-g is large); the margin 4 + 2 max(-g, 0) ulps covers that with a
+// factor >= 1.78.  t's distance to the tie of its bf16 interval is
+// 32768 - |low 16 bits of t read as int16| ulps, so the test below is
+// "distance <= margin" rearranged into one add and one subtract (their own
+// rounding, under 2^-7 ulp, is inside the slack).  For g < -80 (e^-g near
+// overflow, sigma near the subnormal range) the element always takes the
+// exact path.  Tiny g needs no special case: there sigma = 1/2 exactly and
+// t = g/2 is exact, which is either a bf16 number that the exact silu
+// (larger by ~g^2/4) also rounds to, or sits exactly on a tie (distance 0).
+// For g > 80 the fast value is g itself, also the correctly rounded one.
 __device__ __forceinline__ bool silu_risky(float g, float t) {
-    const uint32_t ag = __float_as_uint(g) & 0x7FFFFFFFu;
-    const bool out = (bool)((int)(g < -80.0f) | (int)(ag - 1u < 0x04800000u - 1u));
-    const float margin = fminf(fmaf(2.0f, fabsf(g), 8.0f), 168.0f);
-    const int d = (int)(__float_as_uint(t) & 0xFFFFu) - 0x8000;
-    return (bool)((int)out | (int)((float)abs(d) <= margin));
+    const float z = fabsf((float)(short)__float_as_uint(t));
+    return (bool)((int)(g < -80.0f) | (int)((z + fabsf(g)) - g >= 32764.0f));
 }
 
 // May bf16(hs), hs = fl32(p * s) with p exact, differ from the bf16 rounding of
@@ -121,7 +133,7 @@ __device__ __forceinline__ bool silu_risky(float g, float t) {
 // normal-or-zero (underflow, overflow, NaN/Inf inputs).
 __device__ __forceinline__ bool product_risky(float p, float hs) {
     const bool tie = (__float_as_uint(hs) & 0xFFFFu) == 0x8000u;
-    return (bool)((int)tie | (int)!__builtin_amdgcn_class(p, kNormalOrZero) | (int)!__builtin_amdgcn_class(hs, kNormalOrZero));
+    return (bool)((int)tie | (int)!normal_or_zero(p) | (int)!normal_or_zero(hs));
 }
 
 // ------------------------------------------------------------------ quantizer
@@ -254,17 +266,29 @@ __device__ __forceinline__ Tile tile_rows(int64_t t, int64_t M, const Groups &gr
     return T;
 }
 
-// ------------------------------------------------------------------ fix-up queue
+// ------------------------------------------------------------------ exact-path queue
 //
-// Pass 1 of every kernel below computes a whole row tile on the fast path and
-// marks the elements that need the exact path in a per-lane bit mask (bit
-// i * CPT + k for row i, column k).  The fix-up then walks the set bits in
-// order, kFixQ at a time: it records their indices in a per-lane LDS queue,
-// recomputes each one in fp64 (one copy of that code per kernel, in a rolled
-// loop, re-reading the element's inputs from memory), and merges the results
-// back into the register tile with a static pass over the tile.
+// Pass 1 of every kernel below computes a row tile on the fast path and marks
+// the elements whose result might differ from the exact definition in a
+// per-lane bit mask (bit i * CPT + k for row i, column k).  Right after each
+// row, if any lane of the wave marked an element of that row, every marking
+// lane appends the element's bf16 inputs and position to its own LDS queue
+// (kQ entries, stored slot-major so the lanes of a wave never conflict).
+// After the tile, a rolled loop recomputes each lane's entries in fp64 (one
+// copy of that code per kernel) and writes the results back into the queue;
+// pass 2 merges them into the register tile, visiting only rows in which
+// some lane has an entry.  A lane with more than kQ marked elements (only
+// adversarial inputs get there) instead takes the slow path below, which
+// walks its whole mask kQ elements at a time and re-reads their inputs from
+// memory.
 
-constexpr int kFixQ = 4;
+constexpr int kQ = 4;
+constexpr int kFixQ = kQ;
+
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0ull; }
+
+// low (hi = 0) or high half of a packed bf16 word
+__device__ __forceinline__ uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xFFFFu); }
 
 template <int ROWS, int CPT>
 constexpr int risk_words() { return (ROWS * CPT + 31) / 32; }
@@ -274,9 +298,10 @@ __device__ __forceinline__ uint32_t row_bits(const uint32_t *risk, int i) {
     return (risk[(i * CPT) / 32] >> ((i * CPT) % 32)) & ((1u << CPT) - 1u);
 }
 
-// Gather the element indices of the set bits of rank [base, base + kFixQ).
-template <int NW>
-__device__ __forceinline__ int fix_gather(const uint32_t *risk, int base, uint32_t *q) {
+// Slow path: gather the element indices of the set bits of rank
+// [base, base + kFixQ) into q[0], q[QS], ... (a lane's column of the queue).
+template <int NW, int QS>
+__device__ __forceinline__ int fix_gather(const uint32_t *risk, int base, uint2 *q) {
     int rank = 0, nq = 0;
 #pragma unroll
     for (int w = 0; w < NW; w++) {
@@ -284,7 +309,7 @@ __device__ __forceinline__ int fix_gather(const uint32_t *risk, int base, uint32
         while (bits) {
             const int b = __builtin_ctz(bits);
             bits &= bits - 1u;
-            if (rank >= base && nq < kFixQ) q[nq++] = (uint32_t)(w * 32 + b);
+            if (rank >= base && nq < kFixQ) q[QS * nq++].x = (uint32_t)(w * 32 + b);
             rank++;
         }
     }
@@ -351,22 +376,26 @@ __device__ __forceinline__ uint32_t fwd_elem_f64(float g, float u, float s, floa
     return bf16_from_f64((double)a * (double)u * (double)s);
 }
 
+constexpr int FNT = 64 * NWAVE;  // forward threads per workgroup
+
+// Slow path for lanes whose marked elements overflowed the queue (their risk
+// mask is passed; other lanes pass zeros); q is the lane's queue column.
 template <int ACT>
-__device__ __forceinline__ void fwd_fix(const FwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
-                                        uint32_t (&h)[RPW][CPT / 2], uint32_t *q) {
+__device__ __forceinline__ void fwd_fix_slow(const FwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
+                                          uint32_t (&h)[RPW][CPT / 2], uint2 *q) {
     int total = 0;
 #pragma unroll
     for (int w = 0; w < NWORDS; w++) total += __builtin_popcount(risk[w]);
     for (int base = 0; base < total; base += kFixQ) {
-        const int nq = fix_gather<NWORDS>(risk, base, q);
+        const int nq = fix_gather<NWORDS, FNT>(risk, base, q);
 #pragma unroll 1
         for (int j = 0; j < nq; j++) {
-            const int idx = (int)q[j];
+            const int idx = (int)q[FNT * j].x;
             const int64_t r = rbase + idx / CPT, c = c0 + idx % CPT;
             const float g = bf16_at(a.gate + r * a.ld_gate + c);
             const float u = bf16_at(a.up + r * a.ld_up + c);
             const float s = a.row_scale != nullptr ? a.row_scale[r] : 1.0f;
-            q[j] = fwd_elem_f64(g, u, s, a.limit, ACT);
+            q[FNT * j].x = fwd_elem_f64(g, u, s, a.limit, ACT);
         }
         int rank = 0;
 #pragma unroll
@@ -376,7 +405,7 @@ __device__ __forceinline__ void fwd_fix(const FwdArgs &a, int64_t rbase, int c0,
 #pragma unroll
                 for (int k = 0; k < CPT; k++) {
                     if (rb & (1u << k)) {
-                        if (rank >= base && rank < base + nq) h[i][k >> 1] = set_half(h[i][k >> 1], k & 1, q[rank - base]);
+                        if (rank >= base && rank < base + nq) h[i][k >> 1] = set_half(h[i][k >> 1], k & 1, q[FNT * (rank - base)].x);
                         rank++;
                     }
                 }
@@ -386,7 +415,7 @@ __device__ __forceinline__ void fwd_fix(const FwdArgs &a, int64_t rbase, int c0,
 }
 
 // Is the row scale s safe for the fast product path (finite, normal or zero)?
-__device__ __forceinline__ bool scale_ok(float s) { return __builtin_amdgcn_class(s, kNormalOrZero); }
+__device__ __forceinline__ bool scale_ok(float s) { return normal_or_zero(s); }
 
 // Scale bytes and NaN masks of CPT columns from their packed |bf16| maxima.
 struct ColScales {
@@ -435,8 +464,8 @@ __device__ __forceinline__ void colmax_exchange(uint32_t (*cmx)[64][CPT / 2], in
 }
 
 template <int ACT, int DIRS>
-__global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a, int64_t nslabs) {
-    __shared__ uint32_t fixq[256 * kFixQ];
+__global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs) {
+    __shared__ uint2 fq[kQ + 1][FNT];  // slot kQ takes the writes of lanes whose queue is full
     __shared__ uint32_t cmx[NWAVE][64][CPT / 2];
     const int64_t bid = blockIdx.x;
     const int64_t t = bid / nslabs;
@@ -465,6 +494,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a, int64_t nslabs) {
     }
     uint32_t h[RPW][CPT / 2];
     uint32_t risk[NWORDS];
+    int nq = 0;  // this lane's marked elements (queued while nq <= kQ)
 #pragma unroll
     for (int w = 0; w < NWORDS; w++) risk[w] = 0u;
 #pragma unroll
@@ -479,12 +509,36 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a, int64_t nslabs) {
             if (!scale_ok(s)) bits = (1u << CPT) - 1u;
             if (!active || i >= nrow) bits = 0u;
             risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
+            if (wave_any(bits != 0u)) {
+#pragma unroll
+                for (int k = 0; k < CPT; k++) {
+                    const uint32_t c = (bits >> k) & 1u;
+                    const int slot = c ? min(nq, kQ) : kQ;
+                    fq[slot][tid] = make_uint2(half16(gv[i].w[k >> 1], k & 1) | (half16(uv[i].w[k >> 1], k & 1) << 16),
+                                               (uint32_t)(i * CPT + k));
+                    nq += (int)c;
+                }
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // the rare exact-path elements
-    if constexpr (ACT != ACT_IDENTITY) fwd_fix<ACT>(a, rbase, co, risk, h, fixq + tid * kFixQ);
+    // the rare exact-path elements: queued ones in fp64, then the overflow lanes
+    if constexpr (ACT != ACT_IDENTITY) {
+        const int nfix = nq <= kQ ? nq : 0;
+#pragma unroll 1
+        for (int j = 0; j < nfix; j++) {
+            const uint2 e = fq[j][tid];
+            const float s = a.row_scale != nullptr ? a.row_scale[rbase + (int)e.y / CPT] : 1.0f;
+            fq[j][tid].x = fwd_elem_f64(lo_f(e.x), hi_f(e.x), s, a.limit, ACT);
+        }
+        if (wave_any(nq > kQ)) {
+            uint32_t rk[NWORDS];
+#pragma unroll
+            for (int w = 0; w < NWORDS; w++) rk[w] = nq > kQ ? risk[w] : 0u;
+            fwd_fix_slow<ACT>(a, rbase, co, rk, h, &fq[0][tid]);
+        }
+    }
 
     // pass 2: rowwise outputs and the wave's column maxima (rows past the
     // tile and lanes past K hold zeros; the latter form whole 32-column
@@ -492,8 +546,22 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a, int64_t nslabs) {
     uint32_t cm[CPT / 2];
 #pragma unroll
     for (int k = 0; k < CPT / 2; k++) cm[k] = 0u;
+    int rank = 0;
 #pragma unroll
     for (int i = 0; i < RPW; i++) {
+        if constexpr (ACT != ACT_IDENTITY) {
+            // merge this row's queued exact results
+            const uint32_t rb = nq <= kQ ? row_bits<CPT>(risk, i) : 0u;
+            if (wave_any(rb != 0u)) {
+#pragma unroll
+                for (int k = 0; k < CPT; k++) {
+                    if (rb & (1u << k)) {
+                        h[i][k >> 1] = set_half(h[i][k >> 1], k & 1, fq[rank][tid].x);
+                        rank++;
+                    }
+                }
+            }
+        }
         uint32_t m = 0u;
 #pragma unroll
         for (int k = 0; k < CPT / 2; k++) {
@@ -544,14 +612,18 @@ struct BwdPair {
     uint32_t risky;      // 2-bit mask
 };
 
-// Error bound of the fast silu'(g) = sig * (1 + g * e * sig) for g >= -80, as
-// an absolute value: e carries up to 1 + |g| ulps (v_exp_f32 plus the
-// rounding of its argument), sig up to 3; both are amplified by |g| * (1 - sig)
-// in the cancellation of 1 + g * (1 - sig); the rest is relative to silu'.
-// Taken with a factor ~2 of slack.
-__device__ __forceinline__ float dsilu_err(float g, float sig, float one_minus) {
-    const float ag = fabsf(g);
-    return sig * (ag * one_minus * (2.0f * ag + 20.0f) + 16.0f) * 0x1p-24f;
+// Absolute error bound of the fast dgate tdg = fl(P * ds'), ds' =
+// fl(sig' * fma(g, om', 1)) with P = fl(dh * u * s).  Measured against the
+// exact silu'(g) for every bf16 g >= -80, |ds' - silu'(g)| stays below 0.51 of
+//   sig * 2^-24 * (6 |1 + g (1 - sig)| + 3 |g| (1 - sig) (|g| + 3)),
+// so that expression (a factor >= 1.98 of slack) bounds the silu' error; P
+// and the final product add one rounding each, covered by 4 * 2^-24 |tdg|.
+// Since |P| sig |1 + g (1 - sig)| is |tdg| up to two roundings, the bound is
+//   2^-24 (10.5 |tdg| + 3 |P| sig |g| om (|g| + 3)).
+__device__ __forceinline__ float dgate_err(float tdg, float P, float g, float sig, float om) {
+    const float k = fabsf(g) * om;
+    const float t3 = fmaf(fabsf(g), 3.0f * 0x1p-24f, 9.0f * 0x1p-24f);
+    return fmaf(fabsf(tdg), 10.5f * 0x1p-24f, (fabsf(P) * sig) * (k * t3));
 }
 
 // Could an error of at most `bound` move t across a bf16 rounding tie?  The
@@ -603,9 +675,8 @@ __device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t u
         const float tdg = P * ds * mg[j];
         vdg[j] = tdg;
         uint32_t r = (uint32_t)silu_risky(g[j], t[j]) | (uint32_t)product_risky(q, qs);
-        r |= (uint32_t)!__builtin_amdgcn_class(du_, kNormalOrZero) | (uint32_t)!__builtin_amdgcn_class(P, kNormalOrZero) |
-             (uint32_t)!__builtin_amdgcn_class(tdg, kNormalOrZero);
-        r |= (uint32_t)(mg[j] != 0.0f) & (uint32_t)near_tie(tdg, fabsf(P) * dsilu_err(g[j], sg[j], om[j]) + fabsf(tdg) * 0x1p-21f);
+        r |= (uint32_t)!normal_or_zero(du_) | (uint32_t)!normal_or_zero(P) | (uint32_t)!normal_or_zero(tdg);
+        r |= (uint32_t)(mg[j] != 0.0f) & (uint32_t)near_tie(tdg, dgate_err(tdg, P, g[j], sg[j], om[j]));
         out.risky |= r << j;
     }
     out.dg = pack_bf16(vdg[0], vdg[1]);
@@ -647,26 +718,30 @@ constexpr int BRPW = 4;
 constexpr int BNWAVE = 8;
 constexpr int BNWORDS = BRPW * CPT / 32;
 
+constexpr int BNT = 64 * BNWAVE;  // backward threads per workgroup
+
+// Slow path for lanes whose marked elements overflowed the queue (see the
+// forward's); the queue column's .x holds indices / results, .y corrections.
 template <int ACT>
-__device__ __forceinline__ void bwd_fix(const BwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
-                                        uint32_t (&hg)[BRPW][CPT / 2], uint32_t (&hu)[BRPW][CPT / 2],
-                                        uint32_t *q, float *qc, float (&dsum)[BRPW]) {
+__device__ __forceinline__ void bwd_fix_slow(const BwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
+                                             uint32_t (&hg)[BRPW][CPT / 2], uint32_t (&hu)[BRPW][CPT / 2],
+                                             uint2 *q, float (&dsum)[BRPW]) {
     int total = 0;
 #pragma unroll
     for (int w = 0; w < BNWORDS; w++) total += __builtin_popcount(risk[w]);
     for (int base = 0; base < total; base += kFixQ) {
-        const int nq = fix_gather<BNWORDS>(risk, base, q);
+        const int nq = fix_gather<BNWORDS, BNT>(risk, base, q);
 #pragma unroll 1
         for (int j = 0; j < nq; j++) {
-            const int idx = (int)q[j];
+            const int idx = (int)q[BNT * j].x;
             const int64_t r = rbase + idx / CPT, c = c0 + idx % CPT;
             const float d = bf16_at(a.grad + r * a.ld_grad + c);
             const float g = bf16_at(a.gate + r * a.ld_gate + c);
             const float u = bf16_at(a.up + r * a.ld_up + c);
             const float s = a.row_scale != nullptr ? a.row_scale[r] : 1.0f;
             float corr;
-            q[j] = bwd_elem_f64<ACT>(d, g, u, s, a.limit, &corr);
-            qc[j] = corr;
+            q[BNT * j].x = bwd_elem_f64<ACT>(d, g, u, s, a.limit, &corr);
+            q[BNT * j].y = __float_as_uint(corr);
         }
         int rank = 0;
 #pragma unroll
@@ -677,10 +752,10 @@ __device__ __forceinline__ void bwd_fix(const BwdArgs &a, int64_t rbase, int c0,
                 for (int k = 0; k < CPT; k++) {
                     if (rb & (1u << k)) {
                         if (rank >= base && rank < base + nq) {
-                            const uint32_t v = q[rank - base];
-                            hg[i][k >> 1] = set_half(hg[i][k >> 1], k & 1, v & 0xFFFFu);
-                            hu[i][k >> 1] = set_half(hu[i][k >> 1], k & 1, v >> 16);
-                            dsum[i] += qc[rank - base];
+                            const uint2 v = q[BNT * (rank - base)];
+                            hg[i][k >> 1] = set_half(hg[i][k >> 1], k & 1, v.x & 0xFFFFu);
+                            hu[i][k >> 1] = set_half(hu[i][k >> 1], k & 1, v.x >> 16);
+                            dsum[i] += __uint_as_float(v.y);
                         }
                         rank++;
                     }
@@ -695,9 +770,8 @@ __device__ __forceinline__ void bwd_fix(const BwdArgs &a, int64_t rbase, int c0,
 // [dgate | dup]) and dup (columns K + j).  dscale partials are reduced
 // through LDS in a fixed order (deterministic) and written per (row, slab).
 template <int ACT, int DIRS>
-__global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a, int64_t nslabs) {
-    __shared__ uint32_t fixq[512 * kFixQ];
-    __shared__ float fixc[512 * kFixQ];
+__global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs) {
+    __shared__ uint2 fq[kQ + 1][BNT];   // slot kQ takes the writes of lanes whose queue is full
     __shared__ uint32_t cmx[2][BNWAVE][64][CPT / 2];
     __shared__ float red[TROWS][65];
     __shared__ float red2[TROWS][9];
@@ -733,6 +807,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a, int64_t nslabs) {
     uint32_t hg[BRPW][CPT / 2], hu[BRPW][CPT / 2];
     uint32_t risk[BNWORDS];
     float dsum[BRPW];
+    int nq = 0;  // this lane's marked elements (queued while nq <= kQ)
 #pragma unroll
     for (int w = 0; w < BNWORDS; w++) risk[w] = 0u;
 #pragma unroll
@@ -762,23 +837,69 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a, int64_t nslabs) {
         }
         risk[(i * CPT) / 32] |= bits << ((i * CPT) % 32);
         dsum[i] = ds;
+        pin(dsum[i]);
+        pin(risk[(i * CPT) / 32]);
+#pragma unroll
+        for (int k = 0; k < CPT / 2; k++) {
+            pin(hg[i][k]);
+            pin(hu[i][k]);
+        }
+        if (wave_any(bits != 0u)) {
+#pragma unroll
+            for (int k = 0; k < CPT; k++) {
+                const uint32_t c = (bits >> k) & 1u;
+                const int slot = c ? min(nq, kQ) : kQ;
+                fq[slot][tid] = make_uint2(half16(gv.w[k >> 1], k & 1) | (half16(uv.w[k >> 1], k & 1) << 16),
+                                          half16(dv.w[k >> 1], k & 1) | ((uint32_t)(i * CPT + k) << 16));
+                nq += (int)c;
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    bwd_fix<ACT>(a, rbase, co, risk, hg, hu, fixq + tid * kFixQ, fixc + tid * kFixQ, dsum);
-    if (want_ds) {
-        // this lane's dscale partials (corrected by the fix-up) for the reduction
+    // the rare exact-path elements: queued ones in fp64, then the overflow lanes
+    {
+        const int nfix = nq <= kQ ? nq : 0;
+#pragma unroll 1
+        for (int j = 0; j < nfix; j++) {
+            const uint2 e = fq[j][tid];
+            const float s = a.row_scale != nullptr ? a.row_scale[rbase + (int)(e.y >> 16) / CPT] : 1.0f;
+            float corr;
+            const uint32_t v = bwd_elem_f64<ACT>(lo_f(e.y), lo_f(e.x), hi_f(e.x), s, L, &corr);
+            fq[j][tid] = make_uint2(v, __float_as_uint(corr));
+        }
+        if (wave_any(nq > kQ)) {
+            uint32_t rk[BNWORDS];
 #pragma unroll
-        for (int i = 0; i < BRPW; i++) red[wave * BRPW + i][lane] = dsum[i];
+            for (int w = 0; w < BNWORDS; w++) rk[w] = nq > kQ ? risk[w] : 0u;
+            bwd_fix_slow<ACT>(a, rbase, co, rk, hg, hu, &fq[0][tid], dsum);
+        }
     }
 
     // pass 2: dense outputs, rowwise outputs, the wave's column maxima
     uint32_t cmg[CPT / 2], cmu[CPT / 2];
 #pragma unroll
     for (int k = 0; k < CPT / 2; k++) cmg[k] = cmu[k] = 0u;
+    int rank = 0;
 #pragma unroll
     for (int i = 0; i < BRPW; i++) {
         const int64_t r = rbase + i;
+        {
+            // merge this row's queued exact results
+            const uint32_t rb = nq <= kQ ? row_bits<CPT>(risk, i) : 0u;
+            if (wave_any(rb != 0u)) {
+#pragma unroll
+                for (int k = 0; k < CPT; k++) {
+                    if (rb & (1u << k)) {
+                        const uint2 v = fq[rank][tid];
+                        hg[i][k >> 1] = set_half(hg[i][k >> 1], k & 1, v.x & 0xFFFFu);
+                        hu[i][k >> 1] = set_half(hu[i][k >> 1], k & 1, v.x >> 16);
+                        dsum[i] += __uint_as_float(v.y);
+                        rank++;
+                    }
+                }
+            }
+        }
         if (dense && active && i < nrow) {
             store_bf16<CPT>(a.dgate + r * a.ld_dgate + co, hg[i]);
             store_bf16<CPT>(a.dup + r * a.ld_dup + co, hu[i]);
@@ -818,6 +939,12 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a, int64_t nslabs) {
                 }
             }
         }
+    }
+
+    if (want_ds) {
+        // this lane's dscale partials (corrected by the exact path) for the reduction
+#pragma unroll
+        for (int i = 0; i < BRPW; i++) red[wave * BRPW + i][lane] = dsum[i];
     }
 
     // pass 3: colwise outputs

@@ -44,6 +44,15 @@ def dirs_of(d):
     return {"row": 1, "col": 2, "both": 3}[d]
 
 
+def assert_exact(report):
+    """The library's exact path makes every output equal to the correctly
+    rounded definition except within ~1e-15 of a rounding tie, which seeded
+    inputs do not hit: every mismatch count must be zero (the looser parity
+    rules above are the contract; this is the implementation's claim)."""
+    bad = {k: v for k, v in report.items() if not k.endswith("maxerr") and v}
+    assert not bad, f"outputs differ from the oracle: {bad}"
+
+
 def run_fwd_and_compare(m, gu, sc, K, dirs, clamped, splits=None, report=None):
     report = {} if report is None else report
     M = gu.shape[0]
@@ -68,6 +77,7 @@ def run_fwd_and_compare(m, gu, sc, K, dirs, clamped, splits=None, report=None):
         compare_mx("fwd.row", gc_r, gs_r, rc, rs, closeh, True, report=report)
     if dirs & 2:
         compare_mx("fwd.col", gc_c, gs_c, cc, cs, closeh, False, rowblock_of(M, ro_np), report=report)
+    assert_exact(report)
     return report
 
 
@@ -156,6 +166,51 @@ def test_forward_stress_regimes(mxq):
     gu[90, K:K + 32] = -0.0
     gu[5, 0:32] = 0.0
     run_fwd_and_compare(mxq, gu, sc, K, 3, False)
+
+
+def tiny_product_inputs(M, K, seed):
+    """Gate ~2^-99 (silu ~2^-100), up and grad ~2^-40, row scales ~2^20: the
+    products a*u and dh*a, dh*u fall in the fp32 subnormal range (inexact),
+    while the scaled outputs are normal numbers."""
+    gen = torch.Generator().manual_seed(seed)
+    def mag(shape, e):
+        sign = torch.where(torch.rand(shape, generator=gen) < 0.5, -1.0, 1.0)
+        return (sign * (1.0 + torch.rand(shape, generator=gen)) * 2.0 ** e).to(torch.bfloat16)
+    gu = torch.cat([mag((M, K), -99), mag((M, K), -40)], dim=1)
+    sc = ((0.5 + torch.rand(M, generator=gen)) * 2.0 ** 20).to(torch.float32)
+    dy = mag((M, K), -40)
+    return gu, sc, dy
+
+
+def test_forward_subnormal_products(mxq):
+    """a*u lands in the fp32 subnormal range: the fast product is inexact there
+    and must take the exact path."""
+    gu, sc, _ = tiny_product_inputs(64, 128, seed=40)
+    run_fwd_and_compare(mxq, gu, sc, 128, 3, False)
+
+
+def queue_pattern_inputs(M, K, seed):
+    """Inputs whose exact-path elements (gate < -80 always takes it) are placed
+    to hit the per-lane queue boundaries: lane 0 of every 8-column group pattern
+    below, per 32-row tile: exactly 4 marked (queue full), 5 (overflow), every
+    element of the lane, and one row with a NaN row scale (all marked)."""
+    gu = W.packed_gate_up(M, K, seed=seed)
+    sc = W.row_scale(M, seed=seed)
+    for t in range(0, M, 32):
+        gu[t + 0, 0:4] = -100.0                  # columns 0-7 lane: 4 in row 0 ...
+        gu[t + 1, 8:11] = -120.0                 # columns 8-15 lane: 3 + 2 = 5
+        gu[t + 5, 12:14] = -90.0
+        gu[t:t + 32, 16:24] = -200.0             # columns 16-23: every element
+        gu[t + 9, 40] = -85.0                    # a single one
+    if M > 3:
+        sc[3] = float("nan")
+    return gu, sc
+
+
+def test_forward_exact_path_queue(mxq):
+    gu, sc = queue_pattern_inputs(64, 256, seed=41)
+    run_fwd_and_compare(mxq, gu, sc, 256, 3, False)
+    run_fwd_and_compare(mxq, gu, sc, 256, 1, True)
 
 
 def test_forward_empty(mxq):
@@ -284,6 +339,7 @@ def run_bwd_and_compare(m, gu, sc, dy, K, dirs, clamped, splits=None, dense=True
         err = np.abs(gds - ds.astype(np.float64))
         assert np.all(err <= tol + 1e-30), f"dscale off by {err.max()} (tol {tol[np.argmax(err)]})"
         rep["dscale.maxerr"] = float(err.max())
+    assert_exact(rep)
     return rep
 
 
@@ -333,6 +389,19 @@ def test_backward_large_magnitudes(mxq):
     sc = W.row_scale(64, seed=17)
     dy = W.grad_out(64, 256, seed=17)
     run_bwd_and_compare(mxq, gu, sc, dy, 256, 3, False)
+
+
+def test_backward_subnormal_products(mxq):
+    gu, sc, dy = tiny_product_inputs(64, 128, seed=42)
+    run_bwd_and_compare(mxq, gu, sc, dy, 128, 3, False)
+
+
+@pytest.mark.parametrize("d", ["none", "both"])
+def test_backward_exact_path_queue(mxq, d):
+    gu, sc = queue_pattern_inputs(96, 256, seed=43)
+    dy = W.grad_out(96, 256, seed=43)
+    run_bwd_and_compare(mxq, gu, sc, dy, 256, dirs_of(d) if d != "none" else 0, False)
+    run_bwd_and_compare(mxq, gu, sc, dy, 256, 1, True)
 
 
 def test_silu_exhaustive_through_dup(mxq):
@@ -401,3 +470,4 @@ def test_full_size_sampled_stripes(mxq, shape):
         err = np.abs(b[5][r0:r1].cpu().numpy().astype(np.float64) - o[6].astype(np.float64))
         assert np.all(err <= o[8] + 1e-30)
         say("  stripe", stripe, rep)
+        assert_exact(rep)
