@@ -228,6 +228,20 @@ __device__ __forceinline__ void store_bf16(uint16_t *p, const uint32_t *w) {
 
 // ------------------------------------------------------------------ tiles
 
+// The dispatcher hands consecutive workgroups to the 8 XCDs in turn (block b
+// runs on XCD b % 8, each with its own L2).  Grids are rounded up to a
+// multiple of 8 and block b takes work item (b % 8) * (grid / 8) + b / 8, so
+// each XCD owns a contiguous range of items: the column slabs of one row tile
+// then share an L2, which merges their partial-line writes (the rowwise scale
+// bytes of a row come from every slab) before they reach HBM.
+constexpr int kXCD = 8;
+
+__device__ __forceinline__ int64_t xcd_item(int64_t bid, int64_t grid) {
+    return (bid % kXCD) * (grid / kXCD) + bid / kXCD;
+}
+
+inline int64_t xcd_grid(int64_t nwork) { return (nwork + kXCD - 1) / kXCD * kXCD; }
+
 struct Tile {
     int64_t r0;    // first row
     int n;         // rows present (0 => nothing to do)
@@ -464,12 +478,13 @@ __device__ __forceinline__ void colmax_exchange(uint32_t (*cmx)[64][CPT / 2], in
 }
 
 template <int ACT, int DIRS>
-__global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs) {
+__global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int64_t nwork) {
     __shared__ uint2 fq[kQ + 1][FNT];  // slot kQ takes the writes of lanes whose queue is full
     __shared__ uint32_t cmx[NWAVE][64][CPT / 2];
-    const int64_t bid = blockIdx.x;
-    const int64_t t = bid / nslabs;
-    const int64_t slab = bid - t * nslabs;
+    const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+    if (item >= nwork) return;  // grid padding (uniform over the workgroup)
+    const int64_t t = item / nslabs;
+    const int64_t slab = item - t * nslabs;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int co = (int)(slab * SLAB) + lane * CPT;
@@ -770,14 +785,15 @@ __device__ __forceinline__ void bwd_fix_slow(const BwdArgs &a, int64_t rbase, in
 // [dgate | dup]) and dup (columns K + j).  dscale partials are reduced
 // through LDS in a fixed order (deterministic) and written per (row, slab).
 template <int ACT, int DIRS>
-__global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs) {
+__global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int64_t nwork) {
     __shared__ uint2 fq[kQ + 1][BNT];   // slot kQ takes the writes of lanes whose queue is full
     __shared__ uint32_t cmx[2][BNWAVE][64][CPT / 2];
     __shared__ float red[TROWS][65];
     __shared__ float red2[TROWS][9];
-    const int64_t bid = blockIdx.x;
-    const int64_t t = bid / nslabs;
-    const int64_t slab = bid - t * nslabs;
+    const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+    if (item >= nwork) return;  // grid padding (uniform over the workgroup)
+    const int64_t t = item / nslabs;
+    const int64_t slab = item - t * nslabs;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int co = (int)(slab * SLAB) + lane * CPT;
@@ -1034,9 +1050,9 @@ int64_t tiles_of(int64_t M, const Groups &g, unsigned dirs) {
 template <int ACT, int DIRS>
 hipError_t fwd_launch(const FwdArgs &a, hipStream_t stream) {
     const int64_t ns = slabs_of(a.K);
-    const int64_t nblocks = tiles_of(a.M, a.groups, DIRS) * ns;
-    if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fwd_kernel<ACT, DIRS>), dim3((unsigned)nblocks), dim3(256), 0, stream, a, ns);
+    const int64_t nwork = tiles_of(a.M, a.groups, DIRS) * ns;
+    if (nwork <= 0) return hipSuccess;
+    hipLaunchKernelGGL((fwd_kernel<ACT, DIRS>), dim3((unsigned)xcd_grid(nwork)), dim3(FNT), 0, stream, a, ns, nwork);
     return hipGetLastError();
 }
 
@@ -1052,9 +1068,9 @@ hipError_t fwd_dispatch(const FwdArgs &a, hipStream_t stream) {
 template <int ACT, int DIRS>
 hipError_t bwd_launch(const BwdArgs &a, hipStream_t stream) {
     const int64_t ns = slabs_of(a.K);
-    const int64_t nblocks = tiles_of(a.M, a.groups, DIRS) * ns;
-    if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_kernel<ACT, DIRS>), dim3((unsigned)nblocks), dim3(512), 0, stream, a, ns);
+    const int64_t nwork = tiles_of(a.M, a.groups, DIRS) * ns;
+    if (nwork <= 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_kernel<ACT, DIRS>), dim3((unsigned)xcd_grid(nwork)), dim3(BNT), 0, stream, a, ns, nwork);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.dscale != nullptr && ns > 1) {
@@ -1089,6 +1105,11 @@ hipError_t launch_act_quant_fwd(const FwdArgs &a, hipStream_t stream) {
 hipError_t launch_act_quant_bwd(const BwdArgs &a, hipStream_t stream) {
     if (a.act == ACT_CLAMPED) return bwd_dispatch<ACT_CLAMPED>(a, stream);
     return bwd_dispatch<ACT_SWIGLU>(a, stream);
+}
+
+int64_t act_quant_launch_threads(int64_t M, int64_t K, int64_t G, bool grouped_colwise, bool backward) {
+    const int64_t tiles = grouped_colwise ? colwise_block_bound(M, G) : (M + TROWS - 1) / TROWS;
+    return xcd_grid(tiles * slabs_of(K)) * (backward ? BNT : FNT);
 }
 
 size_t bwd_workspace_bytes(int64_t M, int64_t K) {

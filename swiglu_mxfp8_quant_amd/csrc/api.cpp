@@ -172,7 +172,6 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, in
         if (row_scale) ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
     }
     const int64_t G = go.g.G;
-    const int64_t nsrows_bound = mxq::colwise_block_bound(M, G);
     if (dirs & 1) {
         s = check_mx_out(row_out, true, M, K, M, "rowwise", outs);
         if (s != MXQ_OK) return s;
@@ -187,9 +186,9 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, in
     } else if (col_out != nullptr && col_out->codes != nullptr) {
         return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
     }
-    // grid bound: tiles x slabs must fit a 31-bit grid
-    if (nsrows_bound * ((K / 8 + 63) / 64) >= (int64_t(1) << 31) || (M / 8 + 1) * ((K / 8 + 63) / 64) >= (int64_t(1) << 31))
-        return fail(MXQ_ERR_OVERFLOW, "launch grid beyond 2^31 workgroups");
+    // launch bound: HIP's grid x block must stay below 2^32 work-items
+    if (mxq::act_quant_launch_threads(M, K, G, (dirs & 2) && G > 0, false) >= (int64_t(1) << 32))
+        return fail(MXQ_ERR_OVERFLOW, "launch beyond 2^32 work-items");
     s = check_alias(ins, outs);
     if (s != MXQ_OK) return s;
     a.act = act_kind;
@@ -341,7 +340,6 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, con
         }
     }
     const int64_t G = go.g.G;
-    const int64_t nsrows_bound = mxq::colwise_block_bound(M, G);
     if (dirs & 1) {
         if ((s = check_mx_out(row_out, true, M, 2 * K, M, "rowwise", outs)) != MXQ_OK) return s;
     } else if (row_out != nullptr && row_out->codes != nullptr) {
@@ -353,8 +351,8 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, con
     } else if (col_out != nullptr && col_out->codes != nullptr) {
         return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
     }
-    if (nsrows_bound * ((K / 4 + 63) / 64) >= (int64_t(1) << 31) || (M / 8 + 1) * ((K / 8 + 63) / 64) >= (int64_t(1) << 31))
-        return fail(MXQ_ERR_OVERFLOW, "launch grid beyond 2^31 workgroups");
+    if (mxq::act_quant_launch_threads(M, K, G, (dirs & 2) && G > 0, true) >= (int64_t(1) << 32))
+        return fail(MXQ_ERR_OVERFLOW, "launch beyond 2^32 work-items");
     if ((s = check_alias(ins, outs)) != MXQ_OK) return s;
 
     mxq::BwdArgs a{};
