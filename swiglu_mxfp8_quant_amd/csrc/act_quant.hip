@@ -216,14 +216,14 @@ __device__ __forceinline__ Vec<CPT> zero_vec() {
 // CPT/4 code dwords -> memory
 template <int CPT>
 __device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t *c) {
-    if constexpr (CPT == 8) *reinterpret_cast<uint2 *>(p) = make_uint2(c[0], c[1]);
-    else *reinterpret_cast<uint32_t *>(p) = c[0];
+    if constexpr (CPT == 8) __builtin_nontemporal_store(u32x2_t{c[0], c[1]}, reinterpret_cast<u32x2_t *>(p));
+    else __builtin_nontemporal_store(c[0], reinterpret_cast<uint32_t *>(p));
 }
 
 template <int CPT>
 __device__ __forceinline__ void store_bf16(uint16_t *p, const uint32_t *w) {
-    if constexpr (CPT == 8) *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
-    else *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    if constexpr (CPT == 8) __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4_t *>(p));
+    else __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, reinterpret_cast<u32x2_t *>(p));
 }
 
 // ------------------------------------------------------------------ tiles
