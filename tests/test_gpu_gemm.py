@@ -241,3 +241,65 @@ def test_single_group_equals_dense(mxq):
     Av = (A.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     Bv = (B[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     check_close(out_np(out), Av @ Bv.T)
+
+
+# ------------------------------------------------------------------ several tiles
+
+BIG_SPLITS = [300, 0, 40, 1, 257]
+
+
+@pytest.mark.parametrize("mode", ["NT", "NN", "TN"])
+def test_multi_tile_mxfp8(mxq, mode):
+    """Several 256 x 256 output tiles in both dimensions, row and column tails,
+    and contraction lengths of several 128-byte steps (the double-buffered
+    pipeline), on quantized normal data."""
+    rng = np.random.default_rng(11)
+    ro, bo, ro_np, bo_np = offsets(mxq, BIG_SPLITS)
+    R, G = sum(BIG_SPLITS), len(BIG_SPLITS)
+    if mode == "NT":
+        N, K = 272, 384
+        A, As = qrows(rng, (R, K))
+        Bl = [qrows(rng, (N, K), 0.05) for _ in range(G)]
+        B, Bs = np.stack([b[0] for b in Bl]), np.stack([b[1] for b in Bl])
+        opA = O.Operand("mxfp8", A, 0, K, 1, As, 0, K // 32, 1)
+        opB = O.Operand("mxfp8", B, N * K, K, 1, Bs, N * (K // 32), K // 32, 1)
+        ref = O.grouped_gemm("m", ro_np, 0, N, K, opA, opB, "bf16")
+        out = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+        mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs))
+        rdt = "bf16"
+    elif mode == "NN":
+        N, K = 272, 416
+        A, As = qrows(rng, (R, K))
+        Bl = [qcols(rng, (K, N), None, 0.05) for _ in range(G)]
+        B, Bs = np.stack([b[0] for b in Bl]), np.stack([b[1] for b in Bl])
+        opA = O.Operand("mxfp8", A, 0, K, 1, As, 0, K // 32, 1)
+        opB = O.Operand("mxfp8", B, K * N, 1, N, Bs, (K // 32) * N, 1, N)
+        ref = O.grouped_gemm("m", ro_np, 0, N, K, opA, opB, "f32")
+        out = torch.empty((R, N), dtype=torch.float32, device="cuda")
+        mxq.grouped_gemm(mxq.GEMM_NN, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs))
+        rdt = "f32"
+    else:
+        M, N = 272, 288
+        A, As = qcols(rng, (R, M), ro_np)
+        B, Bs = qcols(rng, (R, N), ro_np, 0.01)
+        opA = O.Operand("mxfp8", A, 0, 1, M, As, 0, 1, M)
+        opB = O.Operand("mxfp8", B, 0, 1, N, Bs, 0, 1, N)
+        ref = O.grouped_gemm("k", ro_np, M, N, 0, opA, opB, "bf16")
+        out = torch.full((G, M, N), 3.0, dtype=torch.bfloat16, device="cuda")
+        mxq.grouped_gemm(mxq.GEMM_TN, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs), block_off=bo)
+        rdt = "bf16"
+    torch.cuda.synchronize()
+    check_close(out_np(out), ref_np(ref, rdt))
+
+
+def test_multi_tile_bf16(mxq):
+    rng = np.random.default_rng(12)
+    ro, bo, ro_np, _ = offsets(mxq, BIG_SPLITS)
+    R, N, K, G = sum(BIG_SPLITS), 272, 192, len(BIG_SPLITS)
+    A = rand_bf16(rng, (R, K))
+    B = rand_bf16(rng, (G, N, K), 0.05)
+    ref = O.grouped_gemm("m", ro_np, 0, N, K, O.Operand("bf16", A, 0, K, 1), O.Operand("bf16", B, N * K, K, 1), "bf16")
+    out = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B), out)
+    torch.cuda.synchronize()
+    check_close(out_np(out), ref_np(ref, "bf16"))
