@@ -85,6 +85,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t *base, int6
     return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations and for
+// all but the last `keep` vector-memory operations (the usual __syncthreads
+// fence would also wait for the warm-up loads still in flight).  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+template <int KEEP>
+__device__ __forceinline__ void step_barrier() {
+    static_assert(KEEP >= 0 && KEEP < 16, "vmcnt field");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070 | KEEP);   // vmcnt(KEEP) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void to_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, off, 0, 0, 0);
 }
@@ -129,6 +142,25 @@ __device__ __forceinline__ void stage_ks(const Src &o, int64_t s, uint8_t *dst, 
     }
 }
 
+// L2 warm-up two steps ahead: one 4-byte load per 128-byte line of the
+// stage's tile (thread t: K-contiguous row t; K-strided contraction row t / 2,
+// half t % 2), delivered into a scratch LDS area that nothing reads, so no
+// register waits on them: they only bring the lines into L2.
+__device__ __forceinline__ void touch_kc(const Src &o, int64_t s, int t, uint8_t *junk) {
+    const int64_t k0 = s * BK;
+    const __amdgpu_buffer_rsrc_t r = rsrc(o.base + k0, (int64_t)o.valid * o.pitch - k0);
+    const bool ok = (t < o.valid) & (k0 < o.kext);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)junk, 4, ok ? (uint32_t)(t * o.pitch) : kOOB, 0, 0, 0);
+}
+
+__device__ __forceinline__ void touch_ks(const Src &o, int64_t s, int t, uint8_t *junk) {
+    const int64_t kr0 = s * 128;
+    const __amdgpu_buffer_rsrc_t r = rsrc(o.base + kr0 * o.pitch, (o.kext - kr0) * o.pitch);
+    const int kr = t >> 1, c = 128 * (t & 1);
+    const bool ok = (kr0 + kr < o.kext) & (c < o.valid);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)junk, 4, ok ? (uint32_t)(kr * o.pitch + c) : kOOB, 0, 0, 0);
+}
+
 // Rowwise E8M0 scales of a K-contiguous operand: thread t packs row t's 4 block
 // bytes of step s (blocks past the contraction read 0, i.e. 2^-127 times zeros).
 struct RowScales {
@@ -157,6 +189,18 @@ __device__ __forceinline__ RowScaleBytes rowscale_load(const RowScales &sc, int6
 
 __device__ __forceinline__ uint32_t rowscale_word(const RowScaleBytes &v) {
     return v.b[0] | (v.b[1] << 8) | (v.b[2] << 16) | (v.b[3] << 24);
+}
+
+// When the step's 4 block bytes of every row are one aligned word inside the
+// row (the common case: ld % 4 == 0 and a full step of blocks), they go
+// straight to LDS [row][4] with one 4-byte load per thread; returns false
+// when the byte path above has to be used instead.
+__device__ __forceinline__ bool rowscale_dma(const RowScales &sc, int64_t s, int t, uint8_t *dst) {
+    if (!((sc.ld % 4 == 0) & (4 * s + 4 <= sc.nblk))) return false;
+    const __amdgpu_buffer_rsrc_t r = rsrc(sc.base, (int64_t)sc.valid * sc.ld);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + 4 * (t & ~63)), 4,
+                                             t < sc.valid ? (uint32_t)(t * sc.ld + 4 * s) : kOOB, 0, 0, 0);
+    return true;
 }
 
 // Colwise E8M0 scales of a K-strided operand, step s: block rows 4s..4s+3 x
@@ -287,6 +331,7 @@ __device__ __forceinline__ void raster(int64_t item, int64_t ntm, int64_t ntn, i
 template <int MODE, int DT, int OUT>
 __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int64_t ntn, int64_t ntm, int64_t nwork) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t junk[4][256];   // warm-up load sink, one row per wave
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -372,7 +417,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int64_t ntn, int
         for (int y = 0; y < 8; y++) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // stage s -> buffer s & 1: data tiles straight to LDS, row scales via registers
-    RowScaleBytes xsw{}, ysw{};
+
     auto issue = [&](int64_t s) {
         uint8_t *st = smem + (s & 1) * STAGE;
         if constexpr (XKS) stage_ks(X, s, st, wave, lane);
@@ -380,29 +425,38 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int64_t ntn, int
         if constexpr (YKS) stage_ks(Y, s, st + OPB, wave, lane);
         else stage_kc(Y, s, st + OPB, wave, lane);
         if constexpr (F8) {
-            if constexpr (MODE == MODE_NT) xsw = rowscale_load(xr, s, tid);
-            else if (wave == 0) stage_colscales(xc, s, st + 2 * OPB, lane);
+            if constexpr (MODE == MODE_NT) {
+                if (!rowscale_dma(xr, s, tid, st + 2 * OPB))   // rare: byte path, written at once
+                    *reinterpret_cast<uint32_t *>(st + 2 * OPB + 4 * tid) = rowscale_word(rowscale_load(xr, s, tid));
+            } else if (wave == 0) {
+                stage_colscales(xc, s, st + 2 * OPB, lane);
+            }
             if constexpr (MODE == MODE_TN) {
                 if (wave == 1) stage_colscales(yc, s, st + 2 * OPB + SCB, lane);
             } else {
-                ysw = rowscale_load(yr, s, tid);
+                if (!rowscale_dma(yr, s, tid, st + 2 * OPB + SCB))
+                    *reinterpret_cast<uint32_t *>(st + 2 * OPB + SCB + 4 * tid) = rowscale_word(rowscale_load(yr, s, tid));
             }
         }
     };
-    auto put_rowscales = [&](int64_t s) {
-        uint8_t *st = smem + (s & 1) * STAGE;
-        if constexpr (F8) {
-            if constexpr (MODE == MODE_NT) *reinterpret_cast<uint32_t *>(st + 2 * OPB + 4 * tid) = rowscale_word(xsw);
-            if constexpr (MODE != MODE_TN) *reinterpret_cast<uint32_t *>(st + 2 * OPB + SCB + 4 * tid) = rowscale_word(ysw);
+    auto touch = [&](int64_t s) {
+        if (s < ksteps) {
+            if constexpr (XKS) touch_ks(X, s, tid, junk[wave]);
+            else touch_kc(X, s, tid, junk[wave]);
+            if constexpr (YKS) touch_ks(Y, s, tid, junk[wave]);
+            else touch_kc(Y, s, tid, junk[wave]);
         }
     };
 
     if (ksteps > 0) issue(0);
+    touch(1);
     for (int64_t s = 0; s < ksteps; s++) {
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of step s have landed
-        put_rowscales(s);                // (its buffer's last readers passed the previous barrier)
-        __syncthreads();                 // everyone's loads have landed, and step s - 1's reads are done
+        // this wave's loads of step s have landed (only the 2 warm-up loads of
+        // step s + 1 may still be in flight behind them)
+        __builtin_amdgcn_s_waitcnt(0x0F72);
+        step_barrier<2>();               // everyone's loads have landed, and step s - 1's reads are done
         if (s + 1 < ksteps) issue(s + 1);
+        touch(s + 2);                    // after the step's loads: the last vector loads in flight
         const uint8_t *st = smem + (s & 1) * STAGE;
         const uint8_t *tx = st, *ty = st + OPB, *scx = st + 2 * OPB, *scy = st + 2 * OPB + SCB;
 
