@@ -11,7 +11,16 @@ outputs written once; forward 4 + n_dir*(1 + 1/32) B per element + 4 B per
 row, backward 10 + 2*n_dir*(1 + 1/32) B per element + 8 B per row, the
 backward writing the bf16 dgate/dup and the fp32 dscale too).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The grouped GEMMs are measured on the expert-layer workload (Qwen3-MoE-like:
+8192 tokens, hidden 2048, 128 experts, top-8, intermediate 768): one forward +
+backward of the layer through swiglu_mxfp8_quant_amd.moe (FC1 bf16, FC2, FC2
+dgrad / wgrad, FC1 dgrad / wgrad in MXFP8, plus the fused activation and the
+quantizations), with uniform softmax top-8 routing and plain SwiGLU, and with
+skewed Zipf(1.2) routing (8 empty experts) and the clamped SwiGLU.  Reported
+under "gemm": each GEMM's median time and TFLOP/s (2 flops per MAC), and the
+whole layer's wall time.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-moe]
 Prints one JSON line.
 """
 import argparse
@@ -101,6 +110,79 @@ def measured_traffic():
         return None
 
 
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def moe_section(m, torch, W, reps=5):
+    """Expert-layer forward + backward: per-GEMM and whole-layer timings."""
+    from swiglu_mxfp8_quant_amd.moe import Layer, gemm_flops
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, skewed, clamped in (("uniform_plain", False, False), ("zipf_clamped", True, True)):
+        moe = W.moe_layer(0, device="cuda", skewed=skewed)
+        cfg = moe["cfg"]
+        H, I, G = cfg["hidden"], cfg["inter"], cfg["experts"]
+        R = int(moe["splits"].sum())
+        layer = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped)
+        dy = W.moe_grad(R, H, seed=0, device="cuda")
+
+        def full():
+            layer.forward(moe["x_perm"], moe["scale"])
+            layer.backward(dy)
+        full()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            e0.record(stream)
+            full()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        layer_us = sorted(ts)[len(ts) // 2]
+        s, gr, ro, bo = layer.saved, layer.grads, layer.row_off, layer.block_off
+        h13 = torch.empty_like(s["h13"])
+        y = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+        da, dx = torch.empty_like(gr["da"]), torch.empty_like(gr["dx"])
+        dw2, dw13 = torch.empty_like(gr["dw2"]), torch.empty_like(gr["dw13"])
+        calls = {
+            "fc1_fwd": (lambda: m.grouped_gemm(m.GEMM_NT, ro, moe["x_perm"], moe["w13"], h13), "bf16"),
+            "fc2_fwd": (lambda: m.grouped_gemm(m.GEMM_NT, ro, s["a_r"], s["w2q"], y, s["as_r"], s["w2s"]), "fp8"),
+            "fc2_dgrad": (lambda: m.grouped_gemm(m.GEMM_NN, ro, gr["dy_r"], gr["w2c"], da, gr["dys_r"], gr["w2cs"]),
+                          "fp8"),
+            "fc2_wgrad": (lambda: m.grouped_gemm(m.GEMM_TN, ro, gr["dy_c"], s["a_c"], dw2, gr["dys_c"], s["as_c"],
+                                                 block_off=bo), "fp8"),
+            "fc1_dgrad": (lambda: m.grouped_gemm(m.GEMM_NN, ro, gr["dq_r"], gr["w13c"], dx, gr["dqs_r"],
+                                                 gr["w13cs"]), "fp8"),
+            "fc1_wgrad": (lambda: m.grouped_gemm(m.GEMM_TN, ro, gr["dq_c"], gr["x_c"], dw13, gr["dqs_c"], gr["xs_c"],
+                                                 block_off=bo), "fp8"),
+        }
+        flops = gemm_flops(R, H, I, G)
+        per, tot_fl, tot_us = {}, 0.0, 0.0
+        for k, (fn, dt) in calls.items():
+            fn()
+            ts = []
+            for _ in range(reps):
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            us = sorted(ts)[len(ts) // 2]
+            tf = flops[k] / us / 1e6
+            peak = FP8_PEAK_TFLOPS if dt == "fp8" else BF16_PEAK_TFLOPS
+            per[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": dt, "frac_peak": round(tf / peak, 4)}
+            tot_fl += flops[k]
+            tot_us += us
+        out[name] = {"routed_rows": R, "layer_fwd_bwd_us": round(layer_us, 1),
+                     "gemm_total_us": round(tot_us, 1), "gemm_TFLOPs": round(tot_fl / tot_us / 1e6, 1),
+                     "per_gemm": per}
+        del layer, moe, dy
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(rows=256):
     """The CPU oracle (single-threaded C, fp64) over a bounded sample: the
     first `rows` rows of every cell of the step (same byte model)."""
@@ -131,6 +213,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-moe", action="store_true", help="skip the expert-layer (grouped GEMM) section")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the dominant call 3 times and a 1 GiB device copy 3 times "
@@ -231,6 +314,10 @@ def main():
                      "bytes_per_launch": int(dom.bytes), "avg_launch_us": round(dom_us, 2)},
         "per_cell": per_cell,
     }
+    del cells, _data, flush, dom
+    torch.cuda.empty_cache()
+    if not args.no_moe:
+        out["gemm"] = moe_section(m, torch, W)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     print(json.dumps(out), flush=True)
