@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true", help="skip the expert-layer (grouped GEMM) section")
+    ap.add_argument("--moe-only", action="store_true",
+                    help="only run the expert-layer section once and print its record (for profiling the GEMMs)")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the dominant call 3 times and a 1 GiB device copy 3 times "
@@ -228,6 +230,9 @@ def main():
     import swiglu_mxfp8_quant_amd as m
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.moe_only:
+        print(json.dumps({"gemm": moe_section(m, torch, W, reps=2)}), flush=True)
+        return
     cells, _data = build_cells(m, torch, W)
     stream = torch.cuda.current_stream()
     dom = [c for c in cells if c.key() == DOMINANT][0]
