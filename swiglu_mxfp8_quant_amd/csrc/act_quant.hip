@@ -16,22 +16,26 @@
 //
 // Design (MI355X-first; the pages' CuTe DSL kernel for GB200 is prior art only):
 //   * A workgroup owns one row tile (a colwise 32-row block, restarting at
-//     every group, or 8 rows for rowwise-only work) and a slab of columns;
-//     each lane owns CPT (8 or 4) consecutive columns and walks the tile's
-//     rows with 16-byte (8-byte) coalesced loads of gate and up.
-//   * Colwise: the lane keeps its CPT x 32 bf16 results in registers, so the
-//     32x1 amax needs neither a second HBM pass nor an LDS round trip.
-//     Rowwise: the 1x32 amax is a DPP max over the 4 (8) lanes of the block.
+//     every group) and a 512-column slab: the forward splits the 32 rows over
+//     4 waves of 8, the backward over 8 waves of 4; each lane owns 8
+//     consecutive columns and issues 16-byte coalesced loads of gate and up
+//     (and grad), all rows' loads before any arithmetic.  Work items are laid
+//     out so that each XCD takes a contiguous range of them.
+//   * Colwise: each wave keeps its rows' bf16 results in registers and the
+//     32x1 amax combines the waves' partial maxima through LDS, so no second
+//     HBM pass.  Rowwise: the 1x32 amax is a DPP max over the 4 lanes of the
+//     block.
 //   * amax is an integer max of |bf16| bit patterns (NaN/Inf patterns sort
 //     above every finite value), the scale byte comes straight from the amax
 //     exponent bits, and gfx950's v_cvt_scalef32_pk_fp8_bf16 converts bf16
 //     pairs to E4M3 with the block scale (exact RNE, probed over all bf16
-//     inputs and scale bytes).
+//     inputs and scale bytes).  Codes and bf16 gradients leave with
+//     nontemporal stores.
 //   * Exactness: SiLU runs on v_exp_f32 / v_rcp_f32; an element whose fp32
-//     result lies within a proven error margin of a bf16 rounding tie (or is
-//     out of the range where the margin was proven) is recomputed in fp64 the
-//     way the definition reads, so results match the exact definition except
-//     within ~1e-15 of a tie.
+//     result lies within a measured error margin of a bf16 rounding tie (or is
+//     out of the range where the margin was measured, or involves a non-normal
+//     fp32 value) is recomputed in fp64 the way the definition reads, so
+//     results match the exact definition except within ~1e-15 of a tie.
 #include "mxq_internal.h"
 
 #include <math.h>
