@@ -491,6 +491,18 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int64_t ntn, int
                     acc[x][y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fx, fy[y], acc[x][y], 0, 0, 0, sx, 0,
                                                                                   sy[y]);
             }
+            // Issue order: a wave's instructions issue in order and an MFMA holds
+            // the issue for its whole pipeline slot, so LDS reads bunched between
+            // MFMA runs would leave the LDS idle.  Interleave one read after each
+            // MFMA (after the first few reads that the first MFMAs need).
+#pragma unroll
+            for (int i = 0; i < 8; i++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int i = 0; i < 40; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
         } else {
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) {

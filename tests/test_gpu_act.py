@@ -471,3 +471,42 @@ def test_full_size_sampled_stripes(mxq, shape):
         assert np.all(err <= o[8] + 1e-30)
         say("  stripe", stripe, rep)
         assert_exact(rep)
+
+
+def test_bandwidth_stress_sampled_stripes(mxq):
+    """The bandwidth-stress configuration at full size: gate/up (131072, 8192),
+    0.1 % of 1x32 and 32x1 blocks zeroed and 0.1 % holding a ~N(0, 1e3)
+    outlier; forward and backward, both directions, in the benchmark's
+    launch configuration.  The oracle checks 32-row stripes at the start,
+    middle and end and the stripes holding the largest |gate| and the
+    largest |up| (outlier blocks: E8M0 growth, E4M3 saturation)."""
+    M, K = 131072, 8192
+    gu, sc, dy = W.stress_inputs(M, K, seed=11, device="cuda", frac=1e-3)
+    f = mxq.swiglu_quantize_fwd(gu[:, :K], gu[:, K:], sc, rowwise=True, colwise=True)
+    b = mxq.swiglu_quantize_bwd(dy, gu[:, :K], gu[:, K:], sc, rowwise=True, colwise=True)
+    torch.cuda.synchronize()
+    big_g = int(torch.argmax(gu[:, :K].float().abs().amax(dim=1)).item()) // 32
+    big_u = int(torch.argmax(gu[:, K:].float().abs().amax(dim=1)).item()) // 32
+    for stripe in sorted({0, M // 64, M // 32 - 1, big_g, big_u}):
+        r0, r1 = 32 * stripe, 32 * stripe + 32
+        g_np, u_np, d_np = bits(gu[r0:r1, :K]), bits(gu[r0:r1, K:]), bits(dy[r0:r1])
+        s_np = sc[r0:r1].cpu().numpy()
+        rc, cc, rs, cs, h, close = O.swiglu_quantize_fwd(g_np, u_np, s_np, 3, want_close=True)
+        rep = {}
+        compare_mx("fwd.row", np_u8(f[0][r0:r1]), np_u8(f[2][r0:r1]), rc, rs, close != 0, True, report=rep)
+        compare_mx("fwd.col", np_u8(f[1][r0:r1]), np_u8(f[3][stripe:stripe + 1]), cc, cs, close != 0, False,
+                   rowblock_of(32), report=rep)
+        o = O.swiglu_quantize_bwd(d_np, g_np, u_np, s_np, 3, want_close=True)
+        closeb = o[7] != 0
+        compare_mx("bwd.row", np_u8(b[0][r0:r1]), np_u8(b[2][r0:r1]), o[0], o[2], closeb, True, report=rep)
+        compare_mx("bwd.col", np_u8(b[1][r0:r1]), np_u8(b[3][stripe:stripe + 1]), o[1], o[3], closeb, False,
+                   rowblock_of(32), report=rep)
+        dd = bits(b[4][r0:r1])
+        compare_bf16("dgate", dd[:, :K], o[4], closeb[:, :K], rep)
+        compare_bf16("dup", dd[:, K:], o[5], closeb[:, K:], rep)
+        err = np.abs(b[5][r0:r1].cpu().numpy().astype(np.float64) - o[6].astype(np.float64))
+        assert np.all(err <= o[8] + 1e-30)
+        say("  stripe", stripe, rep)
+        assert_exact(rep)
+    del gu, dy, f, b
+    torch.cuda.empty_cache()
