@@ -258,6 +258,9 @@ typedef struct {
     int64_t ld_out;         /* output row pitch, elements */
     int64_t out_gstride;    /* output group stride, elements (TN only) */
     int32_t accumulate;     /* 1: C += result (TN with F32 output only) */
+    int32_t max_workgroups; /* 0: one workgroup per CU; n > 0: at most n (rounded
+                               down to a multiple of 8, at least 8), e.g. to leave
+                               CUs to work overlapping on another stream */
 } mxq_gemm_args;
 
 /* Workspace bytes for mxq_grouped_gemm with these arguments (pointers unused). */

@@ -75,7 +75,7 @@ class mxq_gemm_args(ctypes.Structure):
                 ("K", ctypes.c_int64), ("rows", ctypes.c_int64), ("A", mxq_operand),
                 ("B", mxq_operand), ("out_dtype", ctypes.c_int32), ("out", ctypes.c_void_p),
                 ("ld_out", ctypes.c_int64), ("out_gstride", ctypes.c_int64),
-                ("accumulate", ctypes.c_int32)]
+                ("accumulate", ctypes.c_int32), ("max_workgroups", ctypes.c_int32)]
 
 
 def _load():
@@ -322,7 +322,7 @@ def _torch():
 
 
 def grouped_gemm(mode, row_off, A, B, out, A_scales=None, B_scales=None, block_off=None,
-                 accumulate=False, stream=None):
+                 accumulate=False, max_workgroups=0, stream=None):
     """Run the grouped GEMM.  Shapes (bf16 tensors or uint8 E4M3 codes):
       NT: A (R, K), B (G, N, K), out (R, N); MXFP8 scales (R, K/32), (G, N, K/32)
       NN: A (R, K), B (G, K, N), out (R, N); MXFP8 scales (R, K/32), (G, K/32, N)
@@ -336,13 +336,13 @@ def grouped_gemm(mode, row_off, A, B, out, A_scales=None, B_scales=None, block_o
         args = mxq_gemm_args(mode, G, row_off.data_ptr(), None if block_off is None else block_off.data_ptr(),
                              M, N, K, R, _operand(A, A_scales), _operand(B, B_scales),
                              DTYPE_F32 if out.dtype == _torch().float32 else DTYPE_BF16, out.data_ptr(),
-                             out.stride(1), out.stride(0), int(accumulate))
+                             out.stride(1), out.stride(0), int(accumulate), int(max_workgroups))
     else:
         R, K = A.shape
         N = B.shape[1] if mode == GEMM_NT else B.shape[2]
         args = mxq_gemm_args(mode, G, row_off.data_ptr(), None if block_off is None else block_off.data_ptr(),
                              R, N, K, R, _operand(A, A_scales), _operand(B, B_scales, group_dim=True),
                              DTYPE_F32 if out.dtype == _torch().float32 else DTYPE_BF16, out.data_ptr(),
-                             out.stride(0), 0, int(accumulate))
+                             out.stride(0), 0, int(accumulate), int(max_workgroups))
     check(mxq_grouped_gemm(args, None, stream))
     return out

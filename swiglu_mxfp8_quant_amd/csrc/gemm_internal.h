@@ -29,6 +29,7 @@ struct GemmArgs {
     void *out;
     int64_t ld_out, out_gstride;
     int accumulate;
+    int max_workgroups;
     bool noop;
 };
 

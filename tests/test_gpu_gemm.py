@@ -248,16 +248,13 @@ def test_single_group_equals_dense(mxq):
 BIG_SPLITS = [300, 0, 40, 1, 257]
 
 
-@pytest.mark.parametrize("mode", ["NT", "NN", "TN"])
-def test_multi_tile_mxfp8(mxq, mode):
-    """Several 256 x 256 output tiles in both dimensions, row and column tails,
-    and contraction lengths of several 128-byte steps (the double-buffered
-    pipeline), on quantized normal data."""
-    rng = np.random.default_rng(11)
-    ro, bo, ro_np, bo_np = offsets(mxq, BIG_SPLITS)
-    R, G = sum(BIG_SPLITS), len(BIG_SPLITS)
+def run_mxfp8(mxq, rng, mode, splits, N, KM, max_workgroups=0):
+    """One MXFP8 grouped GEMM on quantized normal data against the oracle.
+    KM is the contraction K (NT, NN) or the output row count M (TN)."""
+    ro, bo, ro_np, bo_np = offsets(mxq, splits)
+    R, G = sum(splits), len(splits)
     if mode == "NT":
-        N, K = 272, 384
+        K = KM
         A, As = qrows(rng, (R, K))
         Bl = [qrows(rng, (N, K), 0.05) for _ in range(G)]
         B, Bs = np.stack([b[0] for b in Bl]), np.stack([b[1] for b in Bl])
@@ -265,10 +262,11 @@ def test_multi_tile_mxfp8(mxq, mode):
         opB = O.Operand("mxfp8", B, N * K, K, 1, Bs, N * (K // 32), K // 32, 1)
         ref = O.grouped_gemm("m", ro_np, 0, N, K, opA, opB, "bf16")
         out = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
-        mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs))
+        mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs),
+                         max_workgroups=max_workgroups)
         rdt = "bf16"
     elif mode == "NN":
-        N, K = 272, 416
+        K = KM
         A, As = qrows(rng, (R, K))
         Bl = [qcols(rng, (K, N), None, 0.05) for _ in range(G)]
         B, Bs = np.stack([b[0] for b in Bl]), np.stack([b[1] for b in Bl])
@@ -276,30 +274,79 @@ def test_multi_tile_mxfp8(mxq, mode):
         opB = O.Operand("mxfp8", B, K * N, 1, N, Bs, (K // 32) * N, 1, N)
         ref = O.grouped_gemm("m", ro_np, 0, N, K, opA, opB, "f32")
         out = torch.empty((R, N), dtype=torch.float32, device="cuda")
-        mxq.grouped_gemm(mxq.GEMM_NN, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs))
+        mxq.grouped_gemm(mxq.GEMM_NN, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs),
+                         max_workgroups=max_workgroups)
         rdt = "f32"
     else:
-        M, N = 272, 288
+        M = KM
         A, As = qcols(rng, (R, M), ro_np)
         B, Bs = qcols(rng, (R, N), ro_np, 0.01)
         opA = O.Operand("mxfp8", A, 0, 1, M, As, 0, 1, M)
         opB = O.Operand("mxfp8", B, 0, 1, N, Bs, 0, 1, N)
         ref = O.grouped_gemm("k", ro_np, M, N, 0, opA, opB, "bf16")
         out = torch.full((G, M, N), 3.0, dtype=torch.bfloat16, device="cuda")
-        mxq.grouped_gemm(mxq.GEMM_TN, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs), block_off=bo)
+        mxq.grouped_gemm(mxq.GEMM_TN, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs), block_off=bo,
+                         max_workgroups=max_workgroups)
         rdt = "bf16"
     torch.cuda.synchronize()
     check_close(out_np(out), ref_np(ref, rdt))
 
 
-def test_multi_tile_bf16(mxq):
+@pytest.mark.parametrize("mode,N,KM", [("NT", 272, 384), ("NN", 272, 416), ("TN", 288, 272)])
+def test_multi_tile_mxfp8(mxq, mode, N, KM):
+    """Several 256 x 256 output tiles in both dimensions, row and column tails,
+    and contraction lengths of several 128-byte steps (the double-buffered
+    pipeline), on quantized normal data."""
+    run_mxfp8(mxq, np.random.default_rng(11), mode, BIG_SPLITS, N, KM)
+
+
+# Many tiles per workgroup: the persistent loop, the next tile's first stage
+# loaded during the current tile's last step, tiles with no contraction steps
+# (empty K-groups) between tiles with steps, and the per-XCD tile ranges.
+# Small groups keep the oracle's cost down while giving ~100 tiles.
+PERSIST_SPLITS = [5, 0, 3, 140, 0, 0, 1, 7, 260, 2, 0, 31, 33, 0, 129, 1, 64, 0, 0, 9,
+                  17, 4, 0, 2, 255, 0, 6, 8, 0, 1, 0, 44, 3, 0, 0, 12, 1, 0, 2, 70]
+
+
+@pytest.mark.parametrize("max_wg", [8, 24])
+@pytest.mark.parametrize("mode,N,KM", [("NT", 272, 256), ("NN", 272, 288), ("TN", 272, 272)])
+def test_persistent_many_tiles_mxfp8(mxq, mode, N, KM, max_wg):
+    run_mxfp8(mxq, np.random.default_rng(21), mode, PERSIST_SPLITS, N, KM, max_workgroups=max_wg)
+
+
+def test_many_groups_scan_path(mxq):
+    """More groups than the LDS tile table holds (4096): every tile lookup scans
+    the offsets on the device; mostly empty groups, a few of several tiles."""
+    rng = np.random.default_rng(22)
+    G, N, K = 4500, 32, 64
+    splits = [0] * G
+    for g in rng.choice(G, 40, replace=False):
+        splits[int(g)] = int(rng.integers(1, 300))
+    splits[G - 1] = 257
+    ro, bo, ro_np, _ = offsets(mxq, splits)
+    R = sum(splits)
+    A, As = qrows(rng, (R, K))
+    B, Bs = qrows(rng, (G * N, K), 0.05)          # rowwise blocks: one call for all groups
+    opA = O.Operand("mxfp8", A, 0, K, 1, As, 0, K // 32, 1)
+    opB = O.Operand("mxfp8", B, N * K, K, 1, Bs, N * (K // 32), K // 32, 1)
+    ref = ref_np(O.grouped_gemm("m", ro_np, 0, N, K, opA, opB, "bf16"), "bf16")
+    for max_wg in (0, 8):
+        out = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+        mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B.reshape(G, N, K)), out, to_dev(As),
+                         to_dev(Bs.reshape(G, N, K // 32)), max_workgroups=max_wg)
+        torch.cuda.synchronize()
+        check_close(out_np(out), ref)
+
+
+@pytest.mark.parametrize("splits,max_wg", [(BIG_SPLITS, 0), (PERSIST_SPLITS, 8)])
+def test_multi_tile_bf16(mxq, splits, max_wg):
     rng = np.random.default_rng(12)
-    ro, bo, ro_np, _ = offsets(mxq, BIG_SPLITS)
-    R, N, K, G = sum(BIG_SPLITS), 272, 192, len(BIG_SPLITS)
+    ro, bo, ro_np, _ = offsets(mxq, splits)
+    R, N, K, G = sum(splits), 272, 192, len(splits)
     A = rand_bf16(rng, (R, K))
     B = rand_bf16(rng, (G, N, K), 0.05)
     ref = O.grouped_gemm("m", ro_np, 0, N, K, O.Operand("bf16", A, 0, K, 1), O.Operand("bf16", B, N * K, K, 1), "bf16")
     out = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
-    mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B), out)
+    mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B), out, max_workgroups=max_wg)
     torch.cuda.synchronize()
     check_close(out_np(out), ref_np(ref, "bf16"))
