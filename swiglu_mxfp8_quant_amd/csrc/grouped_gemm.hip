@@ -52,18 +52,22 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 
 constexpr int BT = 256;            // tile rows on each side (X = output n, Y = output m)
-constexpr int BK = 128;            // contraction bytes per step
+constexpr int BK = 64;             // contraction bytes per step (one stage)
+constexpr int NBUF = 4;            // stage buffers: one computing, three loading
 constexpr int NTHR = 256;
 constexpr int OPB = BT * BK;       // bytes of one operand's stage tile (either layout)
-constexpr int SCB = 1024;          // bytes of one operand's stage scales
-constexpr int STAGE = 2 * OPB + 2 * SCB;
+constexpr int SCB = 1024;          // bytes of one operand's per-stage scales
+constexpr int RGS = 8;             // stages per scale-ring group (16 E8M0 bytes per row)
+constexpr int RSLOT = BT * 16;     // bytes of one operand's ring slot
 constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every range: loads zeros
 constexpr int kXCD = 8;
 
@@ -108,12 +112,39 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
-__device__ __forceinline__ void to_lds(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, off, 0, 0, 0);
+// Buffer loads straight into LDS (lane l's bytes land at M0 + size * l).
+// They are written out here rather than through the compiler's builtin: the
+// compiler would otherwise wait for every such load in flight before any LDS
+// access it cannot tell apart from their destinations (which would serialize
+// the stage pipeline), while the kernel orders them itself with its explicit
+// vmcnt waits and barriers.  They have no register results; M0, which they
+// read at issue, is saved and restored around them.
+__device__ __forceinline__ i32x4_t rsrc4(const uint8_t *base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes);
+    const uint64_t b = (uint64_t)uni64(reinterpret_cast<int64_t>(base));
+    return i32x4_t{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)__builtin_amdgcn_readfirstlane(n), 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)p);
+}
+
+__device__ __forceinline__ void to_lds(const i32x4_t &r, uint8_t *dst, uint32_t off) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_addr(dst)), "v"(off), "s"(r) : "memory");
+}
+
+__device__ __forceinline__ void to_lds4(const i32x4_t &r, uint8_t *dst, uint32_t off) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_addr(dst)), "v"(off), "s"(r) : "memory");
 }
 
 // One operand's view for staging.  K-contiguous: tile rows are output rows,
-// 128 contraction bytes each per step.  K-strided: tile rows are contraction
+// 64 contraction bytes each per step.  K-strided: tile rows are contraction
 // rows, 256 output columns (bytes) each.
 struct Src {
     const uint8_t *base;   // tile origin (row 0 / contraction row 0, first column)
@@ -122,60 +153,46 @@ struct Src {
     int valid;             // K-contiguous: valid tile rows; K-strided: valid column bytes
 };
 
-// K-contiguous stage s -> LDS [256 rows][128 B], chunk c of row r at c ^ (r & 7).
-// Wave w fills 1 KB blocks 8w..8w+7 (8 rows each).
-__device__ __forceinline__ void stage_kc(const Src &o, int s, uint8_t *dst, int wave, int lane) {
+// Every stage issue below is a fixed number of load instructions per wave
+// (4 + 4 data, 2 scale for MXFP8), whether or not it carries data: loads
+// with `live` false or outside the operand go out of range (no memory
+// access; zeros land in LDS).  The step waits count on that.
+
+// K-contiguous stage s -> LDS [256 rows][64 B], chunk c of row r at c ^ ((r >> 2) & 3).
+// Wave w fills 1 KB blocks 4w..4w+3 (16 rows each).
+__device__ __forceinline__ void stage_kc(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live) {
     const int k0 = s * BK;
-    const __amdgpu_buffer_rsrc_t r = rsrc(o.base + k0, (int64_t)o.valid * o.pitch - k0);
+    const i32x4_t r = rsrc4(o.base + k0, (int64_t)o.valid * o.pitch - k0);
     const int pitch = opaque(o.pitch);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int b = wave * 8 + j;
-        const int row = 8 * b + (lane >> 3);
-        const int c = (lane & 7) ^ (row & 7);
-        const bool ok = (row < o.valid) & (k0 + 16 * c < o.kext);
+    for (int j = 0; j < 4; j++) {
+        const int b = wave * 4 + j;
+        const int row = 16 * b + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        const bool ok = live & (row < o.valid) & (k0 + 16 * c < o.kext);
         to_lds(r, dst + 1024 * b, ok ? (uint32_t)(row * pitch + 16 * c) : kOOB);
     }
 }
 
-// K-strided stage s -> LDS [128 contraction rows][256 B], chunk c of row k at c ^ (k & 15).
-// Wave w fills 1 KB blocks 8w..8w+7 (4 contraction rows each).
-__device__ __forceinline__ void stage_ks(const Src &o, int s, uint8_t *dst, int wave, int lane) {
-    const int kr0 = s * 128;
-    const __amdgpu_buffer_rsrc_t r = rsrc(o.base + (int64_t)kr0 * o.pitch, (int64_t)(o.kext - kr0) * o.pitch);
+// K-strided stage s -> LDS [64 contraction rows][256 B], chunk c of row k at c ^ (k & 15).
+// Wave w fills 1 KB blocks 4w..4w+3 (4 contraction rows each).
+__device__ __forceinline__ void stage_ks(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live) {
+    const int kr0 = s * BK;
+    const i32x4_t r = rsrc4(o.base + (int64_t)kr0 * o.pitch, (int64_t)(o.kext - kr0) * o.pitch);
     const int pitch = opaque(o.pitch);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int b = wave * 8 + j;
+    for (int j = 0; j < 4; j++) {
+        const int b = wave * 4 + j;
         const int kr = 4 * b + (lane >> 4);
         const int c = (lane & 15) ^ (kr & 15);
-        const bool ok = (kr0 + kr < o.kext) & (16 * c < o.valid);
+        const bool ok = live & (kr0 + kr < o.kext) & (16 * c < o.valid);
         to_lds(r, dst + 1024 * b, ok ? (uint32_t)(kr * pitch + 16 * c) : kOOB);
     }
 }
 
-// L2 warm-up two steps ahead: one 4-byte load per 128-byte line of the
-// stage's tile (thread t: K-contiguous row t; K-strided contraction row t / 2,
-// half t % 2), delivered into a scratch LDS area that nothing reads, so no
-// register waits on them: they only bring the lines into L2.  When `live` is
-// false the load is still issued, out of range (no memory access).
-__device__ __forceinline__ void touch_kc(const Src &o, int s, int t, uint8_t *junk, bool live) {
-    const int k0 = s * BK;
-    const __amdgpu_buffer_rsrc_t r = rsrc(o.base + k0, (int64_t)o.valid * o.pitch - k0);
-    const bool ok = live & (t < o.valid) & (k0 < o.kext);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)junk, 4, ok ? (uint32_t)(t * o.pitch) : kOOB, 0, 0, 0);
-}
-
-__device__ __forceinline__ void touch_ks(const Src &o, int s, int t, uint8_t *junk, bool live) {
-    const int kr0 = s * 128;
-    const __amdgpu_buffer_rsrc_t r = rsrc(o.base + (int64_t)kr0 * o.pitch, (int64_t)(o.kext - kr0) * o.pitch);
-    const int kr = t >> 1, c = 128 * (t & 1);
-    const bool ok = live & (kr0 + kr < o.kext) & (c < o.valid);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)junk, 4, ok ? (uint32_t)(kr * o.pitch + c) : kOOB, 0, 0, 0);
-}
-
-// Rowwise E8M0 scales of a K-contiguous operand: thread t packs row t's 4 block
-// bytes of step s (blocks past the contraction read 0, i.e. 2^-127 times zeros).
+// Rowwise E8M0 scales of a K-contiguous operand.  Stage s uses blocks 2s and
+// 2s + 1, which sit in the aligned 4-byte word s / 2 of the row; thread t
+// puts row t's word into LDS [row][4] (one 4-byte LDS load per thread).
 struct RowScales {
     const uint8_t *base;   // scales of tile row 0
     int ld;                // bytes between rows (< 2^23)
@@ -183,41 +200,40 @@ struct RowScales {
     int valid;             // valid tile rows
 };
 
-struct RowScaleBytes {
-    uint32_t b[4];
-};
-
-// Issued with the stage's loads (range-checked byte loads, no branch), packed
-// into a word only when the stage is written to LDS.
-__device__ __forceinline__ RowScaleBytes rowscale_load(const RowScales &sc, int s, int t) {
+// One load instruction per wave.  The word goes straight to LDS when it lies
+// inside the row (ld % 4 == 0 and 4 blocks left); otherwise (a ragged last
+// word) its bytes are read one by one through registers and stored, and an
+// out-of-range load into `junk` keeps the instruction count.
+// WORDS: every row's words lie inside it (ld % 4 == 0, blocks per row a
+// multiple of 4), decided per launch so that the common path has no branch.
+// (Touching one cache line per row for two stages' scales costs the address
+// unit as much as a whole 1 KB data load; the scale ring in the kernel loads
+// 16 bytes per row once per 8 stages instead, where the shape allows.)
+template <bool WORDS>
+__device__ __forceinline__ void stage_rowscales(const RowScales &sc, int s, int t, uint8_t *dst, uint8_t *junk,
+                                                bool live) {
+    const int w = s >> 1;
+    const i32x4_t r4 = rsrc4(sc.base, (int64_t)sc.valid * sc.ld);
+    if (WORDS || !live || ((sc.ld % 4 == 0) & (4 * w + 4 <= sc.nblk))) {
+        to_lds4(r4, dst + 4 * (t & ~63), live & (t < sc.valid) ? (uint32_t)(t * sc.ld + 4 * w) : kOOB);
+        return;
+    }
     const __amdgpu_buffer_rsrc_t r = rsrc(sc.base, (int64_t)sc.valid * sc.ld);
-    RowScaleBytes v;
+    uint32_t word = 0;
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-        const bool ok = (t < sc.valid) & (4 * s + b < sc.nblk);
-        v.b[b] = __builtin_amdgcn_raw_buffer_load_b8(r, ok ? (uint32_t)(t * sc.ld + 4 * s + b) : kOOB, 0, 0);
+        const bool ok = (t < sc.valid) & (4 * w + b < sc.nblk);
+        word |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, ok ? (uint32_t)(t * sc.ld + 4 * w + b) : kOOB, 0, 0)
+                << (8 * b);
     }
-    return v;
+    *reinterpret_cast<uint32_t *>(dst + 4 * t) = word;
+    to_lds4(r4, junk, kOOB);
 }
 
-__device__ __forceinline__ uint32_t rowscale_word(const RowScaleBytes &v) {
-    return v.b[0] | (v.b[1] << 8) | (v.b[2] << 16) | (v.b[3] << 24);
-}
-
-// When the step's 4 block bytes of every row are one aligned word inside the
-// row (the common case: ld % 4 == 0 and a full step of blocks), they go
-// straight to LDS [row][4] with one 4-byte load per thread; returns false
-// when the byte path above has to be used instead.
-__device__ __forceinline__ bool rowscale_dma(const RowScales &sc, int s, int t, uint8_t *dst) {
-    if (!((sc.ld % 4 == 0) & (4 * s + 4 <= sc.nblk))) return false;
-    const __amdgpu_buffer_rsrc_t r = rsrc(sc.base, (int64_t)sc.valid * sc.ld);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + 4 * (t & ~63)), 4,
-                                             t < sc.valid ? (uint32_t)(t * sc.ld + 4 * s) : kOOB, 0, 0, 0);
-    return true;
-}
-
-// Colwise E8M0 scales of a K-strided operand, step s: block rows 4s..4s+3 x
-// 256 columns -> LDS [4][256], loaded by wave 0 (16 bytes per lane).
+// Colwise E8M0 scales of a K-strided operand, stage s: block rows 2s, 2s + 1
+// x 256 columns -> LDS [2][256] (lanes 32-63 fill the next 512 bytes with
+// zeros).  One load instruction per wave; only wave `owner` carries data,
+// the others load out of range into `junk`.
 struct ColScales {
     const uint8_t *base;   // block row 0, tile column 0
     int ld;                // bytes between block rows (< 2^23)
@@ -225,28 +241,38 @@ struct ColScales {
     int valid;             // valid column bytes
 };
 
-__device__ __forceinline__ void stage_colscales(const ColScales &sc, int s, uint8_t *dst, int lane) {
-    const int b0 = 4 * s;
-    const __amdgpu_buffer_rsrc_t r = rsrc(sc.base + (int64_t)b0 * sc.ld, (int64_t)(sc.nblk - b0) * sc.ld);
+__device__ __forceinline__ void stage_colscales(const ColScales &sc, int s, uint8_t *dst, uint8_t *junk, int wave,
+                                                int owner, int lane, bool live) {
+    const int b0 = 2 * s;
+    const i32x4_t r = rsrc4(sc.base + (int64_t)b0 * sc.ld, (int64_t)(sc.nblk - b0) * sc.ld);
     const int b = lane >> 4, c = lane & 15;
-    const bool ok = (b0 + b < sc.nblk) & (16 * c < sc.valid);
-    to_lds(r, dst, ok ? (uint32_t)(b * sc.ld + 16 * c) : kOOB);
+    const bool mine = wave == owner;
+    const bool ok = live & mine & (lane < 32) & (b0 + b < sc.nblk) & (16 * c < sc.valid);
+    to_lds(r, mine ? dst : junk, ok ? (uint32_t)(b * sc.ld + 16 * c) : kOOB);
 }
 
 // ------------------------------------------------------------------ fragments
+//
+// The scaled fp8 32x32x64 MFMA: lane 32g + i carries row i's contraction
+// bytes [16g, 16g + 16) (E8M0 block 0) and [32 + 16g, 48 + 16g) (block 1),
+// and the scale of row i's block g.  Any assignment of bytes to contraction
+// positions works as long as both operands use the same one and every byte
+// sits in its own block.  bf16 32x32x16: lane 32g + i carries row i's
+// elements [8g, 8g + 8) of the 16.  The 32x32 fp32 result: lane 32g + j holds
+// C[8q + 4g + r][j] in its register 4q + r.
 
-// fp8, K-contiguous tile: lane (g, i) gets row `row`'s chunks g and 4 + g.
+// fp8, K-contiguous tile: lane (g, i) gets row `row`'s chunks g and 2 + g.
 __device__ __forceinline__ i32x8_t frag_kc_f8(const uint8_t *t, int row, int g) {
-    const int sw = row & 7;
+    const int sw = (row >> 2) & 3;
     const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * (g ^ sw));
-    const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * ((4 + g) ^ sw));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * ((2 + g) ^ sw));
     return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// fp8, K-strided tile: the same 32 bytes for column col0 + m via transposed
-// reads: lane m of the 16-lane group points at contraction row k0 + m/2, bytes
-// col0 + 8 (m % 2) .. + 8, and receives 8 consecutive contraction bytes of
-// column col0 + m.
+// fp8, K-strided tile: the same 32 bytes for column col0 + m (col0 a multiple
+// of 16) via transposed reads: lane m of the 16-lane group points at
+// contraction row k0 + m/2, bytes col0 + 8 (m % 2) .. + 8, and receives 8
+// consecutive contraction bytes of column col0 + m.
 __device__ __forceinline__ i32x2_t tr8(const uint8_t *t, int k0, int col0, int m) {
     const int kr = k0 + (m >> 1);
     const uint8_t *p = t + kr * 256 + 16 * ((col0 >> 4) ^ (kr & 15)) + 8 * (m & 1);
@@ -256,15 +282,15 @@ __device__ __forceinline__ i32x2_t tr8(const uint8_t *t, int k0, int col0, int m
 __device__ __forceinline__ i32x8_t frag_ks_f8(const uint8_t *t, int col0, int g, int m) {
     const i32x2_t a = tr8(t, 16 * g, col0, m);
     const i32x2_t b = tr8(t, 16 * g + 8, col0, m);
-    const i32x2_t c = tr8(t, 64 + 16 * g, col0, m);
-    const i32x2_t d = tr8(t, 64 + 16 * g + 8, col0, m);
+    const i32x2_t c = tr8(t, 32 + 16 * g, col0, m);
+    const i32x2_t d = tr8(t, 40 + 16 * g, col0, m);
     return i32x8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // bf16, K-contiguous: lane (g, i) carries row i's elements 8g..8g+7 of the
-// 32-element half kk of the 64-element step (chunk 4 kk + g).
+// 16-element half kk of the 32-element stage (chunk 2 kk + g).
 __device__ __forceinline__ bf16x8_t frag_kc_bf16(const uint8_t *t, int row, int g, int kk) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * ((4 * kk + g) ^ (row & 7)));
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * ((2 * kk + g) ^ ((row >> 2) & 3)));
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
@@ -309,7 +335,7 @@ __device__ __forceinline__ int group_mtiles(const GemmArgs &a, int64_t g, int ca
 }
 
 // Groups up to this count keep their offsets and m-tile prefix in LDS.
-constexpr int kTab = 2048;
+constexpr int kTab = 1024;
 
 // LDS group tables, so that the tile loop reads no global memory:
 //   rs[g]  (g <= G) = row_off[g] clipped to [0, M] (TN: [0, rows]), so group
@@ -399,7 +425,7 @@ __device__ __forceinline__ void raster(int item, int ntm, int ntn, int &mt, int 
 // ------------------------------------------------------------------ kernel
 
 // What the steps and the epilogue of one tile need (32-bit counts, origins
-// precomputed), so that two of them fit in scalar registers beside the loop.
+// precomputed).
 struct Tile {
     const uint8_t *x, *y;     // operand tile origins (contraction position 0)
     const uint8_t *xs, *ys;   // E8M0 scale origins
@@ -413,24 +439,39 @@ struct Tile {
 };
 
 // A persistent grid (one workgroup per CU at most): workgroup j of XCD x runs
-// items x * per + j, + nj, ... of that XCD's contiguous range.  While a tile's
-// last step computes, the next tile's first stage is already loading into the
-// free buffer, and the epilogue stores straight from registers, so the stores
-// drain under the next tile's loads and MFMAs.  TAB: the groups' m-tile
-// prefix is kept in LDS (G <= kTab), else every lookup scans the offsets.
-template <int MODE, int DT, int OUT, bool TAB>
+// items x * per + j, + nj, ... of that XCD's contiguous range.  Four stage
+// buffers: while one step computes, the next three stages load, and the load
+// side runs ahead across tile boundaries (it walks the same tile sequence,
+// skipping tiles without steps), so a tile's first stages are in LDS when its
+// first step starts.  TAB: the groups' offsets and m-tile prefix are kept in
+// LDS (G <= kTab), else every lookup reads the offsets.
+// SC, the row scales' path (MXFP8 NT/NN): 0 bytes per stage through
+// registers, 1 a 4-byte word per row per stage, 2 the scale ring: 16 bytes per
+// row per 8-stage group into one of two LDS slots (used when every group
+// spans at least 3 stages, so that a slot is refilled only after the group
+// before the previous one is done; blocks past the contraction take the unit
+// scale in registers, so bytes read past a row's end are harmless).
+template <int MODE, int DT, int OUT, bool TAB, int SC>
 __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm_ub) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t junk[4][256];   // warm-up load sink, one row per wave
+    constexpr bool F8_ = (DT == MXQ_DTYPE_MXFP8_E4M3);
+    constexpr bool XKS_ = (MODE != MODE_NT), YKS_ = (MODE == MODE_TN);
+    constexpr bool XRING = F8_ && !XKS_ && SC == 2, YRING = F8_ && !YKS_ && SC == 2;
+    constexpr int XSB = F8_ && !XRING ? SCB : 0, YSB = F8_ && !YRING ? SCB : 0;   // per-stage scale bytes
+    constexpr int STAGE = 2 * OPB + XSB + YSB;
+    constexpr int NRING = (XRING ? 1 : 0) + (YRING ? 1 : 0);
+    static_assert(STAGE >= 64 * 512, "the epilogue stages a quarter tile in one stage buffer");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NBUF * STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NRING ? NRING * 2 * RSLOT : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t junk[1024];   // sink of the loads that carry nothing
     __shared__ int tab[TAB ? kTab + 1 : 1];
     __shared__ int rs[TAB ? kTab + 1 : 1];
     __shared__ int wsum[4];
     // the arguments that only the per-tile lookup reads live in LDS, so that
     // they do not hold scalar registers through the loop
     __shared__ GemmArgs sa;
-    // the next tile's descriptor, one copy per wave: read back only at the
-    // tile's last steps, so it holds no scalar registers through the loop
-    __shared__ Tile tnext[4];
+    // the computing tile's descriptor, one copy per wave: read back only by
+    // the epilogue, so it holds no scalar registers through the steps
+    __shared__ Tile tcur[4];
     // Per-lane indices are refreshed through an opaque copy at every tile, so
     // that values derived from them are recomputed per tile instead of being
     // hoisted out of the tile loop, where they would hold registers for good.
@@ -438,12 +479,13 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wy = (wave & 1) * 128, wx = (wave >> 1) * 128;   // this wave's quadrant (m, n)
-    int gq = lane >> 4, li = lane & 15;
+    int g32 = lane >> 5, l32 = lane & 31, l16 = lane & 15;
     auto refresh_lane = [&]() {
         asm volatile("" : "+v"(tid));
         lane = tid & 63;
-        gq = lane >> 4;
-        li = lane & 15;
+        g32 = lane >> 5;
+        l32 = lane & 31;
+        l16 = lane & 15;
     };
     constexpr bool F8 = (DT == MXQ_DTYPE_MXFP8_E4M3);
     constexpr int ESZ = F8 ? 1 : 2;
@@ -503,7 +545,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             T.yv = (int)(sa.M - m0 < BT ? sa.M - m0 : BT);
             T.kext = (int)(r1 - r0);
             T.nblk = (T.kext + 31) / 32;
-            T.ksteps = (T.kext + 127) / 128;
+            T.ksteps = (T.kext + BK - 1) / BK;
         } else {
             int mt, nt;
             raster(item, ntm, ntn, mt, nt);
@@ -552,127 +594,120 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         T.valid = 1;
         return true;
     };
-    auto next_tile = [&](int from) {
+    // the first tile at or after `from` (every one, or only those with steps)
+    auto next_tile = [&](int from, bool with_steps) {
         Tile T{};
         for (int item = from; item < hi; item += nj)
-            if (describe(item, T)) return T;
+            if (describe(item, T) && (!with_steps || T.ksteps > 0)) return T;
         T.valid = 0;
         T.ksteps = 0;
         return T;
     };
 
-    auto src_x = [&](const Tile &T) {
-        return XKS ? Src{T.x, ldb, T.kext, T.xv} : Src{T.x, ldb, T.kext, T.xv};
-    };
+    // scale-ring groups issued (load side) and begun (compute side)
+    unsigned lgrp = 0, cgrp = 0, cgrp_slot = 0;
+    const int nblk_k = (int)((a.K + 31) / 32);
+    auto src_x = [&](const Tile &T) { return Src{T.x, ldb, T.kext, T.xv}; };
     auto src_y = [&](const Tile &T) { return Src{T.y, lda, T.kext, T.yv}; };
 
-    // stage s of tile T -> stage buffer st: data tiles straight to LDS, scales
-    // by 4-byte LDS loads (or, rarely, bytes through registers)
-    auto issue = [&](const Tile &T, int s, uint8_t *st) {
-        if constexpr (XKS) stage_ks(src_x(T), s, st, wave, lane);
-        else stage_kc(src_x(T), s, st, wave, lane);
-        if constexpr (YKS) stage_ks(src_y(T), s, st + OPB, wave, lane);
-        else stage_kc(src_y(T), s, st + OPB, wave, lane);
+    // stage s of tile T -> stage buffer st (live false: a stage that carries
+    // nothing, with the same instruction count)
+    auto issue = [&](const Tile &T, int s, uint8_t *st, bool live) {
+        if constexpr (XKS) stage_ks(src_x(T), s, st, wave, lane, live);
+        else stage_kc(src_x(T), s, st, wave, lane, live);
+        if constexpr (YKS) stage_ks(src_y(T), s, st + OPB, wave, lane, live);
+        else stage_kc(src_y(T), s, st + OPB, wave, lane, live);
         if constexpr (F8) {
-            if constexpr (MODE == MODE_NT) {
-                const RowScales xr{T.xs, ldsb, T.nblk, T.xv};
-                if (!rowscale_dma(xr, s, tid, st + 2 * OPB))
-                    *reinterpret_cast<uint32_t *>(st + 2 * OPB + 4 * tid) = rowscale_word(rowscale_load(xr, s, tid));
-            } else if (wave == 0) {
-                stage_colscales(ColScales{T.xs, ldsb, T.nblk, T.xv}, s, st + 2 * OPB, lane);
-            }
-            if constexpr (MODE == MODE_TN) {
-                if (wave == 1) stage_colscales(ColScales{T.ys, ldsa, T.nblk, T.yv}, s, st + 2 * OPB + SCB, lane);
-            } else {
-                const RowScales yr{T.ys, ldsa, T.nblk, T.yv};
-                if (!rowscale_dma(yr, s, tid, st + 2 * OPB + SCB))
-                    *reinterpret_cast<uint32_t *>(st + 2 * OPB + SCB + 4 * tid) = rowscale_word(rowscale_load(yr, s, tid));
-            }
+            if constexpr (XKS)
+                stage_colscales(ColScales{T.xs, ldsb, T.nblk, T.xv}, s, st + 2 * OPB, junk, wave, 0, lane, live);
+            else if constexpr (!XRING)
+                stage_rowscales<SC == 1>(RowScales{T.xs, ldsb, T.nblk, T.xv}, s, tid, st + 2 * OPB, junk, live);
+            if constexpr (YKS)
+                stage_colscales(ColScales{T.ys, ldsa, T.nblk, T.yv}, s, st + 2 * OPB + XSB, junk, wave, 1, lane, live);
+            else if constexpr (!YRING)
+                stage_rowscales<SC == 1>(RowScales{T.ys, ldsa, T.nblk, T.yv}, s, tid, st + 2 * OPB + XSB, junk, live);
+
         }
     };
-    // always exactly two loads per thread (out of range past the tile's steps),
-    // so that a step's wait can keep exactly two loads in flight
-    auto touch = [&](const Tile &T, int s) {
-        const bool live = T.valid && s < T.ksteps;
-        if constexpr (XKS) touch_ks(src_x(T), s, tid, junk[wave], live);
-        else touch_kc(src_x(T), s, tid, junk[wave], live);
-        if constexpr (YKS) touch_ks(src_y(T), s, tid, junk[wave], live);
-        else touch_kc(src_y(T), s, tid, junk[wave], live);
-    };
+    // load instructions per wave per stage (at least: a group's first stage
+    // adds its ring loads, which only makes the step waits stricter), and
+    // epilogue memory instructions per wave
+    constexpr int kStageOps = 8 + (F8 ? 2 - NRING : 0);
+    constexpr int kEpiOps = OUT == MXQ_DTYPE_BF16 ? 32 : 64;
 
-    f32x4_t acc[8][8];
+    f32x16_t acc[4][4];
 #pragma unroll
-    for (int x = 0; x < 8; x++)
+    for (int x = 0; x < 4; x++)
 #pragma unroll
-        for (int y = 0; y < 8; y++) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int y = 0; y < 4; y++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[x][y][r] = 0.f;
 
-    auto compute = [&](const uint8_t *st) {
-        const uint8_t *tx = st, *ty = st + OPB, *scx = st + 2 * OPB, *scy = st + 2 * OPB + SCB;
+    // one stage: each wave's 128 x 128 quadrant as 4 x 4 MFMA tiles of 32 x 32
+    auto compute = [&](const uint8_t *st, int s) {
+        const uint8_t *tx = st, *ty = st + OPB, *scx = st + 2 * OPB, *scy = st + 2 * OPB + XSB;
         if constexpr (F8) {
-            i32x8_t fy[8];
-            int sy[8];
+            const int sb = 2 * (s & 1) + g32;   // row-scale byte of this stage's block g32 (per-stage words)
+            // ring: this stage's blocks are bytes 2 (s % 8) + g32 of the row's
+            // 16; blocks past the contraction take the unit scale
+            const uint8_t *rg = ring + (cgrp_slot & 1) * NRING * RSLOT;
+            const int rb = 2 * (s % RGS) + g32;
+            const bool in_k = 2 * s + g32 < nblk_k;
+            i32x8_t fy[4];
+            int sy[4];
 #pragma unroll
-            for (int y = 0; y < 8; y++) {
-                const int m = wy + 16 * y;
+            for (int y = 0; y < 4; y++) {
+                const int m = wy + 32 * y;
                 if constexpr (YKS) {
-                    fy[y] = frag_ks_f8(ty, m, gq, li);
-                    sy[y] = scy[gq * 256 + m + li];
+                    fy[y] = frag_ks_f8(ty, m + 16 * ((lane >> 4) & 1), g32, l16);
+                    sy[y] = scy[g32 * 256 + m + l32];
+                } else if constexpr (YRING) {
+                    fy[y] = frag_kc_f8(ty, m + l32, g32);
+                    sy[y] = in_k ? rg[(XRING ? RSLOT : 0) + (m + l32) * 16 + rb] : 127;
                 } else {
-                    fy[y] = frag_kc_f8(ty, m + li, gq);
-                    sy[y] = scy[(m + li) * 4 + gq];
+                    fy[y] = frag_kc_f8(ty, m + l32, g32);
+                    sy[y] = scy[(m + l32) * 4 + sb];
                 }
             }
 #pragma unroll
-            for (int x = 0; x < 8; x++) {
-                const int n = wx + 16 * x;
+            for (int x = 0; x < 4; x++) {
+                const int n = wx + 32 * x;
                 i32x8_t fx;
                 int sx;
                 if constexpr (XKS) {
-                    fx = frag_ks_f8(tx, n, gq, li);
-                    sx = scx[gq * 256 + n + li];
+                    fx = frag_ks_f8(tx, n + 16 * ((lane >> 4) & 1), g32, l16);
+                    sx = scx[g32 * 256 + n + l32];
+                } else if constexpr (XRING) {
+                    fx = frag_kc_f8(tx, n + l32, g32);
+                    sx = in_k ? rg[(n + l32) * 16 + rb] : 127;
                 } else {
-                    fx = frag_kc_f8(tx, n + li, gq);
-                    sx = scx[(n + li) * 4 + gq];
+                    fx = frag_kc_f8(tx, n + l32, g32);
+                    sx = scx[(n + l32) * 4 + sb];
                 }
 #pragma unroll
-                for (int y = 0; y < 8; y++)
-                    acc[x][y] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fx, fy[y], acc[x][y], 0, 0, 0, sx, 0,
-                                                                                  sy[y]);
+                for (int y = 0; y < 4; y++)
+                    acc[x][y] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fx, fy[y], acc[x][y], 0, 0, 0, sx, 0,
+                                                                                 sy[y]);
             }
-            // Issue order: a wave's instructions issue in order and an MFMA holds
-            // the issue for its whole pipeline slot, so LDS reads bunched between
-            // MFMA runs would leave the LDS idle.  Interleave one read after each
-            // MFMA (after the first few reads that the first MFMAs need).
-#pragma unroll
-            for (int i = 0; i < 8; i++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-            for (int i = 0; i < 40; i++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
         } else {
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) {
-                bf16x8_t fy[8];
+                bf16x8_t fy[4];
 #pragma unroll
-                for (int y = 0; y < 8; y++) fy[y] = frag_kc_bf16(ty, wy + 16 * y + li, gq, kk);
+                for (int y = 0; y < 4; y++) fy[y] = frag_kc_bf16(ty, wy + 32 * y + l32, g32, kk);
 #pragma unroll
-                for (int x = 0; x < 8; x++) {
-                    const bf16x8_t fx = frag_kc_bf16(tx, wx + 16 * x + li, gq, kk);
+                for (int x = 0; x < 4; x++) {
+                    const bf16x8_t fx = frag_kc_bf16(tx, wx + 32 * x + l32, g32, kk);
 #pragma unroll
-                    for (int y = 0; y < 8; y++)
-                        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx, fy[y], acc[x][y], 0, 0, 0);
+                    for (int y = 0; y < 4; y++)
+                        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx, fy[y], acc[x][y], 0, 0, 0);
                 }
             }
         }
     };
 
-    // ---- epilogue: lane holds C[m][n .. n+3] for m = wy + 16y + li, n = wx + 16x + 4gq;
-    // stored straight from registers with buffer stores (one 32-bit row offset
-    // per y, the column as the immediate offset; elements outside the tile go
-    // out of range and are dropped).  A row's 256 bytes of one wave leave in
-    // eight 32-byte pieces, which meet again in L2.
+    // ---- epilogue: lane (g32, l32) holds C[m][n .. n+3] with m = wy + 32y + l32,
+    // n = wx + 32x + 8q + 4 g32, in registers 4q .. 4q+3 of acc[x][y].
     const int ldo = (int)(a.ld_out * OSZ);   // output row pitch in bytes (< 2^23)
     const bool accumulate = a.accumulate != 0;
     auto epilogue = [&](const Tile &T, uint8_t *stg) {
@@ -680,124 +715,188 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         if constexpr (OUT == MXQ_DTYPE_BF16) {
             // Through LDS, so that each output row leaves as 512 contiguous
             // bytes (16-byte nontemporal stores, 32 lanes per row): the stage
-            // buffer the last step read from holds half the tile, 128 rows x
-            // 512 B with 16-byte chunk c of row m at c ^ (m & 31); the two
-            // waves holding rows [128h, 128h + 128) (waves h and h + 2) write
-            // half h, then all four store it.
+            // buffer the last step read from holds a quarter of the tile, 64
+            // rows x 512 B with 16-byte chunk c of row m at c ^ (m & 31).
+            // The two waves holding rows [64h, 64h + 64) write quarter h (their
+            // fragment rows y = 2 (h & 1) + {0, 1}), then all four store it.
             typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
-                step_barrier<63>();   // everyone is done reading stg (last step's fragments, or half h - 1)
-                if ((wave & 1) == h) {
+            for (int h = 0; h < 4; h++) {
+                step_barrier<63>();   // everyone is done reading stg (last step's fragments, or quarter h - 1)
+                if ((wave & 1) == (h >> 1)) {
 #pragma unroll
-                    for (int y = 0; y < 8; y++) {
+                    for (int yy = 0; yy < 2; yy++) {
+                        const int y = 2 * (h & 1) + yy;
                         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int x = 0; x < 8; x++) asm volatile("" : "+a"(acc[x][y]));
-                        const int m = 16 * y + li;
+                        for (int x = 0; x < 4; x++) asm volatile("" : "+a"(acc[x][y]));
+                        const int m = 32 * yy + l32;
 #pragma unroll
-                        for (int x = 0; x < 8; x++) {
-                            const int n = wx + 16 * x + 4 * gq;
-                            const f32x4_t v = acc[x][y];
-                            bf16x4_t b;
-                            b.x = (__bf16)v.x; b.y = (__bf16)v.y; b.z = (__bf16)v.z; b.w = (__bf16)v.w;
-                            *reinterpret_cast<bf16x4_t *>(stg + m * 512 + 16 * ((n >> 3) ^ (m & 31)) + 8 * ((n >> 2) & 1)) = b;
-                        }
+                        for (int x = 0; x < 4; x++)
+#pragma unroll
+                            for (int q = 0; q < 4; q++) {
+                                const int chunk = (wx + 32 * x + 8 * q) >> 3;
+                                bf16x4_t b;
+                                b.x = (__bf16)acc[x][y][4 * q];
+                                b.y = (__bf16)acc[x][y][4 * q + 1];
+                                b.z = (__bf16)acc[x][y][4 * q + 2];
+                                b.w = (__bf16)acc[x][y][4 * q + 3];
+                                *reinterpret_cast<bf16x4_t *>(stg + m * 512 + 16 * (chunk ^ (m & 31)) + 8 * g32) = b;
+                            }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                step_barrier<63>();   // half h is in LDS
+                step_barrier<63>();   // quarter h is in LDS
 #pragma unroll
-                for (int j = 0; j < 16; j++) {
-                    const int q = j * NTHR + tid;
-                    const int m = q >> 5, c = q & 31;
-                    const int row = 128 * h + m;
+                for (int j = 0; j < 8; j++) {
+                    const int qd = j * NTHR + tid;
+                    const int m = qd >> 5, c = qd & 31;
+                    const int row = 64 * h + m;
                     const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + m * 512 + 16 * (c ^ (m & 31)));
                     const uint32_t off = (row < T.yv) & (8 * c < T.xv) ? (uint32_t)(row * opaque(ldo) + 16 * c) : kOOB;
                     __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 2);   // nt
                 }
             }
         } else {
-            // fp32: straight from the accumulators (a row's 256 bytes of one
-            // wave in eight 64-byte pieces)
+            // fp32: straight from the accumulators
 #pragma unroll
-            for (int y = 0; y < 8; y++) {
+            for (int y = 0; y < 4; y++) {
                 // one row of fragments at a time, so that only its accumulators
                 // are copied out of the matrix registers at once
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int x = 0; x < 8; x++) asm volatile("" : "+a"(acc[x][y]));
-                const int ml = wy + 16 * y + li;
-                const uint32_t row = ml < T.yv ? (uint32_t)(ml * opaque(ldo) + (wx + 4 * gq) * OSZ) : kOOB;
+                for (int x = 0; x < 4; x++) asm volatile("" : "+a"(acc[x][y]));
+                const int ml = wy + 32 * y + l32;
+                const uint32_t row = ml < T.yv ? (uint32_t)(ml * opaque(ldo) + (wx + 4 * g32) * OSZ) : kOOB;
 #pragma unroll
-                for (int x = 0; x < 8; x++) {
-                    // columns past N (last n tile only) go out of range too
-                    const uint32_t off = wx + 16 * x + 4 * gq < T.xv ? row + 16 * x * OSZ : kOOB;
-                    f32x4_t w = acc[x][y];
-                    if (accumulate) w += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), ro, off, 0, 0);
-                }
+                for (int x = 0; x < 4; x++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        // columns past N (last n tile only) go out of range too
+                        const uint32_t off = wx + 32 * x + 8 * q + 4 * g32 < T.xv ? row + (32 * x + 8 * q) * OSZ : kOOB;
+                        f32x4_t w = f32x4_t{acc[x][y][4 * q], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2],
+                                            acc[x][y][4 * q + 3]};
+                        if (accumulate)
+                            w += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, w), ro, off, 0, 0);
+                    }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // vector memory operations each wave's epilogue issues (loads it waits
-    // for itself aside): 2 x 16 row stores (bf16), 64 stores (fp32)
-    constexpr int kEpiOps = OUT == MXQ_DTYPE_BF16 ? 32 : 64;
-    constexpr int kFirstWait = 2 + kEpiOps < 63 ? 2 + kEpiOps : 63;
 
-    Tile cur = next_tile(lo);
-    if (!cur.valid) return;
-    int gs = 0;   // steps this workgroup has run: step gs computes from stage buffer gs & 1
-    if (cur.ksteps > 0) issue(cur, 0, smem);
-    touch(cur, 1);
-    // Vector memory operations of a wave complete in issue order on this
-    // target, loads and stores alike (the compiler's wait counts rely on the
-    // same), so a step's wait may leave every later operation in flight: the
-    // 2 warm-up loads, and after a tile whose last step prefetched this one,
-    // also the previous tile's kEpiOps epilogue stores (vmcnt saturates at 63,
-    // which still covers the stage when more operations follow it).
-    bool after_epilogue = false;
+    // ---- the load side: tile `ld` (with steps), its next stage `ls`
+    Tile ld = next_tile(lo, true);
+    int ls = 0;
+    unsigned issued = 0, consumed = 0;
+    // epilogues run so far, and for each stage buffer that count when its
+    // stage was issued (8 bits each): a step's wait leaves in flight every
+    // memory instruction issued after its stage
+    unsigned epis = 0, epi_at = 0;
+    bool pending = false;   // an issued stage the load side has not moved past yet
+    // The scale ring: before the load side issues a group's first stage, the
+    // group's 16 scale bytes per row go into slot lgrp & 1 (this runs ahead of
+    // the stage itself, outside the step's MFMA block; the step waits only
+    // grow stricter for it).
+    auto ring_issue = [&]() {
+        if constexpr (NRING > 0) {
+            if (ld.valid && ls % RGS == 0) {
+                uint8_t *slot = ring + (lgrp & 1) * NRING * RSLOT;
+                const int row = 64 * wave + lane;
+                if constexpr (XRING) {
+                    const i32x4_t r = rsrc4(ld.xs, (int64_t)ld.xv * ldsb);
+                    to_lds(r, slot + 1024 * wave, row < ld.xv ? (uint32_t)(row * ldsb + 2 * ls) : kOOB);
+                }
+                if constexpr (YRING) {
+                    const i32x4_t r = rsrc4(ld.ys, (int64_t)ld.yv * ldsa);
+                    to_lds(r, slot + (XRING ? RSLOT : 0) + 1024 * wave,
+                           row < ld.yv ? (uint32_t)(row * ldsa + 2 * ls) : kOOB);
+                }
+                lgrp++;
+            }
+        }
+    };
+    auto issue_next = [&]() {
+        const int slot = issued & (NBUF - 1);
+        issue(ld, ls, smem + slot * STAGE, ld.valid != 0);
+        epi_at = (epi_at & ~(0xFFu << (8 * slot))) | ((epis & 0xFFu) << (8 * slot));
+        issued++;
+        pending = true;
+    };
+    auto advance_load = [&]() {
+        if (pending && ld.valid && ++ls == ld.ksteps) {
+            ld = next_tile(ld.item + nj, true);
+            ls = 0;
+        }
+        pending = false;
+    };
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; j++) {
+        ring_issue();
+        issue_next();
+        advance_load();
+    }
+
+    // ---- the compute side: every tile, in the same order
+    {
+        const Tile c0 = next_tile(lo, false);
+        if (!c0.valid) return;   // (the loads issued above carried nothing)
+        tcur[wave] = c0;
+    }
     for (;;) {
         refresh_lane();
-        tnext[wave] = next_tile(cur.item + nj);
-        for (int s = 0; s < cur.ksteps; s++, gs++) {
-            // (the condition is opaque so that the compiler does not peel the
-            // first step into a second copy of the loop body)
-            if (opaque(__builtin_amdgcn_readfirstlane((int)((s == 0) & after_epilogue))))
-                // vmcnt(kFirstWait) expcnt(7) lgkmcnt(15)
-                __builtin_amdgcn_s_waitcnt((kFirstWait & 15) | ((kFirstWait >> 4) << 14) | 0x0F70);   // vmcnt(63) expcnt(7) lgkmcnt(15)
-            else __builtin_amdgcn_s_waitcnt(0x0F72);                                    // vmcnt(2) expcnt(7) lgkmcnt(15)
-            step_barrier<63>();   // everyone's loads have landed, and step gs - 1's reads are done
-            uint8_t *nb = smem + ((gs + 1) & 1) * STAGE;
-            if (s + 2 < cur.ksteps) {
-                issue(cur, s + 1, nb);
-                touch(cur, s + 2);
+        const int K = tcur[wave].ksteps;
+        for (int s = 0; s < K; s++) {
+            // the load side moves on here, before this step's MFMAs, so that
+            // its branches do not split them from the issue below
+            advance_load();
+            ring_issue();
+            // Vector memory operations of a wave complete in issue order on
+            // this target, loads and stores alike (the compiler's wait counts
+            // rely on the same), so this stage has landed once no more than
+            // the later ones are in flight: the next two stages, plus an
+            // epilogue's memory operations if one ran since this stage was
+            // issued (vmcnt saturates at 63; more than that follows then).
+            const unsigned slot = consumed & (NBUF - 1);
+            const unsigned since = (epis - (epi_at >> (8 * slot))) & 0xFFu;
+            if (opaque(__builtin_amdgcn_readfirstlane((int)since)) == 0) {
+                constexpr int n = 2 * kStageOps;
+                __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+            } else if (opaque(__builtin_amdgcn_readfirstlane((int)since)) == 1) {
+                constexpr int n = 2 * kStageOps + kEpiOps < 63 ? 2 * kStageOps + kEpiOps : 63;
+                __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
             } else {
-                const Tile nxt = tnext[wave];
-                if (s + 1 < cur.ksteps) issue(cur, s + 1, nb);
-                else if (nxt.ksteps > 0) issue(nxt, 0, nb);
-                touch(nxt, s + 2 - cur.ksteps);
+                __builtin_amdgcn_s_waitcnt(0xCF7F);   // vmcnt(63)
             }
-            compute(smem + (gs & 1) * STAGE);
-        }
-        // the stage buffer the last step read from (or, after a tile without
-        // steps, the one no load is headed for)
-        epilogue(cur, smem + ((gs + 1) & 1) * STAGE);
-        const Tile nxt = tnext[wave];
-        if (!nxt.valid) break;
-        after_epilogue = cur.ksteps > 0;
-        if (cur.ksteps == 0 && nxt.ksteps > 0) {
-            // nothing prefetched the next tile; buffer gs & 1 was last read by
-            // step gs - 2, which every wave finished before step gs - 1's barrier
-            issue(nxt, 0, smem + (gs & 1) * STAGE);
-            touch(nxt, 1);
-        }
+            step_barrier<63>();   // everyone's stage has landed, and the previous step's reads are done
+            if constexpr (NRING > 0) {
+                if (s % RGS == 0) cgrp_slot = cgrp++;
+            }
+            compute(smem + slot * STAGE, s);
+            // the next stage's loads (into the buffer the previous step read,
+            // free since the barrier), set up in the shadow of the MFMAs:
+            // a wave issues in order, so scalar and vector work placed
+            // between MFMAs runs while the matrix core works
+            issue_next();
 #pragma unroll
-        for (int x = 0; x < 8; x++)
+            for (int i = 0; i < 16; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x006, 14, 0);   // then up to 14 VALU / SALU
+            }
+            consumed++;
+        }
+        // the stage buffer the last step read (no load is headed for it)
+        epilogue(tcur[wave], smem + ((consumed + NBUF - 1) & (NBUF - 1)) * STAGE);
+        epis++;
+        const Tile nc = next_tile(tcur[wave].item + nj, false);
+        if (!nc.valid) break;
+        tcur[wave] = nc;
 #pragma unroll
-            for (int y = 0; y < 8; y++) acc[x][y] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        cur = nxt;
+        for (int x = 0; x < 4; x++)
+#pragma unroll
+            for (int y = 0; y < 4; y++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) acc[x][y][r] = 0.f;
     }
 }
 
@@ -833,12 +932,31 @@ hipError_t launch_mode(const GemmArgs &g, hipStream_t stream) {
     if (grid < kXCD) grid = kXCD;
     const int64_t need = (nwork + kXCD - 1) / kXCD * kXCD;
     if (need < grid) grid = need;
-    if (g.G <= kTab)
-        hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true>), dim3((unsigned)grid), dim3(NTHR), 0, stream, g,
-                           (int)ntn, (int)ntm);
-    else
-        hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false>), dim3((unsigned)grid), dim3(NTHR), 0, stream, g,
-                           (int)ntn, (int)ntm);
+    // the row scales' path (see the kernel's SC)
+    int sc = 1;
+    if (DT == MXQ_DTYPE_MXFP8_E4M3 && MODE != MODE_TN) {
+        const int64_t nblk = (g.K + 31) / 32, ks = (g.K + BK - 1) / BK;
+        const bool ld4 = g.A.ld_scales % 4 == 0 && (MODE == MODE_NN || g.B.ld_scales % 4 == 0);
+        const bool ring = ld4 && ks >= 3 && (ks % RGS == 0 || ks % RGS >= 3);
+        sc = ring ? 2 : (ld4 && nblk % 4 == 0 ? 1 : 0);
+    }
+    const dim3 gd((unsigned)grid), bd(NTHR);
+    const int a1 = (int)ntn, a2 = (int)ntm;
+    const bool tab = g.G <= kTab;
+    if constexpr (DT != MXQ_DTYPE_MXFP8_E4M3 || MODE == MODE_TN) {
+        if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 1>), gd, bd, 0, stream, g, a1, a2);
+        else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 1>), gd, bd, 0, stream, g, a1, a2);
+        (void)sc;
+    } else if (sc == 2) {
+        if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 2>), gd, bd, 0, stream, g, a1, a2);
+        else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 2>), gd, bd, 0, stream, g, a1, a2);
+    } else if (sc == 1) {
+        if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 1>), gd, bd, 0, stream, g, a1, a2);
+        else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 1>), gd, bd, 0, stream, g, a1, a2);
+    } else {
+        if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 0>), gd, bd, 0, stream, g, a1, a2);
+        else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 0>), gd, bd, 0, stream, g, a1, a2);
+    }
     return hipGetLastError();
 }
 

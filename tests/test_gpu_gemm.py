@@ -315,7 +315,7 @@ def test_persistent_many_tiles_mxfp8(mxq, mode, N, KM, max_wg):
 
 
 def test_many_groups_scan_path(mxq):
-    """More groups than the LDS tile table holds (4096): every tile lookup scans
+    """More groups than the LDS group tables hold (1024): every tile lookup scans
     the offsets on the device; mostly empty groups, a few of several tiles."""
     rng = np.random.default_rng(22)
     G, N, K = 4500, 32, 64
