@@ -215,7 +215,7 @@ __device__ __forceinline__ void stage_rowscales(const RowScales &sc, int s, int 
     const int w = s >> 1;
     const i32x4_t r4 = rsrc4(sc.base, (int64_t)sc.valid * sc.ld);
     if (WORDS || !live || ((sc.ld % 4 == 0) & (4 * w + 4 <= sc.nblk))) {
-        to_lds4(r4, dst + 4 * (t & ~63), live & (t < sc.valid) ? (uint32_t)(t * sc.ld + 4 * w) : kOOB);
+        to_lds4(r4, dst + 4 * (t & ~63), (live & (t < sc.valid)) ? (uint32_t)(t * sc.ld + 4 * w) : kOOB);
         return;
     }
     const __amdgpu_buffer_rsrc_t r = rsrc(sc.base, (int64_t)sc.valid * sc.ld);
@@ -753,7 +753,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
                     const int m = qd >> 5, c = qd & 31;
                     const int row = 64 * h + m;
                     const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + m * 512 + 16 * (c ^ (m & 31)));
-                    const uint32_t off = (row < T.yv) & (8 * c < T.xv) ? (uint32_t)(row * opaque(ldo) + 16 * c) : kOOB;
+                    const uint32_t off = ((row < T.yv) & (8 * c < T.xv)) ? (uint32_t)(row * opaque(ldo) + 16 * c) : kOOB;
                     __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 2);   // nt
                 }
             }
