@@ -24,6 +24,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
 Prints one JSON line.
 """
 import argparse
+import collections
+import csv
+import statistics
 import json
 import os
 import sys
@@ -207,6 +210,75 @@ def cpu_baseline(rows=256):
                       f"({total_bytes / 1e6:.1f} MB algorithmic), {dt:.1f} s on 1 host thread"}
 
 
+# ------------------------------------------------------------------ GEMM profile summary
+# `--summarize-gemm-profile DIR`: the per-GEMM table of the grouped-GEMM
+# profile from a rocprofv3 kernel trace (DIR/trace) and TCC_HIT/TCC_MISS
+# (DIR/tcc) and FETCH_SIZE (DIR/fetch) counter runs of `--moe-only`, which
+# runs, per routing, three forward+backward layers and then each of the six
+# grouped GEMMs three times, always in the order FC1, FC2, FC2 dgrad, FC2
+# wgrad, FC1 dgrad, FC1 wgrad; the GEMM dispatches are labelled from that order.
+
+GP_ORDER = ["FC1 forward", "FC2 forward", "FC2 dgrad", "FC2 wgrad", "FC1 dgrad", "FC1 wgrad"]
+GP_MODE = {"FC1 forward": "NT bf16", "FC2 forward": "NT MXFP8", "FC2 dgrad": "NN MXFP8", "FC2 wgrad": "TN MXFP8",
+           "FC1 dgrad": "NN MXFP8", "FC1 wgrad": "TN MXFP8"}
+_FC1, _FC2 = 2 * 65536 * 2 * 768 * 2048, 2 * 65536 * 2048 * 768   # 65,536 routed rows, hidden 2048, intermediate 768
+GP_FL = {"FC1 forward": _FC1, "FC2 forward": _FC2, "FC2 dgrad": _FC2, "FC2 wgrad": _FC2, "FC1 dgrad": _FC1,
+         "FC1 wgrad": _FC1}
+# algorithmic bytes of each GEMM: operands and their E8M0 scales read once, bf16 output written once
+GP_BY = {"FC1 forward": 1275e6, "FC2 forward": 528e6, "FC2 dgrad": 447e6, "FC2 wgrad": 593e6, "FC1 dgrad": 787e6,
+         "FC1 wgrad": 1048e6}
+GP_PEAK = {"NT bf16": 2500.0}
+GP_FETCH_SCALE = 2.0   # FETCH_SIZE calibration against a plain copy of known size
+
+
+def _gemm_labels(ids):
+    per_routing = 6 * 3 + 6 * 3
+    out = {}
+    for k, d in enumerate(ids):
+        j = k % per_routing
+        out[d] = GP_ORDER[j % 6] if j < 18 else GP_ORDER[(j - 18) // 3]
+    return out
+
+
+def summarize_gemm_profile(base):
+    tr = [r for r in csv.DictReader(open(f"{base}/trace/moe_kernel_trace.csv")) if "gemm_kernel" in r["Kernel_Name"]]
+    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+    lab = _gemm_labels([int(r["Dispatch_Id"]) for r in tr])
+    dur = collections.defaultdict(list)
+    for r in tr:
+        dur[lab[int(r["Dispatch_Id"])]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counters(path, names):
+        rows = [r for r in csv.DictReader(open(path)) if "gemm_kernel" in r["Kernel_Name"]]
+        disp = sorted({int(r["Dispatch_Id"]) for r in rows})
+        lb = _gemm_labels(disp)
+        acc = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in rows:
+            if r["Counter_Name"] in names:
+                acc[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        per = collections.defaultdict(list)
+        for d, v in acc.items():
+            per[lb[d]].append(v)
+        return per
+
+    tcc = counters(f"{base}/tcc/moe_counter_collection.csv", {"TCC_HIT_sum", "TCC_MISS_sum"})
+    fet = counters(f"{base}/fetch/moe_counter_collection.csv", {"FETCH_SIZE"})
+    print("| GEMM | mode | dispatches | median us | TFLOP/s | % of dense peak | algorithmic bytes | flop/B |"
+          " roofline-attainable TFLOP/s | % of attainable | L2 hit rate | HBM read MB |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for g in GP_ORDER:
+        us = statistics.median(dur[g])
+        tf = GP_FL[g] / us / 1e6
+        peak = GP_PEAK.get(GP_MODE[g], 5000.0)
+        ai = GP_FL[g] / GP_BY[g]
+        att = min(peak, ai * 8.0)   # flop/B x 8 TB/s, in TFLOP/s
+        hits = statistics.median(v["TCC_HIT_sum"] / max(1.0, v["TCC_HIT_sum"] + v["TCC_MISS_sum"]) for v in tcc[g])
+        mb = statistics.median(v["FETCH_SIZE"] for v in fet[g]) * 1024 * GP_FETCH_SCALE / 1e6
+        print(f"| {g} | {GP_MODE[g]} | {len(dur[g])} | {us:.1f} | {tf:.0f} | {100 * tf / peak:.1f} | {GP_BY[g] / 1e6:.0f} MB |"
+              f" {ai:.0f} | {att:.0f} | {100 * tf / att:.1f} | {100 * hits:.1f} % | {mb:.0f} |")
+
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,10 +289,15 @@ def main():
     ap.add_argument("--moe-only", action="store_true",
                     help="only run the expert-layer section once and print its record (for profiling the GEMMs)")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--summarize-gemm-profile", metavar="DIR",
+                    help="print the per-GEMM table of a --moe-only profile (CPU only, no GPU run)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the dominant call 3 times and a 1 GiB device copy 3 times "
                          "(for the HBM byte counters of rocprofv3 --pmc)")
     args = ap.parse_args()
+    if args.summarize_gemm_profile:
+        summarize_gemm_profile(args.summarize_gemm_profile)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the fused path shards by rows with no exchange, see the design notes", file=sys.stderr)
