@@ -12,40 +12,50 @@
 //
 // Design (the pages' cuBLASLt / CuTe GEMMs for NVIDIA parts are prior art only):
 //   * A workgroup of 4 waves computes a 256 x 256 output tile, each wave a
-//     128 x 128 quadrant as 8 x 8 MFMA tiles of 16 x 16 (256 fp32 accumulators
-//     per lane).  Per 128-byte contraction step a wave reads 16 fragments of
-//     2 KB from LDS for 64 MFMAs, which keeps LDS reads at half of its
-//     bandwidth while the matrix cores run.
-//   * Operand tiles go from HBM straight into LDS (buffer_load ... lds, 16 bytes
-//     per lane), double-buffered: one barrier per step, the next step's loads in
-//     flight during the current step's MFMAs.  Buffer loads are range-checked by
-//     the hardware, so rows, columns and contraction tails outside the operand
+//     128 x 128 quadrant as 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators
+//     per lane, in the matrix registers).  MXFP8 uses
+//     v_mfma_scale_f32_32x32x64_f8f6f4: lane 32g + i carries row i's
+//     contraction bytes [16g, 16g + 16) and [32 + 16g, 48 + 16g) and the E8M0
+//     scale of row i's 32-element block g, so the block scales are applied
+//     inside the matrix core.  bf16 uses v_mfma_f32_32x32x16_bf16.
+//   * A stage is 64 contraction bytes of the tile's 256 rows per operand
+//     (16 KB).  Operand tiles go from memory straight into LDS (buffer_load
+//     ... lds, 16 bytes per lane); buffer loads are range-checked by the
+//     hardware, so rows, columns and contraction tails outside the operand
 //     arrive as zeros without a branch.
+//   * Four stage buffers.  Stage c is computed from registers while stage
+//     c + 1 sits in LDS and stages c + 2 .. c + 4 load: after two of stage c's
+//     MFMAs a wave waits for stage c + 1, passes the step's barrier, then
+//     alternates the remaining MFMAs with the reads of stage c + 1's fragments
+//     (into a second register set) and with the loads of stage c + 4 (into
+//     stage c's buffer).
 //   * LDS tiles are XOR-swizzled at 16-byte granularity (chunk c of row r at
-//     c ^ (r mod 8) for 128-byte rows, c ^ (r mod 16) for 256-byte rows), which
-//     makes both the fragment reads and the transposed reads conflict-free.
-//   * MXFP8 uses v_mfma_scale_f32_16x16x128_f8f6f4: lane 16g+i carries row i's
-//     contraction bytes [16g, 16g+16) and [64+16g, 80+16g) and the E8M0 scale of
-//     row i's 32-element block g, so the block scales are applied inside the
-//     matrix core.  bf16 uses v_mfma_f32_16x16x32_bf16.
+//     c ^ ((r >> 2) & 3) for 64-byte rows, c ^ (k & 15) for the 256-byte
+//     contraction rows of K-strided operands), which keeps the fragment reads
+//     and the transposed reads conflict-free.
 //   * Operands whose contraction index is strided in memory (the dgrad weight
 //     and both wgrad operands) are staged as they lie ([k][column] tiles) and
 //     read with ds_read_b64_tr_b8, which transposes 16 lanes' 8-byte rows.
+//   * The row scales of K-contiguous MXFP8 operands come through a two-slot
+//     ring, 16 bytes per row per 8 stages, instead of a load per stage.
 //   * The output tile is computed transposed (the MFMA's first operand is the
-//     N side), so every lane owns 4 consecutive output columns of one row.
+//     N side), so every lane owns 4 consecutive output columns of one row; a
+//     bf16 tile is staged through LDS so that each output row leaves as 512
+//     contiguous bytes, fp32 goes straight from the accumulators.
 //   * Group boundaries come from the device offsets only.  Each workgroup of
 //     an M-grouped launch first builds the groups' m-tile prefix sums in LDS
-//     (for up to 4096 groups; beyond that every lookup scans the offsets), so
+//     (for up to 1024 groups; beyond that every lookup scans the offsets), so
 //     the exact tile count is known on the device and a tile's group is two
 //     wave-wide LDS probes away.
 //   * The grid is persistent: one workgroup per CU, each looping over its
 //     share of the tiles.  Each XCD takes a contiguous range of tiles (one
-//     expert's tiles share that XCD's L2).  The next tile's first stage is
-//     loaded during the current tile's last step, and the epilogue stores
-//     straight from the accumulators, so consecutive tiles overlap.
+//     expert's tiles share that XCD's L2).  The load side walks the same tile
+//     sequence as the compute side, a few stages ahead, so consecutive tiles
+//     overlap.
 #include "gemm_internal.h"
 
 #include <string>
+#include <type_traits>
 
 namespace mxq {
 namespace {
@@ -159,35 +169,29 @@ struct Src {
 // access; zeros land in LDS).  The step waits count on that.
 
 // K-contiguous stage s -> LDS [256 rows][64 B], chunk c of row r at c ^ ((r >> 2) & 3).
-// Wave w fills 1 KB blocks 4w..4w+3 (16 rows each).
-__device__ __forceinline__ void stage_kc(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live) {
+// Wave w fills 1 KB blocks 4w..4w+3 (16 rows each); this is its load j of 4.
+__device__ __forceinline__ void stage_kc(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live, int j) {
     const int k0 = s * BK;
     const i32x4_t r = rsrc4(o.base + k0, (int64_t)o.valid * o.pitch - k0);
     const int pitch = opaque(o.pitch);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int b = wave * 4 + j;
-        const int row = 16 * b + (lane >> 2);
-        const int c = (lane & 3) ^ ((row >> 2) & 3);
-        const bool ok = live & (row < o.valid) & (k0 + 16 * c < o.kext);
-        to_lds(r, dst + 1024 * b, ok ? (uint32_t)(row * pitch + 16 * c) : kOOB);
-    }
+    const int b = wave * 4 + j;
+    const int row = 16 * b + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const bool ok = live & (row < o.valid) & (k0 + 16 * c < o.kext);
+    to_lds(r, dst + 1024 * b, ok ? (uint32_t)(row * pitch + 16 * c) : kOOB);
 }
 
 // K-strided stage s -> LDS [64 contraction rows][256 B], chunk c of row k at c ^ (k & 15).
-// Wave w fills 1 KB blocks 4w..4w+3 (4 contraction rows each).
-__device__ __forceinline__ void stage_ks(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live) {
+// Wave w fills 1 KB blocks 4w..4w+3 (4 contraction rows each); this is its load j of 4.
+__device__ __forceinline__ void stage_ks(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live, int j) {
     const int kr0 = s * BK;
     const i32x4_t r = rsrc4(o.base + (int64_t)kr0 * o.pitch, (int64_t)(o.kext - kr0) * o.pitch);
     const int pitch = opaque(o.pitch);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int b = wave * 4 + j;
-        const int kr = 4 * b + (lane >> 4);
-        const int c = (lane & 15) ^ (kr & 15);
-        const bool ok = live & (kr0 + kr < o.kext) & (16 * c < o.valid);
-        to_lds(r, dst + 1024 * b, ok ? (uint32_t)(kr * pitch + 16 * c) : kOOB);
-    }
+    const int b = wave * 4 + j;
+    const int kr = 4 * b + (lane >> 4);
+    const int c = (lane & 15) ^ (kr & 15);
+    const bool ok = live & (kr0 + kr < o.kext) & (16 * c < o.valid);
+    to_lds(r, dst + 1024 * b, ok ? (uint32_t)(kr * pitch + 16 * c) : kOOB);
 }
 
 // Rowwise E8M0 scales of a K-contiguous operand.  Stage s uses blocks 2s and
@@ -292,6 +296,30 @@ __device__ __forceinline__ i32x8_t frag_ks_f8(const uint8_t *t, int col0, int g,
 __device__ __forceinline__ bf16x8_t frag_kc_bf16(const uint8_t *t, int row, int g, int kk) {
     const u32x4_t v = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * ((2 * kk + g) ^ ((row >> 2) & 3)));
     return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// One stage's fragments of a wave's 128 x 128 quadrant: MXFP8, 4 + 4 operand
+// fragments with their E8M0 scale bytes; bf16, the same for each of the two
+// 16-element halves of the stage.
+struct FragsF8 {
+    i32x8_t fx[4], fy[4];
+    int sx[4], sy[4];
+    int in_k;   // ring scales: this lane's block lies inside the contraction (else the unit scale applies)
+};
+struct FragsBF16 {
+    bf16x8_t fx[2][4], fy[2][4];
+};
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+// f(IC<I>{}) for I = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // ------------------------------------------------------------------ tile mapping
@@ -440,17 +468,20 @@ struct Tile {
 
 // A persistent grid (one workgroup per CU at most): workgroup j of XCD x runs
 // items x * per + j, + nj, ... of that XCD's contiguous range.  Four stage
-// buffers: while one step computes, the next three stages load, and the load
-// side runs ahead across tile boundaries (it walks the same tile sequence,
-// skipping tiles without steps), so a tile's first stages are in LDS when its
-// first step starts.  TAB: the groups' offsets and m-tile prefix are kept in
-// LDS (G <= kTab), else every lookup reads the offsets.
+// buffers: while one stage computes from registers, the next one is read from
+// LDS and the three after it load; the load side runs ahead across tile
+// boundaries (it walks the same tile sequence, skipping tiles without steps),
+// so a tile's first stages are in LDS when its first step starts.  TAB: the
+// groups' offsets and m-tile prefix are kept in LDS (G <= kTab), else every
+// lookup reads the offsets.
 // SC, the row scales' path (MXFP8 NT/NN): 0 bytes per stage through
 // registers, 1 a 4-byte word per row per stage, 2 the scale ring: 16 bytes per
 // row per 8-stage group into one of two LDS slots (used when every group
-// spans at least 3 stages, so that a slot is refilled only after the group
-// before the previous one is done; blocks past the contraction take the unit
-// scale in registers, so bytes read past a row's end are harmless).
+// spans at least 3 stages: a group's slot is refilled when the load side
+// issues the first stage of the group after next, which happens after the
+// barrier that follows the last read of that slot's earlier group; blocks
+// past the contraction take the unit scale in registers, so bytes read past a
+// row's end are harmless).
 template <int MODE, int DT, int OUT, bool TAB, int SC>
 __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm_ub) {
     constexpr bool F8_ = (DT == MXQ_DTYPE_MXFP8_E4M3);
@@ -610,29 +641,35 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     auto src_x = [&](const Tile &T) { return Src{T.x, ldb, T.kext, T.xv}; };
     auto src_y = [&](const Tile &T) { return Src{T.y, lda, T.kext, T.yv}; };
 
-    // stage s of tile T -> stage buffer st (live false: a stage that carries
-    // nothing, with the same instruction count)
-    auto issue = [&](const Tile &T, int s, uint8_t *st, bool live) {
-        if constexpr (XKS) stage_ks(src_x(T), s, st, wave, lane, live);
-        else stage_kc(src_x(T), s, st, wave, lane, live);
-        if constexpr (YKS) stage_ks(src_y(T), s, st + OPB, wave, lane, live);
-        else stage_kc(src_y(T), s, st + OPB, wave, lane, live);
-        if constexpr (F8) {
+    // Load instruction p of stage s of tile T into stage buffer st (live
+    // false: a stage that carries nothing, with the same instruction count):
+    // p = 0..3 the X operand, 4..7 the Y operand, then (MXFP8) the X and Y
+    // per-stage scales where they do not come through the ring.
+    auto issue_piece = [&](auto P, const Tile &T, int s, uint8_t *st, bool live) {
+        constexpr int p = decltype(P)::value;
+        if constexpr (p < 4) {
+            if constexpr (XKS) stage_ks(src_x(T), s, st, wave, lane, live, p);
+            else stage_kc(src_x(T), s, st, wave, lane, live, p);
+        } else if constexpr (p < 8) {
+            if constexpr (YKS) stage_ks(src_y(T), s, st + OPB, wave, lane, live, p - 4);
+            else stage_kc(src_y(T), s, st + OPB, wave, lane, live, p - 4);
+        } else if constexpr (p == 8 && XSB > 0) {
             if constexpr (XKS)
                 stage_colscales(ColScales{T.xs, ldsb, T.nblk, T.xv}, s, st + 2 * OPB, junk, wave, 0, lane, live);
-            else if constexpr (!XRING)
+            else
                 stage_rowscales<SC == 1>(RowScales{T.xs, ldsb, T.nblk, T.xv}, s, tid, st + 2 * OPB, junk, live);
+        } else if constexpr (YSB > 0) {
             if constexpr (YKS)
                 stage_colscales(ColScales{T.ys, ldsa, T.nblk, T.yv}, s, st + 2 * OPB + XSB, junk, wave, 1, lane, live);
-            else if constexpr (!YRING)
+            else
                 stage_rowscales<SC == 1>(RowScales{T.ys, ldsa, T.nblk, T.yv}, s, tid, st + 2 * OPB + XSB, junk, live);
-
         }
     };
     // load instructions per wave per stage (at least: a group's first stage
     // adds its ring loads, which only makes the step waits stricter), and
     // epilogue memory instructions per wave
-    constexpr int kStageOps = 8 + (F8 ? 2 - NRING : 0);
+    constexpr int kStageOps = 8 + (XSB > 0 ? 1 : 0) + (YSB > 0 ? 1 : 0);
+    static_assert(kStageOps == 8 + (F8 ? 2 - NRING : 0), "one load per operand's per-stage scales");
     constexpr int kEpiOps = OUT == MXQ_DTYPE_BF16 ? 32 : 64;
 
     f32x16_t acc[4][4];
@@ -643,66 +680,97 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[x][y][r] = 0.f;
 
-    // one stage: each wave's 128 x 128 quadrant as 4 x 4 MFMA tiles of 32 x 32
-    auto compute = [&](const uint8_t *st, int s) {
-        const uint8_t *tx = st, *ty = st + OPB, *scx = st + 2 * OPB, *scy = st + 2 * OPB + XSB;
+    // ---- one stage's fragments (each wave's 128 x 128 quadrant as 4 x 4 MFMA
+    // tiles of 32 x 32).  MFMA i: MXFP8 x = i / 4, y = i % 4 (16 per stage);
+    // bf16 half kk = i / 16, then the same (32 per stage).  Fragment read j
+    // (8 per stage and half) follows the order the MFMAs first need them:
+    // x0, y0..y3, x1..x3.
+    using Frags = std::conditional_t<F8, FragsF8, FragsBF16>;
+    constexpr int kMfma = F8 ? 16 : 32;
+    constexpr int kReads = F8 ? 8 : 16;
+    struct StageView {
+        const uint8_t *st;   // stage buffer
+        const uint8_t *rg;   // ring slot of the stage's group
+        int sb, rb;          // scale byte of this lane's block: per-stage words, ring
+        bool in_k;           // this lane's block lies inside the contraction
+    };
+    auto view = [&](const uint8_t *st, int s) {
+        StageView v;
+        v.st = st;
+        v.rg = ring + (cgrp_slot & 1) * NRING * RSLOT;
+        v.sb = 2 * (s & 1) + g32;
+        v.rb = 2 * (s % RGS) + g32;
+        v.in_k = 2 * s + g32 < nblk_k;
+        return v;
+    };
+    auto read_frag = [&](Frags &F, auto J, const StageView &v) {
+        constexpr int j = decltype(J)::value;
+        constexpr int jj = j % 8;
+        constexpr bool isx = jj == 0 || jj >= 5;
+        constexpr int idx = jj == 0 ? 0 : (jj < 5 ? jj - 1 : jj - 4);
+        const uint8_t *tx = v.st, *ty = v.st + OPB, *scx = v.st + 2 * OPB, *scy = v.st + 2 * OPB + XSB;
         if constexpr (F8) {
-            const int sb = 2 * (s & 1) + g32;   // row-scale byte of this stage's block g32 (per-stage words)
-            // ring: this stage's blocks are bytes 2 (s % 8) + g32 of the row's
-            // 16; blocks past the contraction take the unit scale
-            const uint8_t *rg = ring + (cgrp_slot & 1) * NRING * RSLOT;
-            const int rb = 2 * (s % RGS) + g32;
-            const bool in_k = 2 * s + g32 < nblk_k;
-            i32x8_t fy[4];
-            int sy[4];
-#pragma unroll
-            for (int y = 0; y < 4; y++) {
-                const int m = wy + 32 * y;
-                if constexpr (YKS) {
-                    fy[y] = frag_ks_f8(ty, m + 16 * ((lane >> 4) & 1), g32, l16);
-                    sy[y] = scy[g32 * 256 + m + l32];
-                } else if constexpr (YRING) {
-                    fy[y] = frag_kc_f8(ty, m + l32, g32);
-                    sy[y] = in_k ? rg[(XRING ? RSLOT : 0) + (m + l32) * 16 + rb] : 127;
-                } else {
-                    fy[y] = frag_kc_f8(ty, m + l32, g32);
-                    sy[y] = scy[(m + l32) * 4 + sb];
-                }
-            }
-#pragma unroll
-            for (int x = 0; x < 4; x++) {
-                const int n = wx + 32 * x;
-                i32x8_t fx;
-                int sx;
+            if constexpr (isx) {
+                const int n = wx + 32 * idx;
                 if constexpr (XKS) {
-                    fx = frag_ks_f8(tx, n + 16 * ((lane >> 4) & 1), g32, l16);
-                    sx = scx[g32 * 256 + n + l32];
+                    F.fx[idx] = frag_ks_f8(tx, n + 16 * ((lane >> 4) & 1), g32, l16);
+                    F.sx[idx] = scx[g32 * 256 + n + l32];
                 } else if constexpr (XRING) {
-                    fx = frag_kc_f8(tx, n + l32, g32);
-                    sx = in_k ? rg[(n + l32) * 16 + rb] : 127;
+                    F.fx[idx] = frag_kc_f8(tx, n + l32, g32);
+                    F.sx[idx] = v.rg[(n + l32) * 16 + v.rb];   // bytes past the row's end: see ring_scales
+                    F.in_k = v.in_k;
                 } else {
-                    fx = frag_kc_f8(tx, n + l32, g32);
-                    sx = scx[(n + l32) * 4 + sb];
+                    F.fx[idx] = frag_kc_f8(tx, n + l32, g32);
+                    F.sx[idx] = scx[(n + l32) * 4 + v.sb];
                 }
-#pragma unroll
-                for (int y = 0; y < 4; y++)
-                    acc[x][y] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fx, fy[y], acc[x][y], 0, 0, 0, sx, 0,
-                                                                                 sy[y]);
+            } else {
+                const int m = wy + 32 * idx;
+                if constexpr (YKS) {
+                    F.fy[idx] = frag_ks_f8(ty, m + 16 * ((lane >> 4) & 1), g32, l16);
+                    F.sy[idx] = scy[g32 * 256 + m + l32];
+                } else if constexpr (YRING) {
+                    F.fy[idx] = frag_kc_f8(ty, m + l32, g32);
+                    F.sy[idx] = v.rg[(XRING ? RSLOT : 0) + (m + l32) * 16 + v.rb];
+                    F.in_k = v.in_k;
+                } else {
+                    F.fy[idx] = frag_kc_f8(ty, m + l32, g32);
+                    F.sy[idx] = scy[(m + l32) * 4 + v.sb];
+                }
             }
         } else {
+            constexpr int kk = j / 8;
+            if constexpr (isx) F.fx[kk][idx] = frag_kc_bf16(tx, wx + 32 * idx + l32, g32, kk);
+            else F.fy[kk][idx] = frag_kc_bf16(ty, wy + 32 * idx + l32, g32, kk);
+        }
+    };
+    // Ring scale bytes of blocks past the contraction are whatever follows
+    // the row; such blocks have zero codes and take the unit scale, applied
+    // here once the set's reads are complete (a select next to each read
+    // would wait for it).
+    auto ring_scales = [&](Frags &F) {
+        if constexpr (F8 && (XRING || YRING)) {
 #pragma unroll
-            for (int kk = 0; kk < 2; kk++) {
-                bf16x8_t fy[4];
-#pragma unroll
-                for (int y = 0; y < 4; y++) fy[y] = frag_kc_bf16(ty, wy + 32 * y + l32, g32, kk);
-#pragma unroll
-                for (int x = 0; x < 4; x++) {
-                    const bf16x8_t fx = frag_kc_bf16(tx, wx + 32 * x + l32, g32, kk);
-#pragma unroll
-                    for (int y = 0; y < 4; y++)
-                        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx, fy[y], acc[x][y], 0, 0, 0);
-                }
+            for (int x = 0; x < 4; x++) {
+                if constexpr (XRING) F.sx[x] = F.in_k ? F.sx[x] : 127;
+                if constexpr (YRING) F.sy[x] = F.in_k ? F.sy[x] : 127;
             }
+        }
+    };
+    // MFMA i of a stage.  The empty asm statement after it takes its result,
+    // so that the MFMA stays in its slot: a computation without side effects
+    // could otherwise be sunk past the step's waits and barrier, off the
+    // loads and reads it is meant to overlap.
+    auto mfma = [&](const Frags &F, auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (F8) {
+            constexpr int x = i / 4, y = i % 4;
+            acc[x][y] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.fx[x], F.fy[y], acc[x][y], 0, 0, 0, F.sx[x],
+                                                                         0, F.sy[y]);
+            asm volatile("" ::"a"(acc[x][y]));
+        } else {
+            constexpr int kk = i / 16, x = (i % 16) / 4, y = i % 4;
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.fx[kk][x], F.fy[kk][y], acc[x][y], 0, 0, 0);
+            asm volatile("" ::"a"(acc[x][y]));
         }
     };
 
@@ -790,14 +858,12 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     int ls = 0;
     unsigned issued = 0, consumed = 0;
     // epilogues run so far, and for each stage buffer that count when its
-    // stage was issued (8 bits each): a step's wait leaves in flight every
-    // memory instruction issued after its stage
+    // stage was issued (8 bits each): a stage's wait leaves in flight every
+    // memory instruction issued after it
     unsigned epis = 0, epi_at = 0;
     bool pending = false;   // an issued stage the load side has not moved past yet
     // The scale ring: before the load side issues a group's first stage, the
-    // group's 16 scale bytes per row go into slot lgrp & 1 (this runs ahead of
-    // the stage itself, outside the step's MFMA block; the step waits only
-    // grow stricter for it).
+    // group's 16 scale bytes per row go into slot lgrp & 1.
     auto ring_issue = [&]() {
         if constexpr (NRING > 0) {
             if (ld.valid && ls % RGS == 0) {
@@ -816,9 +882,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             }
         }
     };
-    auto issue_next = [&]() {
-        const int slot = issued & (NBUF - 1);
-        issue(ld, ls, smem + slot * STAGE, ld.valid != 0);
+    auto issued_one = [&](unsigned slot) {
         epi_at = (epi_at & ~(0xFFu << (8 * slot))) | ((epis & 0xFFu) << (8 * slot));
         issued++;
         pending = true;
@@ -830,63 +894,108 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         }
         pending = false;
     };
-#pragma unroll
-    for (int j = 0; j < NBUF - 1; j++) {
-        ring_issue();
-        issue_next();
-        advance_load();
-    }
+    // Wait until stage c has landed.  Vector memory operations of a wave
+    // complete in issue order on this target, loads and stores alike (the
+    // compiler's wait counts rely on the same), so it has once no more than
+    // the later ones are in flight: the next two stages, plus an epilogue's
+    // memory operations if one ran since stage c was issued (vmcnt saturates
+    // at 63; more than that follows then).
+    auto wait_stage = [&](unsigned c) {
+        const unsigned slot = c & (NBUF - 1);
+        const unsigned since = (epis - (epi_at >> (8 * slot))) & 0xFFu;
+        if (opaque(__builtin_amdgcn_readfirstlane((int)since)) == 0) {
+            constexpr int n = 2 * kStageOps;
+            __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+        } else if (opaque(__builtin_amdgcn_readfirstlane((int)since)) == 1) {
+            constexpr int n = 2 * kStageOps + kEpiOps < 63 ? 2 * kStageOps + kEpiOps : 63;
+            __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0xCF7F);   // vmcnt(63)
+        }
+    };
 
-    // ---- the compute side: every tile, in the same order
+    // ---- the pipeline.  Stage c is computed from registers while stage
+    // c + 1 sits in LDS and stages c + 2 .. c + 4 load: in the shadow of
+    // stage c's MFMAs a wave waits for stage c + 1, passes the step's barrier
+    // (after which every wave has its stage-c fragments, so that buffer is
+    // free), reads stage c + 1's fragments into the other register set and
+    // issues stage c + 4 into stage c's buffer.  The load side walks the same
+    // tile sequence (skipping tiles without steps), so at a tile's last step
+    // the stage read is the next tile's first, and the epilogue stages the
+    // output through that stage's buffer (its fragments are in registers; the
+    // next step's barrier orders the buffer's reuse).
+    static_for<0, NBUF>([&](auto) {
+        ring_issue();
+        const unsigned slot = issued & (NBUF - 1);
+        static_for<0, kStageOps>([&](auto P) { issue_piece(P, ld, ls, smem + slot * STAGE, ld.valid != 0); });
+        issued_one(slot);
+        advance_load();
+    });
     {
         const Tile c0 = next_tile(lo, false);
         if (!c0.valid) return;   // (the loads issued above carried nothing)
         tcur[wave] = c0;
     }
+    Frags FA, FB;
+    {
+        constexpr int n = 3 * kStageOps;   // stage 0 has landed: stages 1..3 may be in flight
+        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+        step_barrier<63>();
+        if constexpr (NRING > 0) cgrp_slot = cgrp++;
+        const StageView v = view(smem, 0);
+        static_for<0, kReads>([&](auto J) { read_frag(FA, J, v); });
+    }
+    // step s of a K-step tile: MFMAs from P, the next stage's fragments into Q
+    auto step = [&](Frags &P, Frags &Q, int s, int K) {
+        advance_load();
+        ring_scales(P);
+        mfma(P, IC<0>{});
+        mfma(P, IC<1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned cn = consumed + 1;
+        wait_stage(cn);
+        step_barrier<63>();   // stage cn has landed everywhere; stage `consumed` is read everywhere
+        ring_issue();
+        const int sn = s + 1 < K ? s + 1 : 0;   // stage cn's step within its tile
+        if constexpr (NRING > 0) {
+            if (sn % RGS == 0) cgrp_slot = cgrp++;
+        }
+        const StageView v = view(smem + (cn & (NBUF - 1)) * STAGE, sn);
+        const unsigned slot = issued & (NBUF - 1);   // == consumed & (NBUF - 1)
+        uint8_t *dst = smem + slot * STAGE;
+        const bool live = ld.valid != 0;
+        // One MFMA per slot; a wave issues in order, so the reads and loads
+        // placed after an MFMA go out while the matrix core runs it.  The
+        // fragment reads take the first slots (they must land by the next
+        // step), the stage's loads the last ones.
+        constexpr int kFirstLoad = kMfma - kStageOps;
+        static_assert(kFirstLoad >= 2, "a load slot per stage load");
+        static_for<2, kMfma>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            mfma(P, I);
+            if constexpr (i - 2 < kReads) read_frag(Q, IC<i - 2>{}, v);
+            if constexpr (i >= kFirstLoad) issue_piece(IC<i - kFirstLoad>{}, ld, ls, dst, live);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        issued_one(slot);
+        consumed++;
+    };
     for (;;) {
         refresh_lane();
         const int K = tcur[wave].ksteps;
-        for (int s = 0; s < K; s++) {
-            // the load side moves on here, before this step's MFMAs, so that
-            // its branches do not split them from the issue below
-            advance_load();
-            ring_issue();
-            // Vector memory operations of a wave complete in issue order on
-            // this target, loads and stores alike (the compiler's wait counts
-            // rely on the same), so this stage has landed once no more than
-            // the later ones are in flight: the next two stages, plus an
-            // epilogue's memory operations if one ran since this stage was
-            // issued (vmcnt saturates at 63; more than that follows then).
-            const unsigned slot = consumed & (NBUF - 1);
-            const unsigned since = (epis - (epi_at >> (8 * slot))) & 0xFFu;
-            if (opaque(__builtin_amdgcn_readfirstlane((int)since)) == 0) {
-                constexpr int n = 2 * kStageOps;
-                __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
-            } else if (opaque(__builtin_amdgcn_readfirstlane((int)since)) == 1) {
-                constexpr int n = 2 * kStageOps + kEpiOps < 63 ? 2 * kStageOps + kEpiOps : 63;
-                __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
-            } else {
-                __builtin_amdgcn_s_waitcnt(0xCF7F);   // vmcnt(63)
-            }
-            step_barrier<63>();   // everyone's stage has landed, and the previous step's reads are done
-            if constexpr (NRING > 0) {
-                if (s % RGS == 0) cgrp_slot = cgrp++;
-            }
-            compute(smem + slot * STAGE, s);
-            // the next stage's loads (into the buffer the previous step read,
-            // free since the barrier), set up in the shadow of the MFMAs:
-            // a wave issues in order, so scalar and vector work placed
-            // between MFMAs runs while the matrix core works
-            issue_next();
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x006, 14, 0);   // then up to 14 VALU / SALU
-            }
-            consumed++;
+        // two steps per iteration, so that the register sets alternate
+        // without copies (an odd last step copies once)
+        int s = 0;
+        for (; s + 1 < K; s += 2) {
+            step(FA, FB, s, K);
+            step(FB, FA, s + 1, K);
         }
-        // the stage buffer the last step read (no load is headed for it)
-        epilogue(tcur[wave], smem + ((consumed + NBUF - 1) & (NBUF - 1)) * STAGE);
+        if (s < K) {
+            step(FA, FB, s, K);
+            FA = FB;
+        }
+        // the buffer of the stage just read (no load is headed for it)
+        epilogue(tcur[wave], smem + (consumed & (NBUF - 1)) * STAGE);
         epis++;
         const Tile nc = next_tile(tcur[wave].item + nj, false);
         if (!nc.valid) break;
