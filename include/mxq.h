@@ -263,12 +263,22 @@ typedef struct {
                                CUs to work overlapping on another stream */
 } mxq_gemm_args;
 
-/* Workspace bytes for mxq_grouped_gemm with these arguments (pointers unused). */
+/* Workspace bytes for mxq_grouped_gemm with these arguments (pointers unused):
+ * 256 for MXQ_GEMM_TN, 0 otherwise. */
 mxq_status mxq_grouped_gemm_workspace(const mxq_gemm_args *args, size_t *bytes);
 
 /* Run the grouped GEMM.  Group sizes are read on the device only; the grid is
  * sized from M (NT/NN) or from G and the output size (TN), never from a
- * host copy of the offsets. */
+ * host copy of the offsets.
+ *   ws  device workspace of at least mxq_grouped_gemm_workspace bytes, 4-byte
+ *       aligned (NULL allowed when that is 0), owned by the caller; its
+ *       contents need no initialisation and are overwritten.  MXQ_GEMM_TN
+ *       keeps a counter there: with skewed group sizes the tiles are handed
+ *       out largest group first to whichever workgroup finishes first, which
+ *       balances the work (the result does not depend on the order).  Two
+ *       calls in flight at once must not share a workspace.
+ * Errors: MXQ_ERR_WORKSPACE if ws is NULL or smaller than needed,
+ * MXQ_ERR_ALIGN if it is not 4-byte aligned. */
 mxq_status mxq_grouped_gemm(const mxq_gemm_args *args, void *ws, size_t ws_bytes,
                             void *stream);
 

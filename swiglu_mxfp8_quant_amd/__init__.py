@@ -147,6 +147,15 @@ def _stream(stream):
     return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
 
 
+def _hold(t, stream):
+    """Keep a temporary device buffer (a workspace) from being handed out again
+    before the work queued on `stream` has used it (torch frees it on return;
+    its caching allocator only orders reuse on the current stream).  With a raw
+    stream handle the caller must keep the current stream ordered with it."""
+    if t is not None and stream is not None and not isinstance(stream, int):
+        t.record_stream(stream)
+
+
 def make_act(kind=ACT_SWIGLU, limit=7.0):
     return mxq_act(kind, limit)
 
@@ -291,6 +300,7 @@ def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False,
     ds = torch.empty(M, dtype=torch.float32, device=gate.device) if want_dscale else None
     nws = mxq_swiglu_quantize_bwd_workspace(M, K, dirs)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=gate.device) if (want_dscale and nws) else None
+    _hold(ws, stream)
     act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit)
     check(mxq_swiglu_quantize_bwd(act, grad, gate, up, scale, make_groups(row_off, block_off),
                                   dd[:, :K] if dense else None, dd[:, K:] if dense else None, ds,
@@ -344,5 +354,10 @@ def grouped_gemm(mode, row_off, A, B, out, A_scales=None, B_scales=None, block_o
                              R, N, K, R, _operand(A, A_scales), _operand(B, B_scales, group_dim=True),
                              DTYPE_F32 if out.dtype == _torch().float32 else DTYPE_BF16, out.data_ptr(),
                              out.stride(0), 0, int(accumulate), int(max_workgroups))
-    check(mxq_grouped_gemm(args, None, stream))
+    ws = None
+    need = mxq_grouped_gemm_workspace(args)
+    if need:
+        ws = _torch().empty(need, dtype=_torch().uint8, device=out.device)
+        _hold(ws, stream)
+    check(mxq_grouped_gemm(args, ws, stream))
     return out

@@ -20,8 +20,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "offsets.hip", "act_quant.hip", "grouped_gemm.hip"]
+# (the atomic optimizer would turn the grouped GEMM's one-lane tile counter
+# into a wave-wide pattern that waits for the counter's result at once)
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I", INCLUDE, "-I", CSRC]
 
 

@@ -377,20 +377,29 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, con
     return hip_status(mxq::launch_act_quant_bwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_bwd launch");
 }
 
+// K-grouped launches keep one counter of their dynamic tile order in the
+// workspace (256 bytes keep the allocation's alignment simple).
+static size_t gemm_ws_bytes(const mxq_gemm_args &a) { return a.mode == MXQ_GEMM_TN ? 256 : 0; }
+
 mxq_status mxq_grouped_gemm_workspace(const mxq_gemm_args *args, size_t *bytes) {
     if (args == nullptr || bytes == nullptr) return fail(MXQ_ERR_NULL, "args and bytes are required");
-    *bytes = 0;
+    *bytes = gemm_ws_bytes(*args);
     return ok();
 }
 
 mxq_status mxq_grouped_gemm(const mxq_gemm_args *args, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (args == nullptr) return fail(MXQ_ERR_NULL, "args is NULL");
     mxq::GemmArgs g{};
     std::string err;
     const int st = mxq::gemm_prepare(*args, g, err);
     if (st != MXQ_OK) return fail((mxq_status)st, "%s", err.c_str());
+    const size_t need = gemm_ws_bytes(*args);
+    if (need > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return fail(MXQ_ERR_WORKSPACE, "the workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+        if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return fail(MXQ_ERR_ALIGN, "the workspace must be 4-byte aligned");
+        g.sched = static_cast<int *>(ws);
+    }
     if (g.noop) return ok();
     return hip_status(mxq::launch_grouped_gemm(g, (hipStream_t)stream), "mxq_grouped_gemm launch");
 }

@@ -30,6 +30,7 @@ struct GemmArgs {
     int64_t ld_out, out_gstride;
     int accumulate;
     int max_workgroups;
+    int *sched;             // K-grouped: device counter of the dynamic tile order (workspace)
     bool noop;
 };
 

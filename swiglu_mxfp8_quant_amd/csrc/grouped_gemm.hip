@@ -365,6 +365,20 @@ __device__ __forceinline__ int group_mtiles(const GemmArgs &a, int64_t g, int ca
 // Groups up to this count keep their offsets and m-tile prefix in LDS.
 constexpr int kTab = 1024;
 
+// K-grouped launches with up to kDynG groups can take their tiles in a
+// dynamic largest-first order (see the kernel); an epilogue counts as this
+// many contraction steps when the schedules are compared.
+constexpr int kDynG = 256;
+constexpr int kEpiCost = 2;
+constexpr int kQueue = 16;   // entries of a workgroup's queue of taken tiles
+constexpr int kTake0 = 7;    // tiles a workgroup is dealt before it takes any
+
+// Sets the dynamic tile counter of a K-grouped launch to zero (a kernel, not
+// a memset, so that the pair can be captured in a graph).
+__global__ void sched_reset(int *counter) {
+    if (threadIdx.x == 0) counter[0] = 0;
+}
+
 // LDS group tables, so that the tile loop reads no global memory:
 //   rs[g]  (g <= G) = row_off[g] clipped to [0, M] (TN: [0, rows]), so group
 //          g's rows are [rs[g], max(rs[g + 1], rs[g]));
@@ -497,6 +511,11 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     __shared__ int tab[TAB ? kTab + 1 : 1];
     __shared__ int rs[TAB ? kTab + 1 : 1];
     __shared__ int wsum[4];
+    constexpr bool DYN = MODE == MODE_TN && TAB;   // the dynamic order is available
+    __shared__ int gsteps[DYN ? kDynG : 1];   // contraction steps per group
+    __shared__ int gord[DYN ? kDynG : 1];     // groups by steps, largest first
+    __shared__ int dq[DYN ? kQueue : 1];      // taken tiles, in order
+    __shared__ int64_t red[8];
     // the arguments that only the per-tile lookup reads live in LDS, so that
     // they do not hold scalar registers through the loop
     __shared__ GemmArgs sa;
@@ -541,18 +560,104 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     const int nj = gridDim.x / kXCD;
     const int per = (nitems + kXCD - 1) / kXCD;
     const int xcd = blockIdx.x % kXCD;
-    const int lo = xcd * per + blockIdx.x / kXCD;
-    const int hi = (xcd + 1) * per < nitems ? (xcd + 1) * per : nitems;
+    int lo = xcd * per + blockIdx.x / kXCD;
+    int hi = (xcd + 1) * per < nitems ? (xcd + 1) * per : nitems;
+    int istep = nj;   // from one item of this workgroup to its next
+
+    // ---- K-grouped: static or dynamic tile order.  The static order gives
+    // each XCD a contiguous range of tiles (a group's tiles share an L2), which
+    // balances when the groups are alike.  When the heaviest workgroup of that
+    // order would carry more than 9/8 of the mean (skewed routing: a few large
+    // groups), the tiles of non-empty groups are taken instead from one
+    // counter in the workspace, largest group first, each workgroup taking its
+    // next tile as it finishes one (list scheduling, largest first); the tiles
+    // of empty groups follow in a static split.  A workgroup keeps a queue of
+    // taken tiles, so the load side, which runs a few stages ahead, always
+    // finds its next tile there: kTake0 are taken at the start and one more at
+    // each epilogue, whose counter result is written to the queue one
+    // epilogue later (so that waiting for it waits for nothing else).  Every
+    // workgroup reaches the same decision from the same tables.
+    int dyn = 0, gne = 0, tpg = ntm * ntn;
+    if constexpr (DYN) {
+        if (a.sched != nullptr && a.G <= kDynG && (int)gridDim.x <= NTHR) {
+            const int G = (int)a.G;
+            for (int g = tid; g < G; g += NTHR) {
+                const int rows = rs[g + 1] - rs[g];
+                gsteps[g] = rows > 0 ? (rows + BK - 1) / BK : 0;
+            }
+            __syncthreads();
+            // thread w: the load of workgroup w in the static order; and the total
+            int64_t load = 0, tot = 0;
+            if (tid < (int)gridDim.x) {
+                const int x = tid % kXCD, lo_w = x * per + tid / kXCD;
+                const int hi_w = (x + 1) * per < nitems ? (x + 1) * per : nitems;
+                for (int it = lo_w; it < hi_w; it += nj) load += gsteps[it / tpg] + kEpiCost;
+            }
+            for (int g = tid; g < G; g += NTHR) tot += (int64_t)(gsteps[g] + kEpiCost) * tpg;
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                const int64_t ol = __shfl_xor(load, d, 64), ot = __shfl_xor(tot, d, 64);
+                load = ol > load ? ol : load;
+                tot += ot;
+            }
+            if (lane == 0) {
+                red[wave] = load;
+                red[4 + wave] = tot;
+            }
+            __syncthreads();
+            int64_t mx = red[0], sum = red[4];
+            for (int w = 1; w < 4; w++) {
+                mx = red[w] > mx ? red[w] : mx;
+                sum += red[4 + w];
+            }
+            dyn = 8 * mx > 9 * ((sum + gridDim.x - 1) / gridDim.x);
+            if (dyn) {
+                // rank of each group: more steps first, then the lower index
+                for (int g = tid; g < G; g += NTHR) {
+                    const int sg = gsteps[g];
+                    int r = 0;
+                    for (int h = 0; h < G; h++) {
+                        const int sh = gsteps[h];
+                        r += (sh > sg) | ((sh == sg) & (h < g));
+                    }
+                    gord[r] = g;
+                }
+                for (int g = 0; g < G; g++) gne += gsteps[g] > 0;
+                // the first kTake0 rounds are dealt, one tile per workgroup per
+                // round in alternating direction; the counter hands out the rest
+                if (tid < kTake0) {
+                    const int nw = (int)gridDim.x, w = (int)blockIdx.x;
+                    dq[tid] = tid * nw + ((tid & 1) ? nw - 1 - w : w);
+                }
+                __syncthreads();
+                lo = 0;
+                hi = gne * tpg;   // positions past the taken tiles' range are never read
+                istep = 1;
+            }
+        }
+    }
+    dyn = __builtin_amdgcn_readfirstlane(dyn);
 
     // tile of work item `item` (false: an m tile past its group's rows)
-    auto describe = [&](int item, Tile &T) -> bool {
+    auto describe = [&](int item, Tile &T, bool sorted = false) -> bool {
         const uint8_t *A = static_cast<const uint8_t *>(sa.A.data);
         const uint8_t *B = static_cast<const uint8_t *>(sa.B.data);
         int64_t m0, n0, r0, r1, g;
         if constexpr (MODE == MODE_TN) {
             const int per_g = ntm * ntn;
-            g = item / per_g;
-            const int rem = item - (int)g * per_g;
+            int rem;
+            if (DYN && dyn) {
+                // queue position (or, from describe_sorted, the tile itself) ->
+                // tile in the largest-first order -> group and tile
+                const int t = sorted ? item : dq[item % kQueue];
+                if (!sorted && t >= hi) return false;
+                const int sg = t / per_g;
+                g = gord[sg];
+                rem = t - sg * per_g;
+            } else {
+                g = item / per_g;
+                rem = item - (int)g * per_g;
+            }
             m0 = (int64_t)(rem / ntn) * BT;
             n0 = (int64_t)(rem % ntn) * BT;
             int64_t blk0;
@@ -626,10 +731,17 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         return true;
     };
     // the first tile at or after `from` (every one, or only those with steps)
+    auto describe_sorted = [&](int t, Tile &T) { describe(t, T, true); };
+    // (dynamic order: `from` is a queue position, and every taken tile of a
+    // non-empty group has steps)
     auto next_tile = [&](int from, bool with_steps) {
         Tile T{};
-        for (int item = from; item < hi; item += nj)
-            if (describe(item, T) && (!with_steps || T.ksteps > 0)) return T;
+        if (DYN && dyn) {
+            if (describe(from, T)) return T;
+        } else {
+            for (int item = from; item < hi; item += nj)
+                if (describe(item, T) && (!with_steps || T.ksteps > 0)) return T;
+        }
         T.valid = 0;
         T.ksteps = 0;
         return T;
@@ -889,7 +1001,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     };
     auto advance_load = [&]() {
         if (pending && ld.valid && ++ls == ld.ksteps) {
-            ld = next_tile(ld.item + nj, true);
+            ld = next_tile(ld.item + istep, true);
             ls = 0;
         }
         pending = false;
@@ -931,11 +1043,9 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         issued_one(slot);
         advance_load();
     });
-    {
-        const Tile c0 = next_tile(lo, false);
-        if (!c0.valid) return;   // (the loads issued above carried nothing)
-        tcur[wave] = c0;
-    }
+    const Tile c0 = next_tile(lo, false);
+    if (!c0.valid && !dyn) return;   // (the loads issued above carried nothing)
+    tcur[wave] = c0;
     Frags FA, FB;
     {
         constexpr int n = 3 * kStageOps;   // stage 0 has landed: stages 1..3 may be in flight
@@ -980,7 +1090,14 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         issued_one(slot);
         consumed++;
     };
-    for (;;) {
+    // Dynamic order: the counter value taken at an epilogue reaches the queue
+    // at the start of the next one: the only memory operations the compiler
+    // sees after it are that epilogue's stores, so its wait there leaves the
+    // stage loads in flight alone.  (Only thread 0 takes and reads `taken`.)
+    int taken = 0;
+    bool have = false;
+    int qfill = kTake0;   // queue entries written
+    for (bool more = c0.valid != 0; more;) {
         refresh_lane();
         const int K = tcur[wave].ksteps;
         // two steps per iteration, so that the register sets alternate
@@ -994,11 +1111,20 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             step(FA, FB, s, K);
             FA = FB;
         }
+        if (DYN && dyn) {
+            if (have) {
+                if (tid == 0) dq[qfill % kQueue] = kTake0 * (int)gridDim.x + taken;
+                qfill++;
+            }
+            if (tid == 0) taken = __hip_atomic_fetch_add(a.sched, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            have = true;
+        }
         // the buffer of the stage just read (no load is headed for it)
         epilogue(tcur[wave], smem + (consumed & (NBUF - 1)) * STAGE);
         epis++;
-        const Tile nc = next_tile(tcur[wave].item + nj, false);
-        if (!nc.valid) break;
+        const Tile nc = next_tile(tcur[wave].item + istep, false);
+        more = nc.valid != 0;
+        if (!more) break;
         tcur[wave] = nc;
 #pragma unroll
         for (int x = 0; x < 4; x++)
@@ -1006,6 +1132,24 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             for (int y = 0; y < 4; y++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) acc[x][y][r] = 0.f;
+    }
+    // Dynamic order: the tiles of empty groups (zeros, or the output left as
+    // it is when accumulating), split statically.
+    if constexpr (DYN) {
+        if (dyn) {
+#pragma unroll
+            for (int x = 0; x < 4; x++)
+#pragma unroll
+                for (int y = 0; y < 4; y++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) acc[x][y][r] = 0.f;
+            const int ne = ((int)a.G - gne) * tpg;
+            for (int e = (int)blockIdx.x; e < ne; e += (int)gridDim.x) {
+                Tile T{};
+                describe_sorted(gne * tpg + e, T);
+                epilogue(T, smem + (consumed & (NBUF - 1)) * STAGE);
+            }
+        }
     }
 }
 
@@ -1052,6 +1196,7 @@ hipError_t launch_mode(const GemmArgs &g, hipStream_t stream) {
     const dim3 gd((unsigned)grid), bd(NTHR);
     const int a1 = (int)ntn, a2 = (int)ntm;
     const bool tab = g.G <= kTab;
+    if (MODE == MODE_TN && g.sched != nullptr) hipLaunchKernelGGL(sched_reset, dim3(1), dim3(64), 0, stream, g.sched);
     if constexpr (DT != MXQ_DTYPE_MXFP8_E4M3 || MODE == MODE_TN) {
         if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 1>), gd, bd, 0, stream, g, a1, a2);
         else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 1>), gd, bd, 0, stream, g, a1, a2);

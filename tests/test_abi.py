@@ -142,3 +142,34 @@ def test_quantize_validation(m):
     assert lib.mxq_quantize(64, 64, fake(0), 60, None, 1, ctypes.byref(row), None, None) == 2
     assert lib.mxq_quantize(64, 33, fake(0), 64, None, 1, ctypes.byref(row), None, None) == 2
     assert lib.mxq_quantize(64, 64, fake(0), 64, None, 3, ctypes.byref(row), None, None) == 1
+
+
+def gemm_args(m, mode, M=256, N=256, K=256, G=4, max_wg=0):
+    """MXFP8 grouped-GEMM arguments over fake, disjoint, aligned device ranges."""
+    f8 = m.DTYPE_MXFP8
+    if mode == m.GEMM_TN:
+        A = m.mxq_operand(f8, BASE + (1 << 28), M, 0, BASE + (2 << 28), M, 0)
+        B = m.mxq_operand(f8, BASE + (3 << 28), N, 0, BASE + (4 << 28), N, 0)
+        return m.mxq_gemm_args(mode, G, BASE, BASE + 4096, M, N, 0, 1024, A, B, m.DTYPE_BF16,
+                               BASE + (5 << 28), N, M * N, 0, max_wg)
+    A = m.mxq_operand(f8, BASE + (1 << 28), K, 0, BASE + (2 << 28), K // 32, 0)
+    B = m.mxq_operand(f8, BASE + (3 << 28), K, N * K, BASE + (4 << 28), K // 32, N * (K // 32))
+    return m.mxq_gemm_args(mode, G, BASE, None, M, N, K, M, A, B, m.DTYPE_BF16, BASE + (5 << 28), N, 0, 0,
+                           max_wg)
+
+
+def test_gemm_workspace_and_validation(m):
+    """The K-grouped GEMM keeps its dynamic tile counter in the caller's
+    workspace: the query asks for it, and a call without it (or misaligned)
+    is refused before anything is launched; the other modes need none.  A
+    negative workgroup cap is a shape error."""
+    lib = m.lib
+    tn, nt = gemm_args(m, m.GEMM_TN), gemm_args(m, m.GEMM_NT)
+    assert m.mxq_grouped_gemm_workspace(tn) == 256
+    assert m.mxq_grouped_gemm_workspace(nt) == 0
+    assert lib.mxq_grouped_gemm(ctypes.byref(tn), None, 0, None) == 8            # MXQ_ERR_WORKSPACE
+    assert lib.mxq_grouped_gemm(ctypes.byref(tn), fake(6 << 28), 255, None) == 8
+    assert lib.mxq_grouped_gemm(ctypes.byref(tn), fake((6 << 28) + 2), 256, None) == 3   # MXQ_ERR_ALIGN
+    assert lib.mxq_grouped_gemm(ctypes.byref(gemm_args(m, m.GEMM_TN, max_wg=-1)), fake(6 << 28), 256, None) == 2
+    assert lib.mxq_grouped_gemm(ctypes.byref(gemm_args(m, m.GEMM_NT, max_wg=-8)), None, 0, None) == 2
+    assert lib.mxq_grouped_gemm(ctypes.byref(gemm_args(m, m.GEMM_NT, K=48)), None, 0, None) == 2

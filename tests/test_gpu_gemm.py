@@ -155,6 +155,60 @@ def test_tn_mxfp8(mxq, accumulate):
         assert np.all(got[1] == 0) and np.all(got[5] == 0)      # empty groups write zeros
 
 
+# One large group among small and empty ones: the K-grouped launch takes its
+# tiles largest group first from the workspace counter (7 dealt per workgroup,
+# the rest taken as workgroups finish), then the empty groups' tiles.
+SKEW_SPLITS = [1300, 0, 3, 0, 40, 7, 0, 90, 1, 1, 2, 300, 0, 5, 64, 0, 33, 2, 0, 150]
+
+
+_SKEW_CACHE = {}
+
+
+def skew_case(accumulate):
+    """Inputs and the oracle's result of the skewed K-grouped case (computed
+    once per output kind: the oracle is the slow part)."""
+    if accumulate not in _SKEW_CACHE:
+        rng = np.random.default_rng(23)
+        splits = SKEW_SPLITS
+        ro_np = O.splits_to_offsets(splits)[0]
+        R, M, N, G = sum(splits), 768, 512, len(splits)
+        A, As = qcols(rng, (R, M), ro_np)
+        B, Bs = qcols(rng, (R, N), ro_np, 0.01)
+        opA = O.Operand("mxfp8", A, 0, 1, M, As, 0, 1, M)
+        opB = O.Operand("mxfp8", B, 0, 1, N, Bs, 0, 1, N)
+        base = (rng.standard_normal((G, M, N)) * 0.5).astype(np.float32)
+        ref = O.grouped_gemm("k", ro_np, M, N, 0, opA, opB, "f32" if accumulate else "bf16",
+                             out=base.copy() if accumulate else None, accumulate=accumulate)
+        _SKEW_CACHE[accumulate] = (A, As, B, Bs, base, ref)
+    return _SKEW_CACHE[accumulate]
+
+
+@pytest.mark.parametrize("max_wg", [8, 0])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_tn_skewed_dynamic_order(mxq, accumulate, max_wg):
+    splits = SKEW_SPLITS
+    ro, bo, ro_np, bo_np = offsets(mxq, splits)
+    M, N, G = 768, 512, len(splits)
+    A, As, B, Bs, base, ref = skew_case(accumulate)
+    if accumulate:
+        out = torch.from_numpy(base.copy()).cuda()
+    else:
+        out = torch.full((G, M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    for rep in range(2):   # the second call reuses a fresh workspace: no state carries over
+        if accumulate and rep:
+            out.copy_(torch.from_numpy(base))
+        mxq.grouped_gemm(mxq.GEMM_TN, ro, to_dev(A), to_dev(B), out, to_dev(As), to_dev(Bs), block_off=bo,
+                         accumulate=accumulate, max_workgroups=max_wg)
+        torch.cuda.synchronize()
+        got = out_np(out)
+        check_close(got, ref_np(ref, "f32" if accumulate else "bf16"))
+        empty = [g for g, n in enumerate(splits) if n == 0]
+        if accumulate:
+            assert np.array_equal(got[empty], base[empty])   # empty groups leave C as it was
+        else:
+            assert np.all(got[empty] == 0)                   # empty groups write zeros
+
+
 def deq(c, s):
     import refmath as R
     return R.E4M3[c] * np.exp2(s.astype(np.float64) - 127)
