@@ -892,6 +892,12 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     const bool accumulate = a.accumulate != 0;
     auto epilogue = [&](const Tile &T, uint8_t *stg) {
         const __amdgpu_buffer_rsrc_t ro = rsrc(T.o, 0x7FFFFFF0);
+        // The tile's extents and the pitch in registers, read once: the stores
+        // below may alias the tile descriptor's LDS copy as far as the compiler
+        // knows (it would read it again after each), and an opaque value used
+        // under a condition would be computed in a branch of its own.
+        const int yv = __builtin_amdgcn_readfirstlane(T.yv), xv = __builtin_amdgcn_readfirstlane(T.xv);
+        const int ldo_r = opaque(ldo);
         if constexpr (OUT == MXQ_DTYPE_BF16) {
             // Through LDS, so that each output row leaves as 512 contiguous
             // bytes (16-byte nontemporal stores, 32 lanes per row): the stage
@@ -927,14 +933,23 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 step_barrier<63>();   // quarter h is in LDS
+                // all eight reads first: the compiler keeps LDS reads behind
+                // earlier buffer stores, so interleaving them would wait for
+                // each read in turn
+                u32x4_t v[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const int qd = j * NTHR + tid;
+                    const int m = qd >> 5, c = qd & 31;
+                    v[j] = *reinterpret_cast<const u32x4_t *>(stg + m * 512 + 16 * (c ^ (m & 31)));
+                }
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
                     const int qd = j * NTHR + tid;
                     const int m = qd >> 5, c = qd & 31;
                     const int row = 64 * h + m;
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + m * 512 + 16 * (c ^ (m & 31)));
-                    const uint32_t off = ((row < T.yv) & (8 * c < T.xv)) ? (uint32_t)(row * opaque(ldo) + 16 * c) : kOOB;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 2);   // nt
+                    const uint32_t off = ((row < yv) & (8 * c < xv)) ? (uint32_t)(row * ldo_r + 16 * c) : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(v[j], ro, off, 0, 2);   // nt
                 }
             }
         } else {
@@ -947,13 +962,13 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
 #pragma unroll
                 for (int x = 0; x < 4; x++) asm volatile("" : "+a"(acc[x][y]));
                 const int ml = wy + 32 * y + l32;
-                const uint32_t row = ml < T.yv ? (uint32_t)(ml * opaque(ldo) + (wx + 4 * g32) * OSZ) : kOOB;
+                const uint32_t row = ml < yv ? (uint32_t)(ml * ldo_r + (wx + 4 * g32) * OSZ) : kOOB;
 #pragma unroll
                 for (int x = 0; x < 4; x++)
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
                         // columns past N (last n tile only) go out of range too
-                        const uint32_t off = wx + 32 * x + 8 * q + 4 * g32 < T.xv ? row + (32 * x + 8 * q) * OSZ : kOOB;
+                        const uint32_t off = wx + 32 * x + 8 * q + 4 * g32 < xv ? row + (32 * x + 8 * q) * OSZ : kOOB;
                         f32x4_t w = f32x4_t{acc[x][y][4 * q], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2],
                                             acc[x][y][4 * q + 3]};
                         if (accumulate)
