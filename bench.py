@@ -263,9 +263,13 @@ def summarize_gemm_profile(base):
 
     tcc = counters(f"{base}/tcc/moe_counter_collection.csv", {"TCC_HIT_sum", "TCC_MISS_sum"})
     fet = counters(f"{base}/fetch/moe_counter_collection.csv", {"FETCH_SIZE"})
+    # optional: rocprofv3's derived MfmaUtil (matrix-core busy cycles over all SIMDs' cycles)
+    mpath = f"{base}/mfma/moe_counter_collection.csv"
+    mfu = counters(mpath, {"MfmaUtil"}) if os.path.exists(mpath) else None
     print("| GEMM | mode | dispatches | median us | TFLOP/s | % of dense peak | algorithmic bytes | flop/B |"
-          " roofline-attainable TFLOP/s | % of attainable | L2 hit rate | HBM read MB |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+          " roofline-attainable TFLOP/s | % of attainable | L2 hit rate | HBM read MB |"
+          + (" MFMA busy % |" if mfu else ""))
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|" + ("---|" if mfu else ""))
     for g in GP_ORDER:
         us = statistics.median(dur[g])
         tf = GP_FL[g] / us / 1e6
@@ -274,8 +278,9 @@ def summarize_gemm_profile(base):
         att = min(peak, ai * 8.0)   # flop/B x 8 TB/s, in TFLOP/s
         hits = statistics.median(v["TCC_HIT_sum"] / max(1.0, v["TCC_HIT_sum"] + v["TCC_MISS_sum"]) for v in tcc[g])
         mb = statistics.median(v["FETCH_SIZE"] for v in fet[g]) * 1024 * GP_FETCH_SCALE / 1e6
+        busy = f" {statistics.median(v['MfmaUtil'] for v in mfu[g]):.1f} |" if mfu else ""
         print(f"| {g} | {GP_MODE[g]} | {len(dur[g])} | {us:.1f} | {tf:.0f} | {100 * tf / peak:.1f} | {GP_BY[g] / 1e6:.0f} MB |"
-              f" {ai:.0f} | {att:.0f} | {100 * tf / att:.1f} | {100 * hits:.1f} % | {mb:.0f} |")
+              f" {ai:.0f} | {att:.0f} | {100 * tf / att:.1f} | {100 * hits:.1f} % | {mb:.0f} |" + busy)
 
 
 
