@@ -186,6 +186,55 @@ def moe_section(m, torch, W, reps=5):
     return out
 
 
+def supplementary_gemm(m, torch, reps=5):
+    """A compute-bound grouped shape, outside the workload's configurations
+    (labelled as such): 8 equal groups of 4096 rows, N = K = 8192, NT, in
+    MXFP8 (random finite E4M3 codes, unit-range E8M0 scales) and in bf16.
+    It shows the matrix-core rate the kernel reaches when the contraction is
+    long and the output small against the flops."""
+    G, rows, N, K = 8, 4096, 8192, 8192
+    dev = "cuda"
+    sp = torch.full((G,), rows, dtype=torch.int64, device=dev)
+    ro, _bo, _ = m.splits_to_offsets(sp)
+    R = G * rows
+    out = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    res = {"shape": f"{G} groups x {rows} rows, N = K = {N}, NT", "configuration": "supplementary, not a workload config"}
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for dt in ("fp8", "bf16"):
+        if dt == "fp8":
+            A = torch.randint(0, 0x70, (R, K), dtype=torch.uint8, device=dev, generator=g)
+            B = torch.randint(0, 0x70, (G, N, K), dtype=torch.uint8, device=dev, generator=g)
+            As = torch.full((R, K // 32), 120, dtype=torch.uint8, device=dev)
+            Bs = torch.full((G, N, K // 32), 120, dtype=torch.uint8, device=dev)
+            fn = lambda: m.grouped_gemm(m.GEMM_NT, ro, A, B, out, As, Bs)
+        else:
+            A = torch.randn((R, K), device=dev, generator=g).to(torch.bfloat16)
+            B = torch.randn((G, N, K), device=dev, generator=g).to(torch.bfloat16)
+            fn = lambda: m.grouped_gemm(m.GEMM_NT, ro, A, B, out)
+        fn()
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = sorted(ts)[len(ts) // 2]
+        tf = 2.0 * R * N * K / us / 1e6
+        peak = FP8_PEAK_TFLOPS if dt == "fp8" else BF16_PEAK_TFLOPS
+        res[dt] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "frac_peak": round(tf / peak, 4)}
+        del A, B
+        if dt == "fp8":
+            del As, Bs
+    del out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(rows=256):
     """The CPU oracle (single-threaded C, fp64) over a bounded sample: the
     first `rows` rows of every cell of the step (same byte model)."""
@@ -405,6 +454,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_moe:
         out["gemm"] = moe_section(m, torch, W)
+        out["gemm_supplementary"] = supplementary_gemm(m, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
     print(json.dumps(out), flush=True)
