@@ -900,36 +900,35 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         const int ldo_r = opaque(ldo);
         if constexpr (OUT == MXQ_DTYPE_BF16) {
             // Through LDS, so that each output row leaves as 512 contiguous
-            // bytes (16-byte nontemporal stores, 32 lanes per row): the stage
-            // buffer the last step read from holds a quarter of the tile, 64
-            // rows x 512 B with 16-byte chunk c of row m at c ^ (m & 31).
-            // The two waves holding rows [64h, 64h + 64) write quarter h (their
-            // fragment rows y = 2 (h & 1) + {0, 1}), then all four store it.
+            // bytes (16-byte nontemporal stores, 32 lanes per row): the buffer
+            // of the stage just read holds a quarter of the tile, 64 rows x
+            // 512 B with 16-byte chunk c of row m at c ^ (m & 31).  Quarter h
+            // is fragment row y = h of every wave: rows 32h .. 32h + 31 (from
+            // the two waves with wy = 0, staged as rows 0..31) and 128 + 32h ..
+            // (from the other two, staged as rows 32..63), so all four waves
+            // write each quarter, then all four store it.
             typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int h = 0; h < 4; h++) {
                 step_barrier<63>();   // everyone is done reading stg (last step's fragments, or quarter h - 1)
-                if ((wave & 1) == (h >> 1)) {
+                {
+                    const int y = h;
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int yy = 0; yy < 2; yy++) {
-                        const int y = 2 * (h & 1) + yy;
-                        __builtin_amdgcn_sched_barrier(0);
+                    for (int x = 0; x < 4; x++) asm volatile("" : "+a"(acc[x][y]));
+                    const int m = (wy >> 2) + l32;   // staging row
 #pragma unroll
-                        for (int x = 0; x < 4; x++) asm volatile("" : "+a"(acc[x][y]));
-                        const int m = 32 * yy + l32;
+                    for (int x = 0; x < 4; x++)
 #pragma unroll
-                        for (int x = 0; x < 4; x++)
-#pragma unroll
-                            for (int q = 0; q < 4; q++) {
-                                const int chunk = (wx + 32 * x + 8 * q) >> 3;
-                                bf16x4_t b;
-                                b.x = (__bf16)acc[x][y][4 * q];
-                                b.y = (__bf16)acc[x][y][4 * q + 1];
-                                b.z = (__bf16)acc[x][y][4 * q + 2];
-                                b.w = (__bf16)acc[x][y][4 * q + 3];
-                                *reinterpret_cast<bf16x4_t *>(stg + m * 512 + 16 * (chunk ^ (m & 31)) + 8 * g32) = b;
-                            }
-                    }
+                        for (int q = 0; q < 4; q++) {
+                            const int chunk = (wx + 32 * x + 8 * q) >> 3;
+                            bf16x4_t b;
+                            b.x = (__bf16)acc[x][y][4 * q];
+                            b.y = (__bf16)acc[x][y][4 * q + 1];
+                            b.z = (__bf16)acc[x][y][4 * q + 2];
+                            b.w = (__bf16)acc[x][y][4 * q + 3];
+                            *reinterpret_cast<bf16x4_t *>(stg + m * 512 + 16 * (chunk ^ (m & 31)) + 8 * g32) = b;
+                        }
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 step_barrier<63>();   // quarter h is in LDS
@@ -947,7 +946,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
                 for (int j = 0; j < 8; j++) {
                     const int qd = j * NTHR + tid;
                     const int m = qd >> 5, c = qd & 31;
-                    const int row = 64 * h + m;
+                    const int row = (m < 32 ? 0 : 128 - 32) + 32 * h + m;   // tile row of staging row m
                     const uint32_t off = ((row < yv) & (8 * c < xv)) ? (uint32_t)(row * ldo_r + 16 * c) : kOOB;
                     __builtin_amdgcn_raw_buffer_store_b128(v[j], ro, off, 0, 2);   // nt
                 }
