@@ -31,11 +31,16 @@ def weight_offsets(G, rows, device):
     return splits_to_offsets(torch.full((G,), rows, dtype=torch.int64, device=device))[:2]
 
 
-def quantize_weight_rowwise(w):
-    """(G, N, K) bf16 -> codes (G, N, K), scales (G, N, K/32)."""
-    G, N, K = w.shape
-    rc, _, rs, _ = quantize(w.reshape(G * N, K), rowwise=True)
-    return rc.view(G, N, K), rs.view(G, N, K // 32)
+def quantize_weight_both(w, offs):
+    """(G, K, N) bf16 -> rowwise codes (G, K, N) and scales (G, K, N/32) (1x32
+    blocks along N, for a contraction over N), and colwise codes (G, K, N) and
+    scales (G, K/32, N) (32x1 blocks along each expert's K rows, for a
+    contraction over K), from one read of the weight."""
+    G, K, N = w.shape
+    ro, bo = offs
+    rc, cc, rs, cs = quantize(w.reshape(G * K, N), rowwise=True, colwise=True, row_off=ro, block_off=bo,
+                              n_col_blocks=G * K // 32)
+    return rc.view(G, K, N), rs.view(G, K, N // 32), cc.view(G, K, N), cs.view(G, K // 32, N)
 
 
 def quantize_weight_colwise(w, offs):
@@ -68,11 +73,13 @@ class Layer:
         a_r, a_c, as_r, as_c = swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, rowwise=True, colwise=True,
                                                    row_off=ro, block_off=bo, clamped=self.clamped,
                                                    limit=self.limit)
-        w2q, w2s = quantize_weight_rowwise(self.w2)
+        # W2 in both directions from one read: rowwise along I for FC2, and
+        # colwise along H (per expert) for FC2's dgrad in the backward
+        w2q, w2s, w2c, w2cs = quantize_weight_both(self.w2, weight_offsets(self.G, H, dev))
         y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         grouped_gemm(GEMM_NT, ro, a_r, w2q, y, as_r, w2s)
         self.saved = dict(x_perm=x_perm, scale=scale, h13=h13, a_r=a_r, a_c=a_c, as_r=as_r, as_c=as_c,
-                          w2q=w2q, w2s=w2s)
+                          w2q=w2q, w2s=w2s, w2c=w2c, w2cs=w2cs)
         return y
 
     def backward(self, dy):
@@ -81,7 +88,7 @@ class Layer:
         dev = dy.device
         ro, bo = self.row_off, self.block_off
         dy_r, dy_c, dys_r, dys_c = quantize(dy, rowwise=True, colwise=True, row_off=ro, block_off=bo)
-        w2c, w2cs = quantize_weight_colwise(self.w2, weight_offsets(G, H, dev))
+        w2c, w2cs = s["w2c"], s["w2cs"]
         da = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
         grouped_gemm(GEMM_NN, ro, dy_r, w2c, da, dys_r, w2cs)
         dw2 = torch.empty((G, H, I), dtype=torch.bfloat16, device=dev)
