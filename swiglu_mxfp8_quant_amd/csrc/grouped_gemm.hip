@@ -51,7 +51,9 @@
 //     share of the tiles.  Each XCD takes a contiguous range of tiles (one
 //     expert's tiles share that XCD's L2).  The load side walks the same tile
 //     sequence as the compute side, a few stages ahead, so consecutive tiles
-//     overlap.
+//     overlap.  K-grouped launches whose static ranges would be unbalanced
+//     (skewed group sizes) take their tiles largest group first from a
+//     counter in the caller's workspace instead.
 #include "gemm_internal.h"
 
 #include <string>
