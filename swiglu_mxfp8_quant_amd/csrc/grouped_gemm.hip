@@ -129,30 +129,51 @@ __device__ __forceinline__ int opaque(int v) {
 // compiler would otherwise wait for every such load in flight before any LDS
 // access it cannot tell apart from their destinations (which would serialize
 // the stage pipeline), while the kernel orders them itself with its explicit
-// vmcnt waits and barriers.  They have no register results; M0, which they
-// read at issue, is saved and restored around them.
+// vmcnt waits and barriers.  They have no register results.  They read M0
+// (the LDS address), an input the compiler writes before each, and the
+// resource from SGPRs.  The compiler cannot see that these statements hold a
+// vector-memory instruction, so it does not keep its distance from them
+// either: a vector instruction that writes an SGPR (a readfirstlane, an SGPR
+// spill reload) needs five wait states before a vector-memory instruction
+// reads that SGPR, and each statement pads itself to five.
 __device__ __forceinline__ i32x4_t rsrc4(const uint8_t *base, int64_t bytes) {
     const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int)bytes);
     const uint64_t b = (uint64_t)uni64(reinterpret_cast<int64_t>(base));
     return i32x4_t{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)__builtin_amdgcn_readfirstlane(n), 0x00020000};
 }
 
+// A resource from `base` on whose range checks nothing relies: every load
+// through it either carries an offset its own bounds checks have admitted or
+// kOOB.
+__device__ __forceinline__ i32x4_t rsrc_open(const uint8_t *base) {
+    const uint64_t b = (uint64_t)uni64(reinterpret_cast<int64_t>(base));
+    return i32x4_t{(int)(uint32_t)b, (int)(uint32_t)(b >> 32), 0x7FFFFFF0, 0x00020000};
+}
+
+// LDS byte address of a generic pointer into LDS: the shared aperture is
+// 4 GB aligned, so it is the pointer's low word.
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)p);
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
 __device__ __forceinline__ void to_lds(const i32x4_t &r, uint8_t *dst, uint32_t off) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_addr(dst)), "v"(off), "s"(r) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(dst))
+                 : "memory");
 }
 
 __device__ __forceinline__ void to_lds4(const i32x4_t &r, uint8_t *dst, uint32_t off) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(lds_addr(dst)), "v"(off), "s"(r) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(dst))
+                 : "memory");
+}
+
+// 16 bytes per lane to LDS address `dst`, from offset `off` in the lanes of
+// `mask` and from kOOB in the others.
+__device__ __forceinline__ void to_lds_sel(const i32x4_t &r, uint32_t dst, uint32_t off, uint64_t mask, uint32_t oob) {
+    uint32_t t;
+    asm volatile("v_cndmask_b32_e64 %0, %1, %2, %3\n\ts_nop 3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+                 : "=&v"(t)
+                 : "v"(oob), "v"(off), "s"(mask), "s"(r), "{m0}"(dst)
+                 : "memory");
 }
 
 // One operand's view for staging.  K-contiguous: tile rows are output rows,
@@ -169,31 +190,58 @@ struct Src {
 // (4 + 4 data, 2 scale for MXFP8), whether or not it carries data: loads
 // with `live` false or outside the operand go out of range (no memory
 // access; zeros land in LDS).  The step waits count on that.
+//
+// The data loads of a wave, load j of 4 per operand, fill the 1 KB blocks
+// 4w + j of the operand's stage tile.  Their per-lane offsets from the tile
+// origin do not depend on the stage; they are worked out once per tile (kOOB
+// for rows or columns outside the tile, and for every lane of a tile that
+// carries nothing), and each stage adds its contraction offset to the
+// resource's base and masks out what lies past the contraction.
+struct Feed {
+    uint32_t v[4];
+};
 
 // K-contiguous stage s -> LDS [256 rows][64 B], chunk c of row r at c ^ ((r >> 2) & 3).
-// Wave w fills 1 KB blocks 4w..4w+3 (16 rows each); this is its load j of 4.
-__device__ __forceinline__ void stage_kc(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live, int j) {
+// Lane l of load j covers row 16 (4w + j) + l / 4, whose swizzle is (l >> 4) & 3.
+__device__ __forceinline__ int kc_chunk(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
+
+__device__ __forceinline__ Feed feed_kc(const Src &o, bool live, int wave, int lane) {
+    Feed f;
+    const int c = kc_chunk(lane);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int row = 16 * (4 * wave + j) + (lane >> 2);
+        f.v[j] = (live & (row < o.valid)) ? (uint32_t)(row * o.pitch + 16 * c) : kOOB;
+    }
+    return f;
+}
+
+template <int J>
+__device__ __forceinline__ void stage_kc(const Src &o, const Feed &f, int s, uint32_t dst, int lane, uint32_t oob) {
     const int k0 = s * BK;
-    const i32x4_t r = rsrc4(o.base + k0, (int64_t)o.valid * o.pitch - k0);
-    const int pitch = opaque(o.pitch);
-    const int b = wave * 4 + j;
-    const int row = 16 * b + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
-    const bool ok = live & (row < o.valid) & (k0 + 16 * c < o.kext);
-    to_lds(r, dst + 1024 * b, ok ? (uint32_t)(row * pitch + 16 * c) : kOOB);
+    const uint64_t in_k = __builtin_amdgcn_ballot_w64(16 * kc_chunk(lane) < o.kext - k0);
+    to_lds_sel(rsrc_open(o.base + k0), dst + 1024 * J, f.v[J], in_k, oob);
 }
 
 // K-strided stage s -> LDS [64 contraction rows][256 B], chunk c of row k at c ^ (k & 15).
-// Wave w fills 1 KB blocks 4w..4w+3 (4 contraction rows each); this is its load j of 4.
-__device__ __forceinline__ void stage_ks(const Src &o, int s, uint8_t *dst, int wave, int lane, bool live, int j) {
+// Lane l of load j covers contraction row 4 (4w + j) + l / 16.
+__device__ __forceinline__ Feed feed_ks(const Src &o, bool live, int wave, int lane) {
+    Feed f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int kr = 4 * (4 * wave + j) + (lane >> 4);
+        const int c = (lane & 15) ^ (kr & 15);
+        f.v[j] = (live & (16 * c < o.valid)) ? (uint32_t)(kr * o.pitch + 16 * c) : kOOB;
+    }
+    return f;
+}
+
+template <int J>
+__device__ __forceinline__ void stage_ks(const Src &o, const Feed &f, int s, uint32_t dst, int wave, int lane,
+                                         uint32_t oob) {
     const int kr0 = s * BK;
-    const i32x4_t r = rsrc4(o.base + (int64_t)kr0 * o.pitch, (int64_t)(o.kext - kr0) * o.pitch);
-    const int pitch = opaque(o.pitch);
-    const int b = wave * 4 + j;
-    const int kr = 4 * b + (lane >> 4);
-    const int c = (lane & 15) ^ (kr & 15);
-    const bool ok = live & (kr0 + kr < o.kext) & (16 * c < o.valid);
-    to_lds(r, dst + 1024 * b, ok ? (uint32_t)(kr * pitch + 16 * c) : kOOB);
+    const uint64_t in_k = __builtin_amdgcn_ballot_w64((lane >> 4) < o.kext - kr0 - 4 * (4 * wave + J));
+    to_lds_sel(rsrc_open(o.base + (int64_t)kr0 * o.pitch), dst + 1024 * J, f.v[J], in_k, oob);
 }
 
 // Rowwise E8M0 scales of a K-contiguous operand.  Stage s uses blocks 2s and
@@ -754,19 +802,24 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     const int nblk_k = (int)((a.K + 31) / 32);
     auto src_x = [&](const Tile &T) { return Src{T.x, ldb, T.kext, T.xv}; };
     auto src_y = [&](const Tile &T) { return Src{T.y, lda, T.kext, T.yv}; };
+    // the load side's per-lane data-load offsets (of its current tile)
+    const uint32_t lds_smem = lds_addr(smem);
+    Feed fdx, fdy;
 
     // Load instruction p of stage s of tile T into stage buffer st (live
     // false: a stage that carries nothing, with the same instruction count):
     // p = 0..3 the X operand, 4..7 the Y operand, then (MXFP8) the X and Y
     // per-stage scales where they do not come through the ring.
-    auto issue_piece = [&](auto P, const Tile &T, int s, uint8_t *st, bool live) {
+    auto issue_piece = [&](auto P, const Tile &T, int s, unsigned slot, bool live) {
         constexpr int p = decltype(P)::value;
+        uint8_t *st = smem + slot * STAGE;
+        const uint32_t dst = lds_smem + slot * STAGE + 4096 * wave;   // this wave's blocks
         if constexpr (p < 4) {
-            if constexpr (XKS) stage_ks(src_x(T), s, st, wave, lane, live, p);
-            else stage_kc(src_x(T), s, st, wave, lane, live, p);
+            if constexpr (XKS) stage_ks<p>(src_x(T), fdx, s, dst, wave, lane, kOOB);
+            else stage_kc<p>(src_x(T), fdx, s, dst, lane, kOOB);
         } else if constexpr (p < 8) {
-            if constexpr (YKS) stage_ks(src_y(T), s, st + OPB, wave, lane, live, p - 4);
-            else stage_kc(src_y(T), s, st + OPB, wave, lane, live, p - 4);
+            if constexpr (YKS) stage_ks<p - 4>(src_y(T), fdy, s, dst + OPB, wave, lane, kOOB);
+            else stage_kc<p - 4>(src_y(T), fdy, s, dst + OPB, lane, kOOB);
         } else if constexpr (p == 8 && XSB > 0) {
             if constexpr (XKS)
                 stage_colscales(ColScales{T.xs, ldsb, T.nblk, T.xv}, s, st + 2 * OPB, junk, wave, 0, lane, live);
@@ -984,6 +1037,14 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     // ---- the load side: tile `ld` (with steps), its next stage `ls`
     Tile ld = next_tile(lo, true);
     int ls = 0;
+    auto make_feeds = [&]() {
+        const bool live = ld.valid != 0;
+        if constexpr (XKS) fdx = feed_ks(src_x(ld), live, wave, lane);
+        else fdx = feed_kc(src_x(ld), live, wave, lane);
+        if constexpr (YKS) fdy = feed_ks(src_y(ld), live, wave, lane);
+        else fdy = feed_kc(src_y(ld), live, wave, lane);
+    };
+    make_feeds();
     unsigned issued = 0, consumed = 0;
     // epilogues run so far, and for each stage buffer that count when its
     // stage was issued (8 bits each): a stage's wait leaves in flight every
@@ -1019,6 +1080,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         if (pending && ld.valid && ++ls == ld.ksteps) {
             ld = next_tile(ld.item + istep, true);
             ls = 0;
+            make_feeds();
         }
         pending = false;
     };
@@ -1055,7 +1117,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     static_for<0, NBUF>([&](auto) {
         ring_issue();
         const unsigned slot = issued & (NBUF - 1);
-        static_for<0, kStageOps>([&](auto P) { issue_piece(P, ld, ls, smem + slot * STAGE, ld.valid != 0); });
+        static_for<0, kStageOps>([&](auto P) { issue_piece(P, ld, ls, slot, ld.valid != 0); });
         issued_one(slot);
         advance_load();
     });
@@ -1088,7 +1150,6 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         }
         const StageView v = view(smem + (cn & (NBUF - 1)) * STAGE, sn);
         const unsigned slot = issued & (NBUF - 1);   // == consumed & (NBUF - 1)
-        uint8_t *dst = smem + slot * STAGE;
         const bool live = ld.valid != 0;
         // One MFMA per slot; a wave issues in order, so the reads and loads
         // placed after an MFMA go out while the matrix core runs it.  The
@@ -1100,7 +1161,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             constexpr int i = decltype(I)::value;
             mfma(P, I);
             if constexpr (i - 2 < kReads) read_frag(Q, IC<i - 2>{}, v);
-            if constexpr (i >= kFirstLoad) issue_piece(IC<i - kFirstLoad>{}, ld, ls, dst, live);
+            if constexpr (i >= kFirstLoad) issue_piece(IC<i - kFirstLoad>{}, ld, ls, slot, live);
             __builtin_amdgcn_sched_barrier(0);
         });
         issued_one(slot);
