@@ -315,14 +315,6 @@ __device__ __forceinline__ void stage_colscales(const ColScales &sc, int s, uint
 // elements [8g, 8g + 8) of the 16.  The 32x32 fp32 result: lane 32g + j holds
 // C[8q + 4g + r][j] in its register 4q + r.
 
-// fp8, K-contiguous tile: lane (g, i) gets row `row`'s chunks g and 2 + g.
-__device__ __forceinline__ i32x8_t frag_kc_f8(const uint8_t *t, int row, int g) {
-    const int sw = (row >> 2) & 3;
-    const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * (g ^ sw));
-    const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * ((2 + g) ^ sw));
-    return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
 // fp8, K-strided tile: the same 32 bytes for column col0 + m (col0 a multiple
 // of 16) via transposed reads: lane m of the 16-lane group points at
 // contraction row k0 + m/2, bytes col0 + 8 (m % 2) .. + 8, and receives 8
@@ -339,13 +331,6 @@ __device__ __forceinline__ i32x8_t frag_ks_f8(const uint8_t *t, int col0, int g,
     const i32x2_t c = tr8(t, 32 + 16 * g, col0, m);
     const i32x2_t d = tr8(t, 40 + 16 * g, col0, m);
     return i32x8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-
-// bf16, K-contiguous: lane (g, i) carries row i's elements 8g..8g+7 of the
-// 16-element half kk of the 32-element stage (chunk 2 kk + g).
-__device__ __forceinline__ bf16x8_t frag_kc_bf16(const uint8_t *t, int row, int g, int kk) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(t + row * BK + 16 * ((2 * kk + g) ^ ((row >> 2) & 3)));
-    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // One stage's fragments of a wave's 128 x 128 quadrant: MXFP8, 4 + 4 operand
@@ -855,59 +840,74 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     using Frags = std::conditional_t<F8, FragsF8, FragsBF16>;
     constexpr int kMfma = F8 ? 16 : 32;
     constexpr int kReads = F8 ? 8 : 16;
+    // K-contiguous fragments: lane (g32, l32) of fragment i takes chunks g32
+    // and 2 + g32 of row w + 32 i + l32 (w the wave's quadrant origin): fp8,
+    // the two halves of its 32 bytes; bf16, its 8 elements of half 0 and of
+    // half 1.  That row's swizzle is (l32 >> 2) & 3 for every i, so the four
+    // fragments of an operand sit at fixed distances (i x 32 rows) from two
+    // per-lane addresses, and their scale bytes likewise from one: the reads
+    // take those distances as immediate offsets.
     struct StageView {
-        const uint8_t *st;   // stage buffer
-        const uint8_t *rg;   // ring slot of the stage's group
-        int sb, rb;          // scale byte of this lane's block: per-stage words, ring
-        bool in_k;           // this lane's block lies inside the contraction
+        const uint8_t *st;       // stage buffer
+        const uint8_t *xl, *xh;  // K-contiguous X: the lane's chunks g32 and 2 + g32 of fragment row wx + l32
+        const uint8_t *yl, *yh;  // the same for Y (row wy + l32)
+        const uint8_t *xs, *ys;  // scale byte of fragment 0 (ring or per-stage words; K-strided: column-major)
+        bool in_k;               // this lane's block lies inside the contraction
     };
     auto view = [&](const uint8_t *st, int s) {
         StageView v;
         v.st = st;
-        v.rg = ring + (cgrp_slot & 1) * NRING * RSLOT;
-        v.sb = 2 * (s & 1) + g32;
-        v.rb = 2 * (s % RGS) + g32;
+        const int sw = (l32 >> 2) & 3;
+        const int lo = 16 * (g32 ^ sw), hi = 16 * ((2 + g32) ^ sw);
+        v.xl = st + (wx + l32) * BK + lo;
+        v.xh = st + (wx + l32) * BK + hi;
+        v.yl = st + OPB + (wy + l32) * BK + lo;
+        v.yh = st + OPB + (wy + l32) * BK + hi;
+        const uint8_t *rg = ring + (cgrp_slot & 1) * NRING * RSLOT;
+        const int sb = 2 * (s & 1) + g32, rb = 2 * (s % RGS) + g32;
+        const uint8_t *scx = st + 2 * OPB, *scy = st + 2 * OPB + XSB;
+        if constexpr (XKS) v.xs = scx + g32 * 256 + wx + l32;
+        else if constexpr (XRING) v.xs = rg + (wx + l32) * 16 + rb;
+        else v.xs = scx + (wx + l32) * 4 + sb;
+        if constexpr (YKS) v.ys = scy + g32 * 256 + wy + l32;
+        else if constexpr (YRING) v.ys = rg + (XRING ? RSLOT : 0) + (wy + l32) * 16 + rb;
+        else v.ys = scy + (wy + l32) * 4 + sb;
         v.in_k = 2 * s + g32 < nblk_k;
         return v;
     };
+    auto kc_f8 = [](const uint8_t *l, const uint8_t *h, int i) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(l + 32 * BK * i);
+        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(h + 32 * BK * i);
+        return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    };
+    auto kc_bf16 = [](const uint8_t *p, int i) {
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t *>(p + 32 * BK * i));
+    };
+    // scale byte of fragment i (32 rows or columns on)
+    constexpr int XSTEP = XKS ? 32 : (XRING ? 32 * 16 : 32 * 4);
+    constexpr int YSTEP = YKS ? 32 : (YRING ? 32 * 16 : 32 * 4);
     auto read_frag = [&](Frags &F, auto J, const StageView &v) {
         constexpr int j = decltype(J)::value;
         constexpr int jj = j % 8;
         constexpr bool isx = jj == 0 || jj >= 5;
         constexpr int idx = jj == 0 ? 0 : (jj < 5 ? jj - 1 : jj - 4);
-        const uint8_t *tx = v.st, *ty = v.st + OPB, *scx = v.st + 2 * OPB, *scy = v.st + 2 * OPB + XSB;
+        const uint8_t *tx = v.st, *ty = v.st + OPB;
         if constexpr (F8) {
             if constexpr (isx) {
-                const int n = wx + 32 * idx;
-                if constexpr (XKS) {
-                    F.fx[idx] = frag_ks_f8(tx, n + 16 * ((lane >> 4) & 1), g32, l16);
-                    F.sx[idx] = scx[g32 * 256 + n + l32];
-                } else if constexpr (XRING) {
-                    F.fx[idx] = frag_kc_f8(tx, n + l32, g32);
-                    F.sx[idx] = v.rg[(n + l32) * 16 + v.rb];   // bytes past the row's end: see ring_scales
-                    F.in_k = v.in_k;
-                } else {
-                    F.fx[idx] = frag_kc_f8(tx, n + l32, g32);
-                    F.sx[idx] = scx[(n + l32) * 4 + v.sb];
-                }
+                if constexpr (XKS) F.fx[idx] = frag_ks_f8(tx, wx + 32 * idx + 16 * ((lane >> 4) & 1), g32, l16);
+                else F.fx[idx] = kc_f8(v.xl, v.xh, idx);
+                F.sx[idx] = v.xs[XSTEP * idx];   // ring bytes past the row's end: see ring_scales
+                if constexpr (XRING) F.in_k = v.in_k;
             } else {
-                const int m = wy + 32 * idx;
-                if constexpr (YKS) {
-                    F.fy[idx] = frag_ks_f8(ty, m + 16 * ((lane >> 4) & 1), g32, l16);
-                    F.sy[idx] = scy[g32 * 256 + m + l32];
-                } else if constexpr (YRING) {
-                    F.fy[idx] = frag_kc_f8(ty, m + l32, g32);
-                    F.sy[idx] = v.rg[(XRING ? RSLOT : 0) + (m + l32) * 16 + v.rb];
-                    F.in_k = v.in_k;
-                } else {
-                    F.fy[idx] = frag_kc_f8(ty, m + l32, g32);
-                    F.sy[idx] = scy[(m + l32) * 4 + v.sb];
-                }
+                if constexpr (YKS) F.fy[idx] = frag_ks_f8(ty, wy + 32 * idx + 16 * ((lane >> 4) & 1), g32, l16);
+                else F.fy[idx] = kc_f8(v.yl, v.yh, idx);
+                F.sy[idx] = v.ys[YSTEP * idx];
+                if constexpr (YRING) F.in_k = v.in_k;
             }
         } else {
             constexpr int kk = j / 8;
-            if constexpr (isx) F.fx[kk][idx] = frag_kc_bf16(tx, wx + 32 * idx + l32, g32, kk);
-            else F.fy[kk][idx] = frag_kc_bf16(ty, wy + 32 * idx + l32, g32, kk);
+            if constexpr (isx) F.fx[kk][idx] = kc_bf16(kk ? v.xh : v.xl, idx);
+            else F.fy[kk][idx] = kc_bf16(kk ? v.yh : v.yl, idx);
         }
     };
     // Ring scale bytes of blocks past the contraction are whatever follows
