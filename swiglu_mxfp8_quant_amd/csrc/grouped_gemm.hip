@@ -216,11 +216,13 @@ __device__ __forceinline__ Feed feed_kc(const Src &o, bool live, int wave, int l
     return f;
 }
 
+// `sb`: the operand's origin advanced to stage s (o.base + s * BK)
 template <int J>
-__device__ __forceinline__ void stage_kc(const Src &o, const Feed &f, int s, uint32_t dst, int lane, uint32_t oob) {
+__device__ __forceinline__ void stage_kc(const Src &o, const uint8_t *sb, const Feed &f, int s, uint32_t dst, int lane,
+                                         uint32_t oob) {
     const int k0 = s * BK;
     const uint64_t in_k = __builtin_amdgcn_ballot_w64(16 * kc_chunk(lane) < o.kext - k0);
-    to_lds_sel(rsrc_open(o.base + k0), dst + 1024 * J, f.v[J], in_k, oob);
+    to_lds_sel(rsrc_open(sb), dst + 1024 * J, f.v[J], in_k, oob);
 }
 
 // K-strided stage s -> LDS [64 contraction rows][256 B], chunk c of row k at c ^ (k & 15).
@@ -236,12 +238,13 @@ __device__ __forceinline__ Feed feed_ks(const Src &o, bool live, int wave, int l
     return f;
 }
 
+// `sb`: the operand's origin advanced to stage s (o.base + s * BK * o.pitch)
 template <int J>
-__device__ __forceinline__ void stage_ks(const Src &o, const Feed &f, int s, uint32_t dst, int wave, int lane,
-                                         uint32_t oob) {
+__device__ __forceinline__ void stage_ks(const Src &o, const uint8_t *sb, const Feed &f, int s, uint32_t dst, int wave,
+                                         int lane, uint32_t oob) {
     const int kr0 = s * BK;
     const uint64_t in_k = __builtin_amdgcn_ballot_w64((lane >> 4) < o.kext - kr0 - 4 * (4 * wave + J));
-    to_lds_sel(rsrc_open(o.base + (int64_t)kr0 * o.pitch), dst + 1024 * J, f.v[J], in_k, oob);
+    to_lds_sel(rsrc_open(sb), dst + 1024 * J, f.v[J], in_k, oob);
 }
 
 // Rowwise E8M0 scales of a K-contiguous operand.  Stage s uses blocks 2s and
@@ -295,10 +298,11 @@ struct ColScales {
     int valid;             // valid column bytes
 };
 
-__device__ __forceinline__ void stage_colscales(const ColScales &sc, int s, uint8_t *dst, uint8_t *junk, int wave,
-                                                int owner, int lane, bool live) {
+// `sb`: sc.base advanced to stage s (block row 2s)
+__device__ __forceinline__ void stage_colscales(const ColScales &sc, const uint8_t *sb, int s, uint8_t *dst, uint8_t *junk,
+                                                int wave, int owner, int lane, bool live) {
     const int b0 = 2 * s;
-    const i32x4_t r = rsrc4(sc.base + (int64_t)b0 * sc.ld, (int64_t)(sc.nblk - b0) * sc.ld);
+    const i32x4_t r = rsrc_open(sb);
     const int b = lane >> 4, c = lane & 15;
     const bool mine = wave == owner;
     const bool ok = live & mine & (lane < 32) & (b0 + b < sc.nblk) & (16 * c < sc.valid);
@@ -790,6 +794,11 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     // the load side's per-lane data-load offsets (of its current tile)
     const uint32_t lds_smem = lds_addr(smem);
     Feed fdx, fdy;
+    // the load tile's operand and column-scale origins advanced to stage `ls`,
+    // carried from stage to stage (per-stage strides are per launch)
+    const uint8_t *sbx = nullptr, *sby = nullptr, *sbxs = nullptr, *sbys = nullptr;
+    const int64_t dsx = XKS ? (int64_t)BK * ldb : BK, dsy = YKS ? (int64_t)BK * lda : BK;
+    const int64_t dsxs = 2 * (int64_t)ldsb, dsys = 2 * (int64_t)ldsa;
 
     // Load instruction p of stage s of tile T into stage buffer st (live
     // false: a stage that carries nothing, with the same instruction count):
@@ -800,19 +809,20 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         uint8_t *st = smem + slot * STAGE;
         const uint32_t dst = lds_smem + slot * STAGE + 4096 * wave;   // this wave's blocks
         if constexpr (p < 4) {
-            if constexpr (XKS) stage_ks<p>(src_x(T), fdx, s, dst, wave, lane, kOOB);
-            else stage_kc<p>(src_x(T), fdx, s, dst, lane, kOOB);
+            if constexpr (XKS) stage_ks<p>(src_x(T), sbx, fdx, s, dst, wave, lane, kOOB);
+            else stage_kc<p>(src_x(T), sbx, fdx, s, dst, lane, kOOB);
         } else if constexpr (p < 8) {
-            if constexpr (YKS) stage_ks<p - 4>(src_y(T), fdy, s, dst + OPB, wave, lane, kOOB);
-            else stage_kc<p - 4>(src_y(T), fdy, s, dst + OPB, lane, kOOB);
+            if constexpr (YKS) stage_ks<p - 4>(src_y(T), sby, fdy, s, dst + OPB, wave, lane, kOOB);
+            else stage_kc<p - 4>(src_y(T), sby, fdy, s, dst + OPB, lane, kOOB);
         } else if constexpr (p == 8 && XSB > 0) {
             if constexpr (XKS)
-                stage_colscales(ColScales{T.xs, ldsb, T.nblk, T.xv}, s, st + 2 * OPB, junk, wave, 0, lane, live);
+                stage_colscales(ColScales{T.xs, ldsb, T.nblk, T.xv}, sbxs, s, st + 2 * OPB, junk, wave, 0, lane, live);
             else
                 stage_rowscales<SC == 1>(RowScales{T.xs, ldsb, T.nblk, T.xv}, s, tid, st + 2 * OPB, junk, live);
         } else if constexpr (YSB > 0) {
             if constexpr (YKS)
-                stage_colscales(ColScales{T.ys, ldsa, T.nblk, T.yv}, s, st + 2 * OPB + XSB, junk, wave, 1, lane, live);
+                stage_colscales(ColScales{T.ys, ldsa, T.nblk, T.yv}, sbys, s, st + 2 * OPB + XSB, junk, wave, 1, lane,
+                                live);
             else
                 stage_rowscales<SC == 1>(RowScales{T.ys, ldsa, T.nblk, T.yv}, s, tid, st + 2 * OPB + XSB, junk, live);
         }
@@ -1043,6 +1053,10 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         else fdx = feed_kc(src_x(ld), live, wave, lane);
         if constexpr (YKS) fdy = feed_ks(src_y(ld), live, wave, lane);
         else fdy = feed_kc(src_y(ld), live, wave, lane);
+        sbx = ld.x;
+        sby = ld.y;
+        sbxs = ld.xs;
+        sbys = ld.ys;
     };
     make_feeds();
     unsigned issued = 0, consumed = 0;
@@ -1077,10 +1091,17 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         pending = true;
     };
     auto advance_load = [&]() {
-        if (pending && ld.valid && ++ls == ld.ksteps) {
-            ld = next_tile(ld.item + istep, true);
-            ls = 0;
-            make_feeds();
+        if (pending && ld.valid) {
+            if (++ls == ld.ksteps) {
+                ld = next_tile(ld.item + istep, true);
+                ls = 0;
+                make_feeds();
+            } else {
+                sbx += dsx;
+                sby += dsy;
+                if constexpr (XKS) sbxs += dsxs;
+                if constexpr (YKS) sbys += dsys;
+            }
         }
         pending = false;
     };
