@@ -20,9 +20,11 @@
 //     inside the matrix core.  bf16 uses v_mfma_f32_32x32x16_bf16.
 //   * A stage is 64 contraction bytes of the tile's 256 rows per operand
 //     (16 KB).  Operand tiles go from memory straight into LDS (buffer_load
-//     ... lds, 16 bytes per lane); buffer loads are range-checked by the
-//     hardware, so rows, columns and contraction tails outside the operand
-//     arrive as zeros without a branch.
+//     ... lds, 16 bytes per lane).  Each lane's offsets are worked out once
+//     per tile; lanes whose rows, columns or contraction tail lie outside the
+//     operand take an offset past the resource's range, which the hardware
+//     turns into zeros without a branch, so a stage's data load is three
+//     instructions.
 //   * Four stage buffers.  Stage c is computed from registers while stage
 //     c + 1 sits in LDS and stages c + 2 .. c + 4 load: after two of stage c's
 //     MFMAs a wave waits for stage c + 1, passes the step's barrier, then
