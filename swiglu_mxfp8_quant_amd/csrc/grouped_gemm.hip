@@ -1177,8 +1177,10 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         // One MFMA per slot; a wave issues in order, so the reads and loads
         // placed after an MFMA go out while the matrix core runs it.  The
         // fragment reads take the first slots (they must land by the next
-        // step), the stage's loads the last ones.
-        constexpr int kFirstLoad = kMfma - kStageOps;
+        // step), the stage's loads the last ones; with a K-strided X and a
+        // K-contiguous Y (dgrad) the loads go out beside the reads instead
+        // (measured: 2 % faster there, 2-5 % slower for the other modes).
+        constexpr int kFirstLoad = MODE == MODE_NN ? 2 : kMfma - kStageOps;
         static_assert(kFirstLoad >= 2, "a load slot per stage load");
         static_for<2, kMfma>([&](auto I) {
             constexpr int i = decltype(I)::value;
