@@ -1177,16 +1177,21 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         // One MFMA per slot; a wave issues in order, so the reads and loads
         // placed after an MFMA go out while the matrix core runs it.  The
         // fragment reads take the first slots (they must land by the next
-        // step), the stage's loads the last ones; with a K-strided X and a
-        // K-contiguous Y (dgrad) the loads go out beside the reads instead
-        // (measured: 2 % faster there, 2-5 % slower for the other modes).
-        constexpr int kFirstLoad = MODE == MODE_NN ? 2 : kMfma - kStageOps;
-        static_assert(kFirstLoad >= 2, "a load slot per stage load");
+        // step).  Where the stage's loads go was measured per mode
+        // (alternating timings on one GPU): MXFP8 from slot 6 on (dgrad: from
+        // slot 2, beside the reads), bf16 in every other slot of the second
+        // half; packing them into the last slots was 1-5 % slower.
+        constexpr int kLoadStride = F8 ? 1 : 2;
+        constexpr int kFirstLoad = MODE == MODE_NN ? 2 : (F8 ? kMfma - 10 : kMfma - 2 * kStageOps);
+        static_assert(kFirstLoad >= 2 && kFirstLoad + (kStageOps - 1) * kLoadStride < kMfma,
+                      "a load slot per stage load");
         static_for<2, kMfma>([&](auto I) {
             constexpr int i = decltype(I)::value;
             mfma(P, I);
             if constexpr (i - 2 < kReads) read_frag(Q, IC<i - 2>{}, v);
-            if constexpr (i >= kFirstLoad) issue_piece(IC<i - kFirstLoad>{}, ld, ls, slot, live);
+            constexpr int q = i - kFirstLoad;
+            if constexpr (q >= 0 && q % kLoadStride == 0 && q / kLoadStride < kStageOps)
+                issue_piece(IC<q / kLoadStride>{}, ld, ls, slot, live);
             __builtin_amdgcn_sched_barrier(0);
         });
         issued_one(slot);
