@@ -1178,11 +1178,12 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         // placed after an MFMA go out while the matrix core runs it.  The
         // fragment reads take the first slots (they must land by the next
         // step).  Where the stage's loads go was measured per mode
-        // (alternating timings on one GPU): MXFP8 from slot 6 on (dgrad: from
-        // slot 2, beside the reads), bf16 in every other slot of the second
-        // half; packing them into the last slots was 1-5 % slower.
+        // (alternating timings on one GPU): MXFP8 NT from slot 4 on, dgrad
+        // from slot 2 (beside the reads), wgrad from slot 6, bf16 in every
+        // other slot of the second half; packing them into the last slots
+        // was 1-5 % slower, and moving the wgrad or bf16 loads earlier too.
         constexpr int kLoadStride = F8 ? 1 : 2;
-        constexpr int kFirstLoad = MODE == MODE_NN ? 2 : (F8 ? kMfma - 10 : kMfma - 2 * kStageOps);
+        constexpr int kFirstLoad = MODE == MODE_NN ? 2 : (!F8 ? kMfma - 2 * kStageOps : (MODE == MODE_NT ? 4 : 6));
         static_assert(kFirstLoad >= 2 && kFirstLoad + (kStageOps - 1) * kLoadStride < kMfma,
                       "a load slot per stage load");
         static_for<2, kMfma>([&](auto I) {
