@@ -8,6 +8,7 @@ bf16 values travel as uint16 bit patterns, E4M3 codes and E8M0 scales as uint8.
 Function map (the C file cites the page passage each one follows):
   e8m0_from_amax, double_to_e4m3, e4m3_to_double, double_to_bf16,
   bf16_to_double              -- number formats and the RCEIL scale rule
+  near_bf16_tie               -- boundary closeness of an exact value
   splits_to_offsets           -- exclusive prefix sums of split sizes
   mx_quantize                 -- the standalone 1x32 / 32x1 block quantizer
   swiglu_fwd / swiglu_bwd     -- the row-scaled (clamped) SwiGLU and its gradient
@@ -63,6 +64,8 @@ def _declare(lib):
     lib.oracle_e8m0_to_double.restype = ctypes.c_double
     lib.oracle_e8m0_from_amax.argtypes = [ctypes.c_double]
     lib.oracle_e8m0_from_amax.restype = ctypes.c_uint8
+    lib.oracle_near_bf16_tie.argtypes = [ctypes.c_double]
+    lib.oracle_near_bf16_tie.restype = ctypes.c_int
     lib.oracle_splits_to_offsets.argtypes = [P, I64, P, P]
     lib.oracle_splits_to_offsets.restype = None
     lib.oracle_mx_quantize.argtypes = [I64, I64, P, I64, I64, P, ctypes.c_uint32, P, P, P, P]
@@ -126,6 +129,15 @@ def e8m0_from_amax(amax):
     amax = np.asarray(amax, dtype=np.float64)
     return np.array([lib.oracle_e8m0_from_amax(float(v)) for v in amax.ravel()],
                     dtype=np.uint8).reshape(amax.shape)
+
+
+def near_bf16_tie(t):
+    """1 where the exact value t lies within 2 binary32 ulps (of t) of a bf16
+    rounding tie (the boundary-closeness flag of the parity rules)."""
+    lib = _load()
+    t = np.asarray(t, dtype=np.float64)
+    return np.array([lib.oracle_near_bf16_tie(float(v)) for v in t.ravel()],
+                    dtype=np.uint8).reshape(t.shape)
 
 
 # ---------------------------------------------------------------- offsets ---

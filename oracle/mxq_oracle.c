@@ -246,7 +246,7 @@ EXPORT void oracle_mx_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t 
 /* evaluation may round the other way than the exact one.                     */
 /* ------------------------------------------------------------------------- */
 
-static int near_bf16_tie(double t)
+EXPORT int oracle_near_bf16_tie(double t)
 {
     if (!isfinite(t) || t == 0.0) return 0;
     double a = fabs(t);
@@ -300,7 +300,7 @@ EXPORT void oracle_swiglu_fwd(int kind, double limit, int64_t M, int64_t K,
             double t_h = a * u * s;
             h[r * K + j] = oracle_double_to_bf16(t_h);
             if (close)
-                close[r * K + j] = (uint8_t)(near_bf16_tie(t_silu) | (near_bf16_tie(t_h) << 1));
+                close[r * K + j] = (uint8_t)(oracle_near_bf16_tie(t_silu) | (oracle_near_bf16_tie(t_h) << 1));
         }
     }
 }
@@ -319,9 +319,12 @@ EXPORT void oracle_swiglu_fwd(int kind, double limit, int64_t M, int64_t K,
  * dgate / dup are written with row strides lddg / lddu (may be NULL).
  * close (optional, M x 2K, laid out like [dgate | dup]): bit0 = the silu of g
  * is near a bf16 tie, bit1 = the pre-rounding value of that output is.
- * dscale_tol (optional, M): the tolerance for dscale described in the
- * design notes: 2e-5 * sum|dh*a*u| + sum over rows where a is near a tie of
- * |dh*u| * ulp_bf16(a).
+ * dscale_tol (optional, M): the tolerance for dscale (the pages give none):
+ * 64 * 2^-24 * sum_j |dh*a*u| -- the error bound of an fp32 summation in which
+ * no term passes through more than 63 additions, plus the final rounding --
+ * + sum over the columns where silu(g) is near a bf16 tie of
+ * |dh*u| * ulp_bf16(a) (a correct fp32 evaluation may round a the other way
+ * there).
  */
 EXPORT void oracle_swiglu_bwd(int kind, double limit, int64_t M, int64_t K,
                               const uint16_t *grad, int64_t ldgr,
@@ -357,7 +360,7 @@ EXPORT void oracle_swiglu_bwd(int kind, double limit, int64_t M, int64_t K,
             double term = dh * a * u;
             acc += term;
             acc_abs += fabs(term);
-            int ca = near_bf16_tie(t_silu);
+            int ca = oracle_near_bf16_tie(t_silu);
             if (ca) {
                 int ex;
                 frexp(fabs(a) > 0 ? fabs(a) : 1e-300, &ex);
@@ -365,12 +368,15 @@ EXPORT void oracle_swiglu_bwd(int kind, double limit, int64_t M, int64_t K,
                 flip += fabs(dh * u) * ldexp(1.0, eb - 7);
             }
             if (close) {
-                close[r * 2 * K + j] = (uint8_t)(ca | (near_bf16_tie(t_dg) << 1));
-                close[r * 2 * K + K + j] = (uint8_t)(ca | (near_bf16_tie(t_du) << 1));
+                close[r * 2 * K + j] = (uint8_t)(ca | (oracle_near_bf16_tie(t_dg) << 1));
+                close[r * 2 * K + K + j] = (uint8_t)(ca | (oracle_near_bf16_tie(t_du) << 1));
             }
         }
         if (dscale) dscale[r] = (float)acc;
-        if (dscale_tol) dscale_tol[r] = 2e-5 * acc_abs + flip;
+        /* an fp32 summation in which no term passes through more than 63
+           additions is within 63 * 2^-24 * sum|t| of the exact sum, and the
+           exact sum's own rounding to fp32 adds at most 2^-24 * sum|t| */
+        if (dscale_tol) dscale_tol[r] = ldexp(64.0, -24) * acc_abs + flip;
     }
 }
 
