@@ -381,6 +381,60 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, con
 // workspace (256 bytes keep the allocation's alignment simple).
 static size_t gemm_ws_bytes(const mxq_gemm_args &a) { return a.mode == MXQ_GEMM_TN ? 256 : 0; }
 
+namespace {
+
+// Footprint of G stacked (rows x cols) arrays with row pitch ld and group
+// stride gstride (elements): one 2-D range for a single group, else the whole
+// interval from the first element to the last.
+Range range_groups(const void *p, int64_t G, int64_t gstride, int64_t rows, int64_t cols, int64_t ld, int64_t esize,
+                   const char *name) {
+    if (G <= 1 || p == nullptr || rows <= 0 || cols <= 0) return range2d(p, rows, cols, ld, esize, name);
+    Range r;
+    r.name = name;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + (uintptr_t)(((G - 1) * gstride + (rows - 1) * ld + cols) * esize);
+    return r;
+}
+
+// The output of a grouped GEMM must not overlap any input (its operands,
+// their scales, the offsets).  With accumulate the output is read too, which
+// is allowed: it is compared with the inputs only.
+mxq_status check_gemm_alias(const mxq_gemm_args &a) {
+    if (a.M == 0 || a.N == 0) return MXQ_OK;
+    const bool f8 = a.A.dtype == MXQ_DTYPE_MXFP8_E4M3;
+    const int64_t esz = f8 ? 1 : 2, osz = a.out_dtype == MXQ_DTYPE_F32 ? 4 : 2;
+    std::vector<Range> ins;
+    ins.push_back(range2d(a.row_off, 1, a.G + 1, a.G + 1, 8, "row_off"));
+    if (a.block_off) ins.push_back(range2d(a.block_off, 1, a.G + 1, a.G + 1, 8, "block_off"));
+    Range out;
+    if (a.mode == MXQ_GEMM_TN) {
+        // colwise scales: the ceil(rows/32) scale rows that always exist
+        const int64_t nb = (a.rows + 31) / 32;
+        ins.push_back(range2d(a.A.data, a.rows, a.M, a.A.ld, esz, "A"));
+        ins.push_back(range2d(a.B.data, a.rows, a.N, a.B.ld, esz, "B"));
+        if (f8) {
+            ins.push_back(range2d(a.A.scales, nb, a.M, a.A.ld_scales, 1, "A scales"));
+            ins.push_back(range2d(a.B.scales, nb, a.N, a.B.ld_scales, 1, "B scales"));
+        }
+        out = range_groups(a.out, a.G, a.out_gstride, a.M, a.N, a.ld_out, osz, "out");
+    } else {
+        const int64_t kb = (a.K + 31) / 32;
+        ins.push_back(range2d(a.A.data, a.M, a.K, a.A.ld, esz, "A"));
+        if (f8) ins.push_back(range2d(a.A.scales, a.M, kb, a.A.ld_scales, 1, "A scales"));
+        if (a.mode == MXQ_GEMM_NT) {
+            ins.push_back(range_groups(a.B.data, a.G, a.B.gstride, a.N, a.K, a.B.ld, esz, "B"));
+            if (f8) ins.push_back(range_groups(a.B.scales, a.G, a.B.scale_gstride, a.N, kb, a.B.ld_scales, 1, "B scales"));
+        } else {
+            ins.push_back(range_groups(a.B.data, a.G, a.B.gstride, a.K, a.N, a.B.ld, esz, "B"));
+            if (f8) ins.push_back(range_groups(a.B.scales, a.G, a.B.scale_gstride, kb, a.N, a.B.ld_scales, 1, "B scales"));
+        }
+        out = range2d(a.out, a.M, a.N, a.ld_out, osz, "out");
+    }
+    return check_alias(ins, {out});
+}
+
+}  // namespace
+
 mxq_status mxq_grouped_gemm_workspace(const mxq_gemm_args *args, size_t *bytes) {
     if (args == nullptr || bytes == nullptr) return fail(MXQ_ERR_NULL, "args and bytes are required");
     *bytes = gemm_ws_bytes(*args);
@@ -393,6 +447,7 @@ mxq_status mxq_grouped_gemm(const mxq_gemm_args *args, void *ws, size_t ws_bytes
     std::string err;
     const int st = mxq::gemm_prepare(*args, g, err);
     if (st != MXQ_OK) return fail((mxq_status)st, "%s", err.c_str());
+    if (check_gemm_alias(*args) != MXQ_OK) return MXQ_ERR_ALIAS;
     const size_t need = gemm_ws_bytes(*args);
     if (need > 0) {
         if (ws == nullptr || ws_bytes < need)

@@ -173,3 +173,24 @@ def test_gemm_workspace_and_validation(m):
     assert lib.mxq_grouped_gemm(ctypes.byref(gemm_args(m, m.GEMM_TN, max_wg=-1)), fake(6 << 28), 256, None) == 2
     assert lib.mxq_grouped_gemm(ctypes.byref(gemm_args(m, m.GEMM_NT, max_wg=-8)), None, 0, None) == 2
     assert lib.mxq_grouped_gemm(ctypes.byref(gemm_args(m, m.GEMM_NT, K=48)), None, 0, None) == 2
+
+
+def test_gemm_output_alias_rejected(m):
+    """An output overlapping an operand, an operand's scales or the offsets is
+    refused with MXQ_ERR_ALIAS before anything is launched, in every mode (a
+    persistent kernel would otherwise read tiles other workgroups overwrite)."""
+    lib = m.lib
+    for mode in (m.GEMM_NT, m.GEMM_NN, m.GEMM_TN):
+        for target in (1 << 28, 2 << 28, 3 << 28, 4 << 28, 0):   # A, A scales, B, B scales, row_off
+            a = gemm_args(m, mode)
+            if mode == m.GEMM_NN:   # B per group (K x N), colwise scales (K/32 x N)
+                a.B.ld, a.B.ld_scales, a.B.scale_gstride = 256, 256, 8 * 256
+            a.out = BASE + target + (64 if target else 0)
+            ws = fake(6 << 28) if mode == m.GEMM_TN else None
+            assert lib.mxq_grouped_gemm(ctypes.byref(a), ws, 256 if ws else 0, None) == 5, (mode, target)
+            assert "overlaps" in m.last_error()
+    # the last group of a stacked B: out just inside its end, then just past it
+    a = gemm_args(m, m.GEMM_NT)
+    endB = (3 << 28) + (4 - 1) * 256 * 256 + (256 - 1) * 256 + 256
+    a.out = BASE + endB - 16
+    assert lib.mxq_grouped_gemm(ctypes.byref(a), None, 0, None) == 5
