@@ -423,6 +423,28 @@ def test_silu_exhaustive_through_dup(mxq):
     assert not mism.any(), f"{int(mism.sum())} silu mismatches, e.g. g bits {g[mism][:5]}"
 
 
+def test_dsilu_exhaustive_through_dgate(mxq):
+    """dgate = bf16(dh * s * u * silu'(g)) with dh = s = u = 1 is bf16(silu'(g)):
+    all 65,280 finite bf16 gate values through the fast path's error bound
+    and the exact path it sends close cases to, bit-exact against the oracle
+    (plain and clamped: the clamp's mask zeroes g > 7)."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = (allb.astype(np.uint32) << 16).view(np.float32)
+    g = allb[np.isfinite(vals)].reshape(-1, 32)
+    u = np.full_like(g, 0x3F80)
+    dh = np.full_like(g, 0x3F80)
+    gg, uu, dd = (W.from_bits(x, "cuda") for x in (g, u, dh))
+    for clamped in (False, True):
+        ref = O.swiglu_bwd(dh, g, u, kind=O.CLAMPED_SWIGLU if clamped else O.SWIGLU)[0]
+        out = mxq.swiglu_quantize_bwd(dd, gg, uu, None, rowwise=False, colwise=False, dense=True,
+                                      want_dscale=False, clamped=clamped)
+        torch.cuda.synchronize()
+        dg = bits(out[4])[:, :32]
+        nan = ((dg & 0x7FFF) > 0x7F80) & ((ref & 0x7FFF) > 0x7F80)
+        mism = (dg != ref) & ~nan
+        assert not mism.any(), f"{int(mism.sum())} silu' mismatches (clamped={clamped}), e.g. g bits {g[mism][:5]}"
+
+
 def test_backward_deterministic(mxq):
     gu = W.packed_gate_up(512, 7168, seed=18).cuda()
     sc = W.row_scale(512, seed=18).cuda()

@@ -404,3 +404,60 @@ def test_multi_tile_bf16(mxq, splits, max_wg):
     mxq.grouped_gemm(mxq.GEMM_NT, ro, to_dev(A), to_dev(B), out, max_workgroups=max_wg)
     torch.cuda.synchronize()
     check_close(out_np(out), ref_np(ref, "bf16"))
+
+
+# ------------------------------------------------------------------ the row-scale ring
+
+# The K-contiguous row scales of MXFP8 NT / NN launches come through a two-slot
+# LDS ring, 16 scale bytes per row per 8 stages of 64 contraction bytes, when
+# every row-scale pitch is a multiple of 4 bytes and the contraction has
+# ks = K/64 >= 3 stages with ks % 8 either 0 or >= 3.  The expert layer's
+# launches all take it, with several ring groups per tile:
+#   NT K = 768 (FC2 forward):  A and B pitches 24 B (24 % 4 == 0); ks = 12 =
+#       one whole 8-stage group and a 4-stage tail group;
+#   NT K = 1024:               pitches 32 B; ks = 16 = two whole groups;
+#   NN K = 1536 (FC1 dgrad):   A's pitch 48 B (B's column scales stay per
+#       stage); ks = 24 = three groups;
+#   NN K = 2048 (FC2 dgrad):   A's pitch 64 B; ks = 32 = four groups.
+# Empty groups sit between the others, and max_workgroups = 8 chains many
+# tiles through each workgroup (the ring's slot parity carries across tiles).
+RING_SPLITS = [70, 0, 300, 1, 0, 129, 33, 0]
+_RING_CACHE = {}
+
+
+def ring_case(mode, K, N=272):
+    """Inputs and the oracle's result of a ring-path case (computed once)."""
+    key = (mode, K)
+    if key not in _RING_CACHE:
+        rng = np.random.default_rng(41 + K)
+        splits = RING_SPLITS
+        ro_np = O.splits_to_offsets(splits)[0]
+        R, G = sum(splits), len(splits)
+        A, As = qrows(rng, (R, K))
+        if mode == "NT":
+            Bl = [qrows(rng, (N, K), 0.05) for _ in range(G)]
+            opB_args = lambda B, Bs: O.Operand("mxfp8", B, N * K, K, 1, Bs, N * (K // 32), K // 32, 1)
+        else:
+            Bl = [qcols(rng, (K, N), None, 0.05) for _ in range(G)]
+            opB_args = lambda B, Bs: O.Operand("mxfp8", B, K * N, 1, N, Bs, (K // 32) * N, 1, N)
+        B, Bs = np.stack([b[0] for b in Bl]), np.stack([b[1] for b in Bl])
+        assert As.shape[1] % 4 == 0 and (mode == "NN" or Bs.shape[2] % 4 == 0)
+        ks = K // 64
+        assert ks >= 3 and (ks % 8 == 0 or ks % 8 >= 3)
+        opA = O.Operand("mxfp8", A, 0, K, 1, As, 0, K // 32, 1)
+        ref = O.grouped_gemm("m", ro_np, 0, N, K, opA, opB_args(B, Bs), "bf16")
+        _RING_CACHE[key] = (A, As, B, Bs, ref)
+    return _RING_CACHE[key]
+
+
+@pytest.mark.parametrize("max_wg", [0, 8])
+@pytest.mark.parametrize("mode,K", [("NT", 768), ("NT", 1024), ("NN", 1536), ("NN", 2048)])
+def test_scale_ring_mxfp8(mxq, mode, K, max_wg):
+    A, As, B, Bs, ref = ring_case(mode, K)
+    ro, bo, ro_np, _ = offsets(mxq, RING_SPLITS)
+    R, N = A.shape[0], 272
+    out = torch.full((R, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    mxq.grouped_gemm(mxq.GEMM_NT if mode == "NT" else mxq.GEMM_NN, ro, to_dev(A), to_dev(B), out, to_dev(As),
+                     to_dev(Bs), max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    check_close(out_np(out), ref_np(ref, "bf16"))

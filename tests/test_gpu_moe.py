@@ -7,8 +7,10 @@ Pages: "Activation + GroupedLinear Fusion for MOE and other MOE optimizations"
 (Sequence Diagram: forward and backward of the grouped expert MLP with the
 fused activation); NVIDIA/TransformerEngine pull 3224 (grouped GEMM over
 expert row groups).  Small Qwen3-MoE-shaped layers: uniform top-k routing
-with the plain SwiGLU, and skewed Zipf routing (empty experts) with the
-clamped SwiGLU.
+with the plain SwiGLU, and skewed Zipf routing (empty experts) with the plain
+and the clamped SwiGLU; and the full-size layer (65,536 routed rows, 128
+experts) in the benchmark's launch configuration, checked on sampled experts,
+rows and columns.
 """
 import numpy as np
 import pytest
@@ -52,7 +54,7 @@ def same(got, ref, what):
     assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} differ"
 
 
-@pytest.mark.parametrize("skewed,clamped", [(False, False), (True, True)])
+@pytest.mark.parametrize("skewed,clamped", [(False, False), (True, False), (True, True)])
 def test_layer_forward_backward(mxq, skewed, clamped):
     from swiglu_mxfp8_quant_amd.moe import Layer
     T, H, E, k, I = 64, 128, 16, 2, 64
@@ -149,3 +151,148 @@ def test_layer_forward_backward(mxq, skewed, clamped):
     ref = O.grouped_gemm("k", ro, 2 * I, H, 0, O.Operand("mxfp8", bcc, 0, 1, 2 * I, bcs, 0, 1, 2 * I),
                          O.Operand("mxfp8", xq[1], 0, 1, H, xq[3], 0, 1, H), "bf16")
     close(bits(gr["dw13"]), ref, "FC1 wgrad")
+
+
+# ------------------------------------------------------------------ full size, sampled
+
+def _pick_experts(splits):
+    """The largest expert, the smallest non-empty one, and the one whose last
+    256-row tile is closest to half full."""
+    nz = [g for g in range(len(splits)) if splits[g] > 0]
+    big = max(nz, key=lambda g: (splits[g], -g))
+    small = min(nz, key=lambda g: (splits[g], g))
+    rest = [g for g in nz if g not in (big, small)]
+    mid = max(rest, key=lambda g: (min(splits[g] % 256, 256 - splits[g] % 256), -g))
+    return [big, small, mid]
+
+
+def _rows(r0, r1):
+    """The first and last 40 rows of a group (every row of a small one)."""
+    if r1 - r0 <= 80:
+        return np.arange(r0, r1)
+    return np.concatenate([np.arange(r0, r0 + 40), np.arange(r1 - 40, r1)])
+
+
+def _host(t, rows=None):
+    x = t if rows is None else t[torch.as_tensor(rows, device=t.device)]
+    return bits(x) if x.dtype == torch.bfloat16 else u8(x)
+
+
+@pytest.mark.parametrize("routing", ["uniform_plain", "zipf_plain", "zipf_clamped"])
+def test_full_size_layer_sampled(mxq, routing):
+    """The expert layer at its full size (8192 tokens, top-8: 65,536 routed rows,
+    hidden 2048, 128 experts, intermediate 768), forward + backward through
+    the same calls the benchmark times.  For the largest expert, the smallest
+    non-empty one and one ending mid-tile: each of the six GEMMs on a
+    64-column slice that crosses a 256-column tile boundary (M-grouped: the
+    first and last 40 rows of the expert; K-grouped: a 64 x 64 block of the
+    expert's weight gradient, summed over all its rows), and every
+    quantization (activation forward and backward, dY, X, W2, W13) over the
+    expert's whole row range, against the oracle on the GPU's own inputs to
+    that stage."""
+    from swiglu_mxfp8_quant_amd.moe import Layer
+    skewed, clamped = routing.startswith("zipf"), routing.endswith("clamped")
+    print(routing, flush=True)
+    moe = W.moe_layer(0, device="cuda", skewed=skewed)
+    cfg = moe["cfg"]
+    H, I, E = cfg["hidden"], cfg["inter"], cfg["experts"]
+    splits = moe["splits"].cpu().numpy()
+    R = int(splits.sum())
+    assert R == 65536 and (not skewed or (splits == 0).sum() == 8)
+    ro, bo = O.splits_to_offsets(splits)
+    kind = O.CLAMPED_SWIGLU if clamped else O.SWIGLU
+    layer = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped)
+    y = layer.forward(moe["x_perm"], moe["scale"])
+    dy = W.moe_grad(R, H, seed=0, device="cuda")
+    layer.backward(dy)
+    torch.cuda.synchronize()
+    s, gr = layer.saved, layer.grads
+    scale = moe["scale"].cpu().numpy()
+    c16 = lambda c0: slice(c0, c0 + 64)
+    for g in _pick_experts(splits):
+        r0, r1 = int(ro[g]), int(ro[g + 1])
+        b0, b1 = int(bo[g]), int(bo[g + 1])
+        S = _rows(r0, r1)
+        n = len(S)
+        one = np.array([0, n], np.int64)
+        print("  expert", g, "rows", r1 - r0, flush=True)
+        # FC1 (bf16 NT): columns 224..287 of the (R, 2I) output
+        cs = c16(224)
+        xs = _host(s["x_perm"], S)
+        w13g = bits(moe["w13"][g, cs, :])
+        ref = O.grouped_gemm("m", one, 0, 64, H, O.Operand("bf16", xs, 0, H, 1), O.Operand("bf16", w13g, 0, H, 1),
+                             "bf16")
+        close(_host(s["h13"], S)[:, cs], ref, f"FC1 expert {g}")
+        # FC2 (MXFP8 NT): columns 224..287 of (R, H)
+        A, As = _host(s["a_r"], S), _host(s["as_r"], S)
+        B, Bs = u8(s["w2q"][g, cs, :]), u8(s["w2s"][g, cs, :])
+        ref = O.grouped_gemm("m", one, 0, 64, I, O.Operand("mxfp8", A, 0, I, 1, As, 0, I // 32, 1),
+                             O.Operand("mxfp8", B, 0, I, 1, Bs, 0, I // 32, 1), "bf16")
+        close(_host(y, S)[:, cs], ref, f"FC2 expert {g}")
+        # FC2 dgrad (MXFP8 NN): columns 224..287 of (R, I)
+        A, As = _host(gr["dy_r"], S), _host(gr["dys_r"], S)
+        B = np.ascontiguousarray(u8(gr["w2c"][g])[:, cs])
+        Bs = np.ascontiguousarray(u8(gr["w2cs"][g])[:, cs])
+        ref = O.grouped_gemm("m", one, 0, 64, H, O.Operand("mxfp8", A, 0, H, 1, As, 0, H // 32, 1),
+                             O.Operand("mxfp8", B, 0, 1, 64, Bs, 0, 1, 64), "bf16")
+        close(_host(gr["da"], S)[:, cs], ref, f"FC2 dgrad expert {g}")
+        # FC1 dgrad (MXFP8 NN): columns 224..287 of (R, H)
+        A, As = _host(gr["dq_r"], S), _host(gr["dqs_r"], S)
+        B = np.ascontiguousarray(u8(gr["w13c"][g])[:, cs])
+        Bs = np.ascontiguousarray(u8(gr["w13cs"][g])[:, cs])
+        ref = O.grouped_gemm("m", one, 0, 64, 2 * I, O.Operand("mxfp8", A, 0, 2 * I, 1, As, 0, 2 * I // 32, 1),
+                             O.Operand("mxfp8", B, 0, 1, 64, Bs, 0, 1, 64), "bf16")
+        close(_host(gr["dx"], S)[:, cs], ref, f"FC1 dgrad expert {g}")
+        # the wgrads (MXFP8 TN) over the expert's whole row range
+        allr = np.arange(r0, r1)
+        grp = np.array([0, r1 - r0], np.int64)
+        for name, Ac, Acs, Bc, Bcs, out, ms, ns in (
+                ("FC2 wgrad", gr["dy_c"], gr["dys_c"], s["a_c"], s["as_c"], gr["dw2"], c16(224), c16(224)),
+                ("FC1 wgrad", gr["dq_c"], gr["dqs_c"], gr["x_c"], gr["xs_c"], gr["dw13"], c16(736), c16(224))):
+            A = np.ascontiguousarray(_host(Ac, allr)[:, ms])
+            As = np.ascontiguousarray(u8(Acs[b0:b1])[:, ms])
+            B = np.ascontiguousarray(_host(Bc, allr)[:, ns])
+            Bs = np.ascontiguousarray(u8(Bcs[b0:b1])[:, ns])
+            ref = O.grouped_gemm("k", grp, 64, 64, 0, O.Operand("mxfp8", A, 0, 1, 64, As, 0, 1, 64),
+                                 O.Operand("mxfp8", B, 0, 1, 64, Bs, 0, 1, 64), "bf16")
+            close(bits(out[g, ms, ns]), ref[0], f"{name} expert {g}")
+        # activation forward on the expert's rows of the GPU's H13 (one group:
+        # colwise blocks restart at the expert's first row)
+        h13 = _host(s["h13"], allr)
+        rc, cc, rs, cs_, _h = O.swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale[r0:r1], 3, None, kind, 7.0)
+        same(u8(s["a_r"][r0:r1]), rc, "act fwd row codes")
+        same(u8(s["as_r"][r0:r1]), rs, "act fwd row scales")
+        same(u8(s["a_c"][r0:r1]), cc, "act fwd col codes")
+        same(u8(s["as_c"][b0:b1]), cs_, "act fwd col scales")
+        # activation backward on the expert's rows of the GPU's dA and H13
+        da = _host(gr["da"], allr)
+        b = O.swiglu_quantize_bwd(da, h13[:, :I], h13[:, I:], scale[r0:r1], 3, None, kind, 7.0, want_close=True)
+        same(u8(gr["dq_r"][r0:r1]), b[0], "act bwd row codes")
+        same(u8(gr["dqs_r"][r0:r1]), b[2], "act bwd row scales")
+        same(u8(gr["dq_c"][r0:r1]), b[1], "act bwd col codes")
+        same(u8(gr["dqs_c"][b0:b1]), b[3], "act bwd col scales")
+        dd = bits(gr["dd"][r0:r1])
+        same(dd[:, :I], b[4], "dgate")
+        same(dd[:, I:], b[5], "dup")
+        err = np.abs(gr["dscale"][r0:r1].cpu().numpy().astype(np.float64) - b[6])
+        assert np.all(err <= b[8] + 1e-30), f"dscale off by {err.max()}"
+        # dY (both directions) and X (colwise) over the expert's rows
+        q = O.mx_quantize(bits(dy[r0:r1]), 3)
+        same(u8(gr["dy_r"][r0:r1]), q[0], "dY row codes")
+        same(u8(gr["dys_r"][r0:r1]), q[2], "dY row scales")
+        same(u8(gr["dy_c"][r0:r1]), q[1], "dY col codes")
+        same(u8(gr["dys_c"][b0:b1]), q[3], "dY col scales")
+        q = O.mx_quantize(_host(s["x_perm"], allr), 2)
+        same(u8(gr["x_c"][r0:r1]), q[1], "X col codes")
+        same(u8(gr["xs_c"][b0:b1]), q[3], "X col scales")
+        # this expert's weights: W2 rowwise along I and colwise along H, W13 colwise along 2I
+        q = O.mx_quantize(bits(moe["w2"][g]), 3)
+        same(u8(s["w2q"][g]), q[0], "W2 row codes")
+        same(u8(s["w2s"][g]), q[2], "W2 row scales")
+        same(u8(s["w2c"][g]), q[1], "W2 col codes")
+        same(u8(s["w2cs"][g]), q[3], "W2 col scales")
+        q = O.mx_quantize(bits(moe["w13"][g]), 2)
+        same(u8(gr["w13c"][g]), q[1], "W13 col codes")
+        same(u8(gr["w13cs"][g]), q[3], "W13 col scales")
+    del layer, moe, dy, y
+    torch.cuda.empty_cache()
