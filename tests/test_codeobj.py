@@ -39,7 +39,11 @@ def _device_code(tmp_path):
     if not os.path.exists(LIB):
         pytest.skip("libmxq.so is not built")
     fat = tmp_path / "fatbin.bin"
-    subprocess.run([tools["objcopy"], "--dump-section", f".hip_fatbin={fat}", LIB], check=True)
+    # objcopy rewrites the file it reads in place: work on a copy, never on the
+    # library this process (or another) has mapped
+    lib_copy = tmp_path / "libmxq_copy.so"
+    shutil.copyfile(LIB, lib_copy)
+    subprocess.run([tools["objcopy"], "--dump-section", f".hip_fatbin={fat}", str(lib_copy)], check=True)
     blob = fat.read_bytes()
     magic = b"__CLANG_OFFLOAD_BUNDLE__"
     starts = [m.start() for m in re.finditer(re.escape(magic), blob)]
