@@ -1,24 +1,36 @@
-"""Benchmark of the fused SwiGLU + MXFP8 path (and, when built, the grouped GEMM)
-on one MI355X.
+"""Benchmark of the fused SwiGLU + MXFP8 path and the grouped GEMM on one MI355X.
 
-One step = every cell of the fused-activation workload once: forward and
-backward, each rowwise / colwise / both, at gate/up shapes (4096, 2048),
-(4096, 7168) and (16384, 7168) (bf16 ~N(0,1) gate/up as views of one packed
-[gate | up] buffer, fp32 row scale ~U(0.5,1.5), bf16 grad ~N(0,1e-2)); the
-shapes are interleaved so that consecutive cells never reuse cached inputs.
-value = algorithmic bytes of the step / step time, in GB/s (inputs read once,
-outputs written once; forward 4 + n_dir*(1 + 1/32) B per element + 4 B per
-row, backward 10 + 2*n_dir*(1 + 1/32) B per element + 8 B per row, the
-backward writing the bf16 dgate/dup and the fp32 dscale too).
+One step = the bandwidth-stress workload: the fused row-scaled SwiGLU + MXFP8
+forward and backward, both scale directions, at gate/up (131072, 8192) bf16
+~N(0,1) passed as views of one packed [gate | up] buffer, fp32 row scale
+~U(0.5,1.5), bf16 grad ~N(0,1e-2), with 0.1 % of aligned 1x32 and 32x1 blocks
+of gate (and of grad) set to zero and 0.1 % of blocks of gate and of up holding
+one ~N(0,1e3) outlier (page "[mxfp8 training] Add a fused gated-activation
+(SwiGLU) + MXFP8 quantization kernel", Performance: the (131072, 8192) rows).
+The backward writes the bf16 dgate/dup and the fp32 dscale besides the MXFP8
+[dgate | dup].  value = algorithmic bytes of the step / step time, in GB/s
+(inputs read once, outputs written once: forward 4 + n_dir*(1 + 1/32) B per
+element + 4 B per row, backward 10 + 2*n_dir*(1 + 1/32) B per element + 8 B per
+row).
 
-The grouped GEMMs are measured on the expert-layer workload (Qwen3-MoE-like:
-8192 tokens, hidden 2048, 128 experts, top-8, intermediate 768): one forward +
-backward of the layer through swiglu_mxfp8_quant_amd.moe (FC1 bf16, FC2, FC2
-dgrad / wgrad, FC1 dgrad / wgrad in MXFP8, plus the fused activation and the
-quantizations), with uniform softmax top-8 routing and plain SwiGLU, and with
-skewed Zipf(1.2) routing (8 empty experts) and the clamped SwiGLU.  Reported
-under "gemm": each GEMM's median time and TFLOP/s (2 flops per MAC), and the
-whole layer's wall time.
+Outside the timed region, for the record:
+  * per_cell: every cell of the (4096, 2048), (4096, 7168), (16384, 7168)
+    shapes and of (131072, 8192), forward and backward x rowwise / colwise /
+    both, and the backward without dense outputs or dscale (the layout the
+    torchao page times: 6 + 2*n_dir*(1 + 1/32) B per element + 4 B per row);
+    p10 / median / p90 of device times with the caches flushed before each;
+  * gemm: the expert-layer workload (Qwen3-MoE-like: 8192 tokens, hidden 2048,
+    128 experts, top-8, intermediate 768) forward + backward through
+    swiglu_mxfp8_quant_amd.moe with uniform softmax top-8 routing and plain
+    SwiGLU, and with skewed Zipf(1.2) routing (8 empty experts) and the plain
+    and the clamped SwiGLU: each grouped GEMM's median time and TFLOP/s, and
+    the whole layer's wall time;
+  * gemm_supplementary: a compute-bound grouped GEMM outside the workload
+    configurations, labelled as such;
+  * clocks: the GPU's current sclk / mclk as rocm-smi reports them;
+  * cpu_baseline: the CPU oracle on a bounded sample of the step's workload,
+    on one host thread and on all of the process's host cores, and the
+    oracle's grouped GEMM on an FC2-shaped slice.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-moe]
 Prints one JSON line.
@@ -26,27 +38,33 @@ Prints one JSON line.
 import argparse
 import collections
 import csv
-import statistics
 import json
 import os
+import re
+import statistics
+import subprocess
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-SHAPES = [(4096, 2048), (4096, 7168), (16384, 7168)]
+STRESS = (131072, 8192)
+C2_SHAPES = [(4096, 2048), (4096, 7168), (16384, 7168)]
 DIRS = [("row", 1), ("col", 2), ("both", 3)]
 HBM_PEAK_GBS = 8000.0
-DOMINANT = ("bwd", "both", (16384, 7168))
+STEP_CELLS = [("fwd", "both", STRESS, "dense"), ("bwd", "both", STRESS, "dense")]
+DOMINANT = ("bwd", "both", STRESS, "dense")
 
 
 def fwd_bytes(M, K, nd):
     return M * K * (4 + nd * (1 + 1 / 32)) + 4 * M
 
 
-def bwd_bytes(M, K, nd):
-    return M * K * (10 + 2 * nd * (1 + 1 / 32)) + 8 * M
+def bwd_bytes(M, K, nd, dense=True):
+    if dense:
+        return M * K * (10 + 2 * nd * (1 + 1 / 32)) + 8 * M
+    return M * K * (6 + 2 * nd * (1 + 1 / 32)) + 4 * M
 
 
 def ndir(d):
@@ -54,11 +72,13 @@ def ndir(d):
 
 
 class Cell:
-    """One (pass, direction, shape) call with its outputs preallocated."""
+    """One (pass, direction, shape, output mode) call with its outputs
+    preallocated.  mode "dense": the backward writes dgate/dup and dscale too;
+    "codes": only the MXFP8 outputs (the forward is always "dense")."""
 
-    def __init__(self, m, torch, data, kind, dname, dirs, shape):
+    def __init__(self, m, torch, data, kind, dname, dirs, shape, mode="dense"):
         M, K = shape
-        self.kind, self.dname, self.dirs, self.shape = kind, dname, dirs, shape
+        self.kind, self.dname, self.dirs, self.shape, self.mode = kind, dname, dirs, shape, mode
         gu, sc, dy = data[shape]
         g, u = gu[:, :K], gu[:, K:]
         act = m.make_act()
@@ -69,32 +89,49 @@ class Cell:
             self.fn = lambda: m.mxq_swiglu_quantize_fwd(act, g, u, sc, None, dirs, ro, co)
             self.bytes = fwd_bytes(M, K, ndir(dirs))
         else:
+            dense = mode == "dense"
             rc, cc, rs, cs = m._alloc_mx(M, 2 * K, dirs, (M + 31) // 32, "cuda")
             ro, co = m._outs(rc, cc, rs, cs, dirs)
-            dd = torch.empty((M, 2 * K), dtype=torch.bfloat16, device="cuda")
-            ds = torch.empty(M, dtype=torch.float32, device="cuda")
-            nws = m.mxq_swiglu_quantize_bwd_workspace(M, K, dirs)
-            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+            dd = torch.empty((M, 2 * K), dtype=torch.bfloat16, device="cuda") if dense else None
+            ds = torch.empty(M, dtype=torch.float32, device="cuda") if dense else None
+            nws = m.mxq_swiglu_quantize_bwd_workspace(M, K, dirs) if dense else 0
+            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if dense else None
             self.keep = (rc, cc, rs, cs, ro, co, dd, ds, ws, act)
-            self.fn = lambda: m.mxq_swiglu_quantize_bwd(act, dy, g, u, sc, None, dd[:, :K], dd[:, K:], ds,
-                                                        dirs, ro, co, ws)
-            self.bytes = bwd_bytes(M, K, ndir(dirs))
+            self.fn = lambda: m.mxq_swiglu_quantize_bwd(act, dy, g, u, sc, None,
+                                                        dd[:, :K] if dense else None,
+                                                        dd[:, K:] if dense else None, ds, dirs, ro, co, ws)
+            self.bytes = bwd_bytes(M, K, ndir(dirs), dense)
 
     def key(self):
-        return (self.kind, self.dname, self.shape)
+        return (self.kind, self.dname, self.shape, self.mode)
+
+    def label(self):
+        s = f"{self.kind}.{self.dname}.{self.shape[0]}x{self.shape[1]}"
+        return s if self.mode == "dense" else s + ".codes_only"
 
 
-def build_cells(m, torch, W):
+def make_data(torch, W, shapes):
     data = {}
-    for (M, K) in SHAPES:
-        data[(M, K)] = (W.packed_gate_up(M, K, seed=0, device="cuda"), W.row_scale(M, seed=0, device="cuda"),
-                        W.grad_out(M, K, seed=0, device="cuda"))
+    for (M, K) in shapes:
+        if (M, K) == STRESS:
+            data[(M, K)] = W.stress_inputs(M, K, seed=0, device="cuda", frac=1e-3)
+        else:
+            data[(M, K)] = (W.packed_gate_up(M, K, seed=0, device="cuda"), W.row_scale(M, seed=0, device="cuda"),
+                            W.grad_out(M, K, seed=0, device="cuda"))
+    return data
+
+
+def record_cells(m, torch, data):
+    """Every cell outside the timed step (per_cell timings)."""
     cells = []
-    for kind in ("fwd", "bwd"):
-        for dname, d in DIRS:
-            for shape in SHAPES:
+    for shape in C2_SHAPES + [STRESS]:
+        for kind in ("fwd", "bwd"):
+            for dname, d in DIRS:
                 cells.append(Cell(m, torch, data, kind, dname, d, shape))
-    return cells, data
+        for dname, d in DIRS:
+            if shape in ((16384, 7168), STRESS):
+                cells.append(Cell(m, torch, data, "bwd", dname, d, shape, "codes"))
+    return cells
 
 
 def measured_traffic():
@@ -104,7 +141,7 @@ def measured_traffic():
     import hashlib
     tf = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(tf))["bwd_both_16384x7168"]
+        rec = json.load(open(tf))["bwd_both_131072x8192"]
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()
         if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
             return None
@@ -113,8 +150,26 @@ def measured_traffic():
         return None
 
 
+def percentiles(ts):
+    ts = sorted(ts)
+    q = lambda p: ts[min(len(ts) - 1, max(0, round(p * (len(ts) - 1))))]
+    return q(0.1), q(0.5), q(0.9)
+
+
+def gpu_clocks():
+    """sclk / mclk of card 0 as rocm-smi reports them (strings), or the error."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        js = json.loads(r.stdout[r.stdout.index("{"):])
+        card = js[sorted(js)[0]]
+        return {k: v for k, v in card.items() if "sclk" in k or "mclk" in k or "fclk" in k}
+    except Exception as e:  # the record only; never fails the benchmark
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+
+
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
+MOE_VARIANTS = (("uniform_plain", False, False), ("zipf_plain", True, False), ("zipf_clamped", True, True))
 
 
 def moe_section(m, torch, W, reps=5):
@@ -122,7 +177,7 @@ def moe_section(m, torch, W, reps=5):
     from swiglu_mxfp8_quant_amd.moe import Layer, gemm_flops
     stream = torch.cuda.current_stream()
     out = {}
-    for name, skewed, clamped in (("uniform_plain", False, False), ("zipf_clamped", True, True)):
+    for name, skewed, clamped in MOE_VARIANTS:
         moe = W.moe_layer(0, device="cuda", skewed=skewed)
         cfg = moe["cfg"]
         H, I, G = cfg["hidden"], cfg["inter"], cfg["experts"]
@@ -144,6 +199,18 @@ def moe_section(m, torch, W, reps=5):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e3)
         layer_us = sorted(ts)[len(ts) // 2]
+        # the same with the MXFP8 weight cache valid (the device flag skips the
+        # weight quantizations, as on the micro-batches after a weight update)
+        layer.mark_weights_current()
+        ts = []
+        for _ in range(reps):
+            e0.record(stream)
+            full()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        cached_us = sorted(ts)[len(ts) // 2]
+        layer.mark_weights_changed()
         s, gr, ro, bo = layer.saved, layer.grads, layer.row_off, layer.block_off
         h13 = torch.empty_like(s["h13"])
         y = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
@@ -179,6 +246,7 @@ def moe_section(m, torch, W, reps=5):
             tot_fl += flops[k]
             tot_us += us
         out[name] = {"routed_rows": R, "layer_fwd_bwd_us": round(layer_us, 1),
+                     "layer_fwd_bwd_cached_weights_us": round(cached_us, 1),
                      "gemm_total_us": round(tot_us, 1), "gemm_TFLOPs": round(tot_fl / tot_us / 1e6, 1),
                      "per_gemm": per}
         del layer, moe, dy
@@ -235,41 +303,98 @@ def supplementary_gemm(m, torch, reps=5):
     return res
 
 
-def cpu_baseline(rows=256):
-    """The CPU oracle (single-threaded C, fp64) over a bounded sample: the
-    first `rows` rows of every cell of the step (same byte model)."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(rows1=2048, rows_per_thread=1024, gemm_rows=64):
+    """The CPU oracle (plain C in fp64, one element at a time) over a bounded
+    sample of the step's workload: forward both + backward both of stress-
+    structured rows of width 8192 (the same generators, at a smaller height),
+    on one host thread, then on every host core the process may use (32-row
+    stripes handed to a thread pool; the oracle's C calls release the GIL).
+    Also the oracle's grouped GEMM on an FC2-shaped slice (gemm_rows rows of
+    one expert, N = 2048, K = 768, MXFP8)."""
+    from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle as O
     import workloads as W
-    total_bytes = 0.0
+    K = STRESS[1]
+    cores = min(16, len(os.sched_getaffinity(0)))   # a GPU's share of the host
+
+    def sample(rows):
+        gu, sc, dy = W.stress_inputs(rows, K, seed=0, frac=1e-3)
+        return W.bf16_bits(dy), W.bf16_bits(gu[:, :K]), W.bf16_bits(gu[:, K:]), sc.numpy()
+
+    def run(part):
+        d, g, u, s = part
+        O.swiglu_quantize_fwd(g, u, s, 3)
+        O.swiglu_quantize_bwd(d, g, u, s, 3)
+
+    per_row = fwd_bytes(1, K, 2) + bwd_bytes(1, K, 2)
+    d, g, u, s = sample(rows1)
     t0 = time.perf_counter()
-    for (M, K) in SHAPES:
-        gu = W.packed_gate_up(rows, K, seed=0)
-        sc = W.row_scale(rows, seed=0).numpy()
-        dy = W.bf16_bits(W.grad_out(rows, K, seed=0))
-        g, u = W.bf16_bits(gu[:, :K]), W.bf16_bits(gu[:, K:])
-        for _, d in DIRS:
-            O.swiglu_quantize_fwd(g, u, sc, d)
-            O.swiglu_quantize_bwd(dy, g, u, sc, d)
-            total_bytes += fwd_bytes(rows, K, ndir(d)) + bwd_bytes(rows, K, ndir(d))
-    dt = time.perf_counter() - t0
-    _ = np
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} rows of each of the 18 fused fwd/bwd cells "
-                      f"({total_bytes / 1e6:.1f} MB algorithmic), {dt:.1f} s on 1 host thread"}
+    run((d, g, u, s))
+    t1 = time.perf_counter() - t0
+    rows_n = rows_per_thread * cores
+    d, g, u, s = sample(rows_n)
+    parts = [(d[i:i + 32], g[i:i + 32], u[i:i + 32], s[i:i + 32]) for i in range(0, rows_n, 32)]
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(run, parts))
+        tn = time.perf_counter() - t0
+    # the oracle's GEMM: FC2 forward of one expert, MXFP8 NT
+    rng = np.random.default_rng(0)
+    N, KK = 2048, 768
+    A = rng.integers(0, 0x70, (gemm_rows, KK)).astype(np.uint8)
+    As = np.full((gemm_rows, KK // 32), 120, np.uint8)
+    B = rng.integers(0, 0x70, (N, KK)).astype(np.uint8)
+    Bs = np.full((N, KK // 32), 120, np.uint8)
+    opB = O.Operand("mxfp8", B, 0, KK, 1, Bs, 0, KK // 32, 1)
+    t0 = time.perf_counter()
+    O.grouped_gemm("m", np.array([0, gemm_rows]), 0, N, KK, O.Operand("mxfp8", A, 0, KK, 1, As, 0, KK // 32, 1),
+                   opB, "bf16")
+    tg1 = time.perf_counter() - t0
+    stripes = [(A[i:i + 8], As[i:i + 8]) for i in range(0, gemm_rows, 8)]
+    gemm_one = lambda p: O.grouped_gemm("m", np.array([0, len(p[0])]), 0, N, KK,
+                                        O.Operand("mxfp8", p[0], 0, KK, 1, p[1], 0, KK // 32, 1), opB, "bf16")
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(gemm_one, stripes))
+        tgn = time.perf_counter() - t0
+    gfl = 2.0 * gemm_rows * N * KK
+    return {"value": round(rows_n * per_row / tn / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fused fwd both + bwd both over stress-structured rows of width {K}: {rows_n} rows "
+                       f"({rows_n * per_row / 1e6:.0f} MB algorithmic) on {cores} threads in {tn:.1f} s; "
+                       f"{rows1} rows on 1 thread in {t1:.1f} s"),
+            "single_thread": {"value": round(rows1 * per_row / t1 / 1e9, 4), "unit": "GB/s", "cores": 1},
+            "nproc": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model(),
+            "gemm_oracle": {"shape": f"FC2 forward slice: {gemm_rows} x {N} x {KK} MXFP8",
+                            "TFLOPs_1_thread": round(gfl / tg1 / 1e12, 8),
+                            f"TFLOPs_{cores}_threads": round(gfl / tgn / 1e12, 8)}}
 
 
 # ------------------------------------------------------------------ GEMM profile summary
 # `--summarize-gemm-profile DIR`: the per-GEMM table of the grouped-GEMM
 # profile from a rocprofv3 kernel trace (DIR/trace) and TCC_HIT/TCC_MISS
-# (DIR/tcc) and FETCH_SIZE (DIR/fetch) counter runs of `--moe-only`, which
-# runs, per routing, three forward+backward layers and then each of the six
-# grouped GEMMs three times, always in the order FC1, FC2, FC2 dgrad, FC2
-# wgrad, FC1 dgrad, FC1 wgrad; the GEMM dispatches are labelled from that order.
+# (DIR/tcc) and FETCH_SIZE (DIR/fetch) counter runs of `--moe-only`.
+# Dispatches are labelled by the kernel's template arguments (mode, dtype):
+# NT bf16 is FC1 forward and NT MXFP8 FC2 forward; the NN (dgrad) and TN
+# (wgrad) launches of FC2 and FC1 share a template, and `--moe-only` issues
+# them in a fixed interleaving that the labeller checks dispatch by dispatch
+# (a run in any other order stops with an error instead of mislabelling).
 
 GP_ORDER = ["FC1 forward", "FC2 forward", "FC2 dgrad", "FC2 wgrad", "FC1 dgrad", "FC1 wgrad"]
 GP_MODE = {"FC1 forward": "NT bf16", "FC2 forward": "NT MXFP8", "FC2 dgrad": "NN MXFP8", "FC2 wgrad": "TN MXFP8",
            "FC1 dgrad": "NN MXFP8", "FC1 wgrad": "TN MXFP8"}
+GP_TEMPLATE = {"FC1 forward": "0, 0", "FC2 forward": "0, 1", "FC2 dgrad": "1, 1", "FC2 wgrad": "2, 1",
+               "FC1 dgrad": "1, 1", "FC1 wgrad": "2, 1"}
 _FC1, _FC2 = 2 * 65536 * 2 * 768 * 2048, 2 * 65536 * 2048 * 768   # 65,536 routed rows, hidden 2048, intermediate 768
 GP_FL = {"FC1 forward": _FC1, "FC2 forward": _FC2, "FC2 dgrad": _FC2, "FC2 wgrad": _FC2, "FC1 dgrad": _FC1,
          "FC1 wgrad": _FC1}
@@ -278,29 +403,51 @@ GP_BY = {"FC1 forward": 1275e6, "FC2 forward": 528e6, "FC2 dgrad": 447e6, "FC2 w
          "FC1 wgrad": 1048e6}
 GP_PEAK = {"NT bf16": 2500.0}
 GP_FETCH_SCALE = 2.0   # FETCH_SIZE calibration against a plain copy of known size
+MOE_ONLY_REPS = 2
 
 
-def _gemm_labels(ids):
-    per_routing = 6 * 3 + 6 * 3
+def _expected_gemm_sequence():
+    """GEMM labels in the order `--moe-only` dispatches them: per routing, one
+    untimed layer, MOE_ONLY_REPS timed layers and MOE_ONLY_REPS timed layers
+    with the weight cache valid (each the six GEMMs in layer order), then
+    each GEMM once untimed and MOE_ONLY_REPS times timed."""
+    one = []
+    for _ in range(1 + 2 * MOE_ONLY_REPS):
+        one += GP_ORDER
+    for g in GP_ORDER:
+        one += [g] * (1 + MOE_ONLY_REPS)
+    return one * len(MOE_VARIANTS)
+
+
+def _gemm_labels(rows):
+    """Dispatch id -> GEMM label for the gemm_kernel rows of a trace (any
+    order); checks every dispatch's template arguments against its label."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    seq = _expected_gemm_sequence()
+    if len(rows) != len(seq):
+        raise SystemExit(f"GEMM profile: {len(rows)} gemm_kernel dispatches, expected {len(seq)}")
     out = {}
-    for k, d in enumerate(ids):
-        j = k % per_routing
-        out[d] = GP_ORDER[j % 6] if j < 18 else GP_ORDER[(j - 18) // 3]
+    for r, lab in zip(rows, seq):
+        t = re.search(r"gemm_kernel<(\d+), (\d+),", r["Kernel_Name"])
+        if t is None or f"{t.group(1)}, {t.group(2)}" != GP_TEMPLATE[lab]:
+            raise SystemExit(f"GEMM profile: dispatch {r['Dispatch_Id']} ({r['Kernel_Name'][:60]}) is not {lab}")
+        out[int(r["Dispatch_Id"])] = lab
     return out
 
 
 def summarize_gemm_profile(base):
     tr = [r for r in csv.DictReader(open(f"{base}/trace/moe_kernel_trace.csv")) if "gemm_kernel" in r["Kernel_Name"]]
-    tr.sort(key=lambda r: int(r["Start_Timestamp"]))
-    lab = _gemm_labels([int(r["Dispatch_Id"]) for r in tr])
+    lab = _gemm_labels(tr)
     dur = collections.defaultdict(list)
     for r in tr:
         dur[lab[int(r["Dispatch_Id"])]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
 
     def counters(path, names):
         rows = [r for r in csv.DictReader(open(path)) if "gemm_kernel" in r["Kernel_Name"]]
-        disp = sorted({int(r["Dispatch_Id"]) for r in rows})
-        lb = _gemm_labels(disp)
+        first = {}
+        for r in rows:
+            first.setdefault(int(r["Dispatch_Id"]), r)
+        lb = _gemm_labels(list(first.values()))
         acc = collections.defaultdict(lambda: collections.defaultdict(float))
         for r in rows:
             if r["Counter_Name"] in names:
@@ -332,17 +479,33 @@ def summarize_gemm_profile(base):
               f" {ai:.0f} | {att:.0f} | {100 * tf / att:.1f} | {100 * hits:.1f} % | {mb:.0f} |" + busy)
 
 
+def time_cell(torch, m, c, flush, reps):
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        flush.zero_()   # evict the 256 MB Infinity Cache and the L2s
+        e0.record(stream)
+        m.check(c.fn())
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    p10, p50, p90 = percentiles(ts)
+    return {"us": round(p50, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+            "GBps": round(c.bytes / p50 / 1e3, 1), "pct_hbm": round(c.bytes / p50 / 1e3 / HBM_PEAK_GBS * 100, 1)}
+
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-moe", action="store_true", help="skip the expert-layer (grouped GEMM) section")
+    ap.add_argument("--no-cells", action="store_true", help="skip the per-cell record")
+    ap.add_argument("--cell-reps", type=int, default=10)
     ap.add_argument("--moe-only", action="store_true",
                     help="only run the expert-layer section once and print its record (for profiling the GEMMs)")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--summarize-gemm-profile", metavar="DIR",
                     help="print the per-GEMM table of a --moe-only profile (CPU only, no GPU run)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -362,9 +525,10 @@ def main():
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.moe_only:
-        print(json.dumps({"gemm": moe_section(m, torch, W, reps=2)}), flush=True)
+        print(json.dumps({"gemm": moe_section(m, torch, W, reps=MOE_ONLY_REPS)}), flush=True)
         return
-    cells, _data = build_cells(m, torch, W)
+    data = make_data(torch, W, [STRESS])
+    cells = [Cell(m, torch, data, k, dn, dict(DIRS)[dn], sh, mo) for (k, dn, sh, mo) in STEP_CELLS]
     stream = torch.cuda.current_stream()
     dom = [c for c in cells if c.key() == DOMINANT][0]
     if args.traffic_probe:
@@ -391,6 +555,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    print(f"bench: {args.warmup} warm-up steps done", file=sys.stderr, flush=True)
 
     # the timed region: exactly `steps` steps, synchronized on both sides;
     # the dominant kernel is bracketed by events on its own stream
@@ -402,31 +567,17 @@ def main():
         step(dom_ev[i])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    dom_us = sum(a.elapsed_time(b) for a, b in dom_ev) / args.steps * 1e3
+    dom_ts = [a.elapsed_time(b) * 1e3 for a, b in dom_ev]
+    dom_us = sum(dom_ts) / args.steps
+    clocks = gpu_clocks()
+    print(f"bench: {args.steps} timed steps done", file=sys.stderr, flush=True)
 
     step_bytes = sum(c.bytes for c in cells)
     ms_per_step = dt / args.steps * 1e3
     value = step_bytes / (dt / args.steps) / 1e9
-
-    # per-cell device times (outside the timed region, for the record)
-    per_cell = {}
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    for c in cells:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ts = []
-        for _ in range(3):
-            flush.zero_()   # evict the 256 MB Infinity Cache and the L2s
-            e0.record(stream)
-            m.check(c.fn())
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        us = sorted(ts)[1]
-        per_cell[f"{c.kind}.{c.dname}.{c.shape[0]}x{c.shape[1]}"] = {
-            "us": round(us, 2), "GBps": round(c.bytes / us / 1e3, 1)}
-
     achieved = dom.bytes / dom_us / 1e3
     traffic = measured_traffic()
+    p10, p50, p90 = percentiles(dom_ts)
     out = {
         "metric": "fused SwiGLU+MXFP8 quant GB/s (% HBM peak); grouped GEMM TFLOP/s",
         "value": round(value, 1),
@@ -440,23 +591,39 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "fused row-scaled SwiGLU + MXFP8 fwd and bwd, rowwise/colwise/both, "
-                               "gate/up (4096,2048), (4096,7168), (16384,7168), packed [gate|up]",
-                   "cells": len(cells), "step_bytes": int(step_bytes),
+        "config": {"workload": "bandwidth stress: fused row-scaled SwiGLU + MXFP8 forward and backward, both "
+                               "directions, gate/up (131072, 8192) packed [gate|up], 0.1% zero and 0.1% outlier "
+                               "32-blocks; the backward also writes bf16 dgate/dup and fp32 dscale",
+                   "cells": [c.label() for c in cells], "step_bytes": int(step_bytes),
                    "pct_hbm_peak": round(value / HBM_PEAK_GBS * 100, 1)},
-        "roofline": {"kernel": "mxq_swiglu_quantize_bwd both (16384,7168)", "bound": "hbm",
+        "roofline": {"kernel": "mxq_swiglu_quantize_bwd both (131072, 8192)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": int(dom.bytes), "avg_launch_us": round(dom_us, 2)},
-        "per_cell": per_cell,
+                     "bytes_per_launch": int(dom.bytes), "avg_launch_us": round(dom_us, 2),
+                     "p10_launch_us": round(p10, 2), "p90_launch_us": round(p90, 2)},
+        "clocks": clocks,
     }
-    del cells, _data, flush, dom
+    del cells, dom
+    torch.cuda.empty_cache()
+    if not args.no_cells:
+        data.update(make_data(torch, W, C2_SHAPES))
+        rec = record_cells(m, torch, data)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        per_cell = {}
+        for c in rec:
+            m.check(c.fn())
+            per_cell[c.label()] = time_cell(torch, m, c, flush, args.cell_reps)
+        out["per_cell"] = per_cell
+        del rec, flush
+        print("bench: per-cell record done", file=sys.stderr, flush=True)
+    del data
     torch.cuda.empty_cache()
     if not args.no_moe:
         out["gemm"] = moe_section(m, torch, W)
         out["gemm_supplementary"] = supplementary_gemm(m, torch)
+        print("bench: grouped GEMM record done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 

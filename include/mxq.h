@@ -207,6 +207,25 @@ mxq_status mxq_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x,
                         const mxq_mx_out *row_out, const mxq_mx_out *col_out,
                         void *stream);
 
+/*
+ * Graph-safe quantization into reused outputs (TE3224, Greptile Summary: the
+ * grouped quantization of the expert weights fills a cached output in place
+ * and takes a no-op flag, so that a captured weight quantization can be
+ * replayed with unchanged pointers; TE2600, review discussion: an optional
+ * no-op tensor for graph capture).  The same computation and layouts as
+ * mxq_quantize, into the caller-owned outputs given, except that when
+ * noop_flag is non-NULL and the device int32 it points to is non-zero when the
+ * kernel runs, the call writes nothing and leaves every output as it was (the
+ * flag is read on the device, so the host never synchronizes and a graph that
+ * holds the call replays correctly whatever the flag holds at replay time).
+ *   noop_flag  device int32, 4-byte aligned, or NULL (then as mxq_quantize);
+ *              an input: no output may overlap it
+ */
+mxq_status mxq_quantize_noop(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x,
+                             const mxq_groups *groups, uint32_t dirs,
+                             const mxq_mx_out *row_out, const mxq_mx_out *col_out,
+                             const int32_t *noop_flag, void *stream);
+
 /* ------------------------------------------------------------ grouped GEMM */
 
 typedef enum { MXQ_DTYPE_BF16 = 0, MXQ_DTYPE_MXFP8_E4M3 = 1, MXQ_DTYPE_F32 = 2 } mxq_dtype;

@@ -39,7 +39,8 @@ GEMM_TN = 2
 # every symbol include/mxq.h declares
 EXPORTS = [
     "mxq_splits_to_offsets", "mxq_swiglu_quantize_fwd", "mxq_swiglu_quantize_bwd_workspace",
-    "mxq_swiglu_quantize_bwd", "mxq_quantize", "mxq_grouped_gemm_workspace", "mxq_grouped_gemm",
+    "mxq_swiglu_quantize_bwd", "mxq_quantize", "mxq_quantize_noop", "mxq_grouped_gemm_workspace",
+    "mxq_grouped_gemm",
     "mxq_status_string", "mxq_last_error_message", "mxq_version",
 ]
 
@@ -95,6 +96,8 @@ def _load():
                                     ctypes.c_size_t, P],
         "mxq_quantize": [I64, I64, P, I64, ctypes.POINTER(mxq_groups), U32,
                          ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P],
+        "mxq_quantize_noop": [I64, I64, P, I64, ctypes.POINTER(mxq_groups), U32,
+                              ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P, P],
         "mxq_grouped_gemm_workspace": [ctypes.POINTER(mxq_gemm_args), ctypes.POINTER(ctypes.c_size_t)],
         "mxq_grouped_gemm": [ctypes.POINTER(mxq_gemm_args), P, ctypes.c_size_t, P],
     }
@@ -214,6 +217,12 @@ def mxq_quantize(x, groups, dirs, row_out, col_out, stream=None):
                             _byref(col_out), _stream(stream))
 
 
+def mxq_quantize_noop(x, groups, dirs, row_out, col_out, noop_flag, stream=None):
+    M, K = x.shape
+    return lib.mxq_quantize_noop(M, K, _ptr(x), _ld(x), _byref(groups), dirs, _byref(row_out),
+                                 _byref(col_out), _ptr(noop_flag), _stream(stream))
+
+
 def mxq_grouped_gemm_workspace(args):
     n = ctypes.c_size_t(0)
     check(lib.mxq_grouped_gemm_workspace(ctypes.byref(args), ctypes.byref(n)))
@@ -281,6 +290,17 @@ def quantize(x, rowwise=True, colwise=False, row_off=None, block_off=None, n_col
     ro, co = _outs(rc, cc, rs, cs, dirs)
     check(mxq_quantize(x, make_groups(row_off, block_off), dirs, ro, co, stream))
     return rc, cc, rs, cs
+
+
+def quantize_into(x, codes_row, codes_col, scales_row, scales_col, noop_flag=None, row_off=None,
+                  block_off=None, stream=None):
+    """Quantize x into caller-owned outputs (a direction is enabled when its
+    codes tensor is given); with noop_flag (a device int32 tensor) the launch
+    does nothing while the flag holds a non-zero value."""
+    dirs = (ROWWISE if codes_row is not None else 0) | (COLWISE if codes_col is not None else 0)
+    ro = make_mx_out(codes_row, scales_row) if codes_row is not None else None
+    co = make_mx_out(codes_col, scales_col) if codes_col is not None else None
+    check(mxq_quantize_noop(x, make_groups(row_off, block_off), dirs, ro, co, noop_flag, stream))
 
 
 def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False, row_off=None,

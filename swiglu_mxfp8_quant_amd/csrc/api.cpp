@@ -281,6 +281,32 @@ mxq_status mxq_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, c
     return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_quantize launch");
 }
 
+mxq_status mxq_quantize_noop(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, const mxq_groups *groups,
+                             uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out,
+                             const int32_t *noop_flag, void *stream) {
+    if (noop_flag != nullptr && !aligned(noop_flag, 4)) return fail(MXQ_ERR_ALIGN, "noop_flag must be 4-byte aligned");
+    mxq::FwdArgs a{};
+    bool noop;
+    mxq_status s = prepare_fwd(a, mxq::ACT_IDENTITY, 0.0f, M, K, x, ld_x, nullptr, 0, nullptr, groups, dirs, row_out,
+                               col_out, &noop);
+    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
+    if (noop_flag != nullptr) {
+        // the flag is an input: no output may overlap it
+        std::vector<Range> outs;
+        if (dirs & 1) {
+            outs.push_back(range2d(row_out->codes, M, K, row_out->ld_codes, 1, "row codes"));
+            outs.push_back(range2d(row_out->scales, M, K / 32, row_out->ld_scales, 1, "row scales"));
+        }
+        if (dirs & 2) {
+            outs.push_back(range2d(col_out->codes, M, K, col_out->ld_codes, 1, "col codes"));
+            outs.push_back(range2d(col_out->scales, (M + 31) / 32, K, col_out->ld_scales, 1, "col scales"));
+        }
+        if ((s = check_alias({range2d(noop_flag, 1, 1, 1, 4, "noop_flag")}, outs)) != MXQ_OK) return s;
+    }
+    a.noop = noop_flag;
+    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_quantize_noop launch");
+}
+
 mxq_status mxq_swiglu_quantize_bwd_workspace(int64_t M, int64_t K, uint32_t dirs, size_t *bytes) {
     (void)dirs;
     if (bytes == nullptr) return fail(MXQ_ERR_NULL, "bytes is NULL");

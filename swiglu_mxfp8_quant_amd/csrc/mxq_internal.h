@@ -35,6 +35,7 @@ struct FwdArgs {
     Groups groups;
     unsigned dirs;
     MxOut row, col;
+    const int32_t *noop;                     // device flag or NULL: non-zero => the launch does nothing
 };
 
 struct BwdArgs {
@@ -60,6 +61,7 @@ hipError_t launch_splits_to_offsets(const int64_t *splits, int64_t G, int64_t *r
 hipError_t launch_act_quant_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_act_quant_bwd(const BwdArgs &a, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t M, int64_t K);
+
 // Work-items of the fused launch for these sizes (an upper bound when grouped;
 // HIP needs grid x block below 2^32).
 int64_t act_quant_launch_threads(int64_t M, int64_t K, int64_t G, bool grouped_colwise, bool backward);

@@ -7,7 +7,9 @@ optimizations" (Sequence Diagram: grouped FC1, the fused row-scaled SwiGLU
 with MXFP8 quantization, grouped FC2; backward: quantized dY, FC2 dgrad and
 wgrad, the fused dSwiGLU with the routing-weight gradient, FC1 dgrad and
 wgrad); NVIDIA/TransformerEngine pull 3224 (Greptile Summary: one grouped GEMM
-over the experts' row groups with device-side offsets).
+over the experts' row groups with device-side offsets; the MXFP8 weights
+cached in place and re-quantized under a device no-op flag, so a captured
+step replays with unchanged pointers).
 
 Layouts (R routed rows sorted by expert, H hidden, I expert intermediate,
 G experts):
@@ -19,38 +21,19 @@ rowwise and colwise (per expert); Y = FC2(A) (R, H) bf16.
 Backward from dY (R, H): dA = dY . W2_g (MXFP8 NN), dW2_g = dY_g^T A_g (MXFP8
 TN), [dgate | dup], dscale and MXFP8 dact from the fused backward,
 dX = dact . W13_g (MXFP8 NN), dW13_g = dact_g^T X_g (MXFP8 TN).
+The MXFP8 weights (W2 rowwise along I and colwise along H, W13 colwise along
+2I) live in buffers the layer owns and are re-quantized in place on every
+call unless the layer's device flag says the cache holds the current weights.
 """
 import torch
 
-from . import (GEMM_NN, GEMM_NT, GEMM_TN, grouped_gemm, quantize, splits_to_offsets,
+from . import (GEMM_NN, GEMM_NT, GEMM_TN, grouped_gemm, quantize, quantize_into, splits_to_offsets,
                swiglu_quantize_bwd, swiglu_quantize_fwd)
 
 
 def weight_offsets(G, rows, device):
     """Device offsets of G equal groups of `rows` rows (a stacked weight)."""
     return splits_to_offsets(torch.full((G,), rows, dtype=torch.int64, device=device))[:2]
-
-
-def quantize_weight_both(w, offs):
-    """(G, K, N) bf16 -> rowwise codes (G, K, N) and scales (G, K, N/32) (1x32
-    blocks along N, for a contraction over N), and colwise codes (G, K, N) and
-    scales (G, K/32, N) (32x1 blocks along each expert's K rows, for a
-    contraction over K), from one read of the weight."""
-    G, K, N = w.shape
-    ro, bo = offs
-    rc, cc, rs, cs = quantize(w.reshape(G * K, N), rowwise=True, colwise=True, row_off=ro, block_off=bo,
-                              n_col_blocks=G * K // 32)
-    return rc.view(G, K, N), rs.view(G, K, N // 32), cc.view(G, K, N), cs.view(G, K // 32, N)
-
-
-def quantize_weight_colwise(w, offs):
-    """(G, K, N) bf16 -> codes (G, K, N), scales (G, K/32, N): 32x1 blocks
-    along each expert's K rows (K a multiple of 32)."""
-    G, K, N = w.shape
-    ro, bo = offs
-    _, cc, _, cs = quantize(w.reshape(G * K, N), rowwise=False, colwise=True, row_off=ro, block_off=bo,
-                            n_col_blocks=G * K // 32)
-    return cc.view(G, K, N), cs.view(G, K // 32, N)
 
 
 class Layer:
@@ -63,6 +46,40 @@ class Layer:
         self.I = self.I2 // 2
         self.clamped, self.limit = clamped, limit
         self.row_off, self.block_off, self.err = splits_to_offsets(splits)
+        G, H, I, dev = self.G, self.H, self.I, w13.device
+        u8 = dict(dtype=torch.uint8, device=dev)
+        # the MXFP8 weight cache: W2 rowwise (1x32 along I, for FC2) and
+        # colwise (32x1 along each expert's H rows, for FC2's dgrad); W13
+        # colwise (32x1 along each expert's 2I rows, for FC1's dgrad)
+        self.w2q, self.w2s = torch.empty((G, H, I), **u8), torch.empty((G, H, I // 32), **u8)
+        self.w2c, self.w2cs = torch.empty((G, H, I), **u8), torch.empty((G, H // 32, I), **u8)
+        self.w13c, self.w13cs = torch.empty((G, 2 * I, H), **u8), torch.empty((G, 2 * I // 32, H), **u8)
+        self.w2_offs = weight_offsets(G, H, dev)
+        self.w13_offs = weight_offsets(G, 2 * I, dev)
+        # device flag: non-zero = the cache holds the current weights (the
+        # quantizations then do nothing); read by the kernels, never the host
+        self.weights_current = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def mark_weights_changed(self):
+        """The next forward / backward re-quantize the weights into the cache."""
+        self.weights_current.zero_()
+
+    def mark_weights_current(self):
+        """The cache holds the current weights (after a forward and a backward
+        since they last changed): the quantizations are skipped on the device."""
+        self.weights_current.fill_(1)
+
+    def _quantize_w2(self):
+        G, H, I = self.G, self.H, self.I
+        quantize_into(self.w2.reshape(G * H, I), self.w2q.view(G * H, I), self.w2c.view(G * H, I),
+                      self.w2s.view(G * H, I // 32), self.w2cs.view(G * H // 32, I),
+                      noop_flag=self.weights_current, row_off=self.w2_offs[0], block_off=self.w2_offs[1])
+
+    def _quantize_w13(self):
+        G, H, I = self.G, self.H, self.I
+        quantize_into(self.w13.reshape(G * 2 * I, H), None, self.w13c.view(G * 2 * I, H), None,
+                      self.w13cs.view(G * 2 * I // 32, H), noop_flag=self.weights_current,
+                      row_off=self.w13_offs[0], block_off=self.w13_offs[1])
 
     def forward(self, x_perm, scale):
         R, I, H = x_perm.shape[0], self.I, self.H
@@ -73,13 +90,13 @@ class Layer:
         a_r, a_c, as_r, as_c = swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, rowwise=True, colwise=True,
                                                    row_off=ro, block_off=bo, clamped=self.clamped,
                                                    limit=self.limit)
-        # W2 in both directions from one read: rowwise along I for FC2, and
-        # colwise along H (per expert) for FC2's dgrad in the backward
-        w2q, w2s, w2c, w2cs = quantize_weight_both(self.w2, weight_offsets(self.G, H, dev))
+        # W2 in both directions from one read (the colwise copy is kept for
+        # the backward's FC2 dgrad)
+        self._quantize_w2()
         y = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
-        grouped_gemm(GEMM_NT, ro, a_r, w2q, y, as_r, w2s)
+        grouped_gemm(GEMM_NT, ro, a_r, self.w2q, y, as_r, self.w2s)
         self.saved = dict(x_perm=x_perm, scale=scale, h13=h13, a_r=a_r, a_c=a_c, as_r=as_r, as_c=as_c,
-                          w2q=w2q, w2s=w2s, w2c=w2c, w2cs=w2cs)
+                          w2q=self.w2q, w2s=self.w2s, w2c=self.w2c, w2cs=self.w2cs)
         return y
 
     def backward(self, dy):
@@ -97,7 +114,8 @@ class Layer:
         dq_r, dq_c, dqs_r, dqs_c, dd, dscale = swiglu_quantize_bwd(
             da, h13[:, :I], h13[:, I:], s["scale"], rowwise=True, colwise=True, row_off=ro, block_off=bo,
             clamped=self.clamped, limit=self.limit)
-        w13c, w13cs = quantize_weight_colwise(self.w13, weight_offsets(G, 2 * I, dev))
+        self._quantize_w13()
+        w13c, w13cs = self.w13c, self.w13cs
         dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         grouped_gemm(GEMM_NN, ro, dq_r, w13c, dx, dqs_r, w13cs)
         _, x_c, _, xs_c = quantize(s["x_perm"], rowwise=False, colwise=True, row_off=ro, block_off=bo)

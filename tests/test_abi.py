@@ -144,6 +144,20 @@ def test_quantize_validation(m):
     assert lib.mxq_quantize(64, 64, fake(0), 64, None, 3, ctypes.byref(row), None, None) == 1
 
 
+def test_quantize_noop_validation(m):
+    """The no-op flag must be 4-byte aligned and must not overlap an output
+    (it is an input); the rest is validated as mxq_quantize does."""
+    lib = m.lib
+    row = m.mxq_mx_out(BASE + (4 << 24), 64, BASE + (5 << 24), 2)
+    assert lib.mxq_quantize_noop(64, 64, fake(0), 64, None, 1, ctypes.byref(row), None, fake((6 << 24) + 2),
+                                 None) == 3
+    assert lib.mxq_quantize_noop(64, 64, fake(0), 64, None, 1, ctypes.byref(row), None, fake((4 << 24) + 64),
+                                 None) == 5
+    assert lib.mxq_quantize_noop(64, 64, fake(0), 64, None, 1, ctypes.byref(row), None, fake((5 << 24) + 4),
+                                 None) == 5
+    assert lib.mxq_quantize_noop(64, 33, fake(0), 64, None, 1, ctypes.byref(row), None, fake(6 << 24), None) == 2
+
+
 def gemm_args(m, mode, M=256, N=256, K=256, G=4, max_wg=0):
     """MXFP8 grouped-GEMM arguments over fake, disjoint, aligned device ranges."""
     f8 = m.DTYPE_MXFP8
