@@ -31,7 +31,9 @@
  *   - Inputs are never written (VEO1340, Design & Code Changes: no input
  *     mutation); an output range that overlaps an input range is rejected.
  *   - Thread-safe: the library holds no mutable global state except the
- *     thread-local error text.
+ *     thread-local error text, and the per-GPU scratch of the one
+ *     allocation-free entry point (mxq_swiglu_quantize_bwd_noalloc), whose
+ *     calls on one GPU the caller must not overlap.
  *
  * Number formats (TAO4743, Summary and Numerics and tests)
  *   - E4M3 is the OCP FP8 "fn" format: bias 7, max finite 448, no infinities,
@@ -195,6 +197,29 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K,
                                    uint32_t dirs, const mxq_mx_out *row_out,
                                    const mxq_mx_out *col_out, void *ws, size_t ws_bytes,
                                    void *stream);
+
+/*
+ * mxq_swiglu_quantize_bwd for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, arguments and results, with no workspace argument.  The
+ * dscale partial sums go to a scratch array built into the library, 16 MiB
+ * per GPU (held until the process ends), which covers M * ceil(K / 512) <=
+ * 4,194,304 (e.g. M = 131072 at K = 8192); a larger call with dscale != NULL
+ * returns MXQ_ERR_WORKSPACE before touching the device.  Every call on one
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (two streams,
+ * two threads) race on it and must be ordered by the caller.  The stream must
+ * belong to the calling thread's current device.  Nothing is allocated or
+ * freed.
+ */
+mxq_status mxq_swiglu_quantize_bwd_noalloc(const mxq_act *act, int64_t M, int64_t K,
+                                           const uint16_t *grad, int64_t ld_grad,
+                                           const uint16_t *gate, int64_t ld_gate,
+                                           const uint16_t *up, int64_t ld_up,
+                                           const float *row_scale, const mxq_groups *groups,
+                                           uint16_t *dgate, int64_t ld_dgate,
+                                           uint16_t *dup, int64_t ld_dup, float *dscale,
+                                           uint32_t dirs, const mxq_mx_out *row_out,
+                                           const mxq_mx_out *col_out, void *stream);
 
 /*
  * Plain MXFP8 block quantization of a bf16 (M x K) matrix (TAO4743, Summary:

@@ -39,7 +39,8 @@ GEMM_TN = 2
 # every symbol include/mxq.h declares
 EXPORTS = [
     "mxq_splits_to_offsets", "mxq_swiglu_quantize_fwd", "mxq_swiglu_quantize_bwd_workspace",
-    "mxq_swiglu_quantize_bwd", "mxq_quantize", "mxq_quantize_noop", "mxq_grouped_gemm_workspace",
+    "mxq_swiglu_quantize_bwd", "mxq_swiglu_quantize_bwd_noalloc", "mxq_quantize", "mxq_quantize_noop",
+    "mxq_grouped_gemm_workspace",
     "mxq_grouped_gemm",
     "mxq_status_string", "mxq_last_error_message", "mxq_version",
 ]
@@ -94,6 +95,9 @@ def _load():
                                     ctypes.POINTER(mxq_groups), P, I64, P, I64, P, U32,
                                     ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P,
                                     ctypes.c_size_t, P],
+        "mxq_swiglu_quantize_bwd_noalloc": [ctypes.POINTER(mxq_act), I64, I64, P, I64, P, I64, P, I64, P,
+                                            ctypes.POINTER(mxq_groups), P, I64, P, I64, P, U32,
+                                            ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P],
         "mxq_quantize": [I64, I64, P, I64, ctypes.POINTER(mxq_groups), U32,
                          ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P],
         "mxq_quantize_noop": [I64, I64, P, I64, ctypes.POINTER(mxq_groups), U32,
@@ -209,6 +213,16 @@ def mxq_swiglu_quantize_bwd(act, grad, gate, up, row_scale, groups, dgate, dup, 
         _ptr(dup), _ld(dup) if dup is not None else 0, _ptr(dscale), dirs, _byref(row_out),
         _byref(col_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
+
+
+def mxq_swiglu_quantize_bwd_noalloc(act, grad, gate, up, row_scale, groups, dgate, dup, dscale, dirs,
+                                    row_out, col_out, stream=None):
+    M, K = gate.shape
+    return lib.mxq_swiglu_quantize_bwd_noalloc(
+        _byref(act), M, K, _ptr(grad), _ld(grad), _ptr(gate), _ld(gate), _ptr(up), _ld(up),
+        _ptr(row_scale), _byref(groups), _ptr(dgate), _ld(dgate) if dgate is not None else 0,
+        _ptr(dup), _ld(dup) if dup is not None else 0, _ptr(dscale), dirs, _byref(row_out),
+        _byref(col_out), _stream(stream))
 
 
 def mxq_quantize(x, groups, dirs, row_out, col_out, stream=None):

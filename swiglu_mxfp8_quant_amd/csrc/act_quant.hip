@@ -40,6 +40,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace mxq {
 namespace {
 
@@ -1120,6 +1122,35 @@ int64_t act_quant_launch_threads(int64_t M, int64_t K, int64_t G, bool grouped_c
 size_t bwd_workspace_bytes(int64_t M, int64_t K) {
     const int64_t ns = slabs_of(K);
     return ns > 1 ? (size_t)M * (size_t)ns * sizeof(float) : 0;
+}
+
+// Scratch of the allocation-free backward: the per-(row, column slab) dscale
+// partials, written in full by the backward kernel before the finisher reads
+// them, so nothing needs clearing.  Each GPU the library runs on holds one
+// copy until the process ends; calls that overlap on one GPU race on it.  In
+// host code `scratch` names a host-side stand-in: only the address that
+// hipGetSymbolAddress returns for the current device may reach a kernel.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+size_t bwd_scratch_capacity() { return kScratchBytes; }
+
+hipError_t bwd_scratch(float **ptr) {
+    static std::mutex mu;
+    static float *addr[64] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<float *>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace mxq

@@ -403,6 +403,31 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, con
     return hip_status(mxq::launch_act_quant_bwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_bwd launch");
 }
 
+mxq_status mxq_swiglu_quantize_bwd_noalloc(const mxq_act *act, int64_t M, int64_t K, const uint16_t *grad,
+                                           int64_t ld_grad, const uint16_t *gate, int64_t ld_gate,
+                                           const uint16_t *up, int64_t ld_up, const float *row_scale,
+                                           const mxq_groups *groups, uint16_t *dgate, int64_t ld_dgate,
+                                           uint16_t *dup, int64_t ld_dup, float *dscale, uint32_t dirs,
+                                           const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *stream) {
+    // the size check needs no device; the scratch's address is looked up
+    // only for a call that fits it
+    const size_t need = (dscale != nullptr && M > 0 && K > 0 && K % 32 == 0) ? mxq::bwd_workspace_bytes(M, K) : 0;
+    const size_t cap = mxq::bwd_scratch_capacity();
+    if (need > cap)
+        return fail(MXQ_ERR_WORKSPACE,
+                    "the allocation-free backward needs %zu bytes of scratch for dscale at M = %lld, K = %lld; "
+                    "the library's scratch holds %zu (use mxq_swiglu_quantize_bwd with a workspace)",
+                    need, (long long)M, (long long)K, cap);
+    float *scratch = nullptr;
+    if (need > 0) {
+        const hipError_t e = mxq::bwd_scratch(&scratch);
+        if (e != hipSuccess) return hip_status(e, "mxq_swiglu_quantize_bwd_noalloc scratch lookup");
+    }
+    return mxq_swiglu_quantize_bwd(act, M, K, grad, ld_grad, gate, ld_gate, up, ld_up, row_scale, groups, dgate,
+                                   ld_dgate, dup, ld_dup, dscale, dirs, row_out, col_out, scratch,
+                                   need > 0 ? cap : 0, stream);
+}
+
 // K-grouped launches keep one counter of their dynamic tile order in the
 // workspace (256 bytes keep the allocation's alignment simple).
 static size_t gemm_ws_bytes(const mxq_gemm_args &a) { return a.mode == MXQ_GEMM_TN ? 256 : 0; }

@@ -61,6 +61,11 @@ hipError_t launch_splits_to_offsets(const int64_t *splits, int64_t G, int64_t *r
 hipError_t launch_act_quant_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_act_quant_bwd(const BwdArgs &a, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t M, int64_t K);
+// The allocation-free backward's scratch (a file-scope device array in
+// act_quant.hip): its capacity in bytes, and its device address on the
+// current device (looked up once per device).
+size_t bwd_scratch_capacity();
+hipError_t bwd_scratch(float **ptr);
 
 // Work-items of the fused launch for these sizes (an upper bound when grouped;
 // HIP needs grid x block below 2^32).

@@ -208,3 +208,13 @@ def test_gemm_output_alias_rejected(m):
     endB = (3 << 28) + (4 - 1) * 256 * 256 + (256 - 1) * 256 + 256
     a.out = BASE + endB - 16
     assert lib.mxq_grouped_gemm(ctypes.byref(a), None, 0, None) == 5
+
+
+def test_noalloc_backward_refuses_beyond_its_scratch(m):
+    """The allocation-free backward checks its scratch size before it touches
+    the device: 2^20 rows at K = 8192 need 64 MiB of dscale partials, more than
+    the 16 MiB the library holds."""
+    f = fake(0)
+    st = m.lib.mxq_swiglu_quantize_bwd_noalloc(None, 1 << 20, 8192, f, 16384, f, 16384, f, 16384, None, None,
+                                               None, 0, None, 0, fake(1 << 30), 1, None, None, None)
+    assert st == 8 and "scratch" in m.last_error()
