@@ -13,6 +13,10 @@ Function map (the C file cites the page passage each one follows):
   mx_quantize                 -- the standalone 1x32 / 32x1 block quantizer
   swiglu_fwd / swiglu_bwd     -- the row-scaled (clamped) SwiGLU and its gradient
   swiglu_quantize_fwd/_bwd    -- activation followed by the block quantizer
+  srelu_fwd / srelu_bwd       -- the row-scaled SReLU (squared ReLU) and its gradient
+  srelu_quantize_fwd/_bwd     -- SReLU followed by the block quantizer
+  glu_split / glu_join        -- gate/up interleaved in blocks of B columns
+  swiglu_quantize_bwd_interleaved -- the backward in the interleaved layout
   grouped_gemm                -- brute-force per-group GEMM, fp32 accumulation
 """
 import ctypes
@@ -76,6 +80,10 @@ def _declare(lib):
     lib.oracle_swiglu_bwd.argtypes = [ctypes.c_int, ctypes.c_double, I64, I64, P, I64, P, I64,
                                       P, I64, P, P, I64, P, I64, P, P, P]
     lib.oracle_swiglu_bwd.restype = None
+    lib.oracle_srelu_fwd.argtypes = [I64, I64, P, I64, P, P, P]
+    lib.oracle_srelu_fwd.restype = None
+    lib.oracle_srelu_bwd.argtypes = [I64, I64, P, I64, P, I64, P, P, I64, P, P, P]
+    lib.oracle_srelu_bwd.restype = None
     lib.oracle_grouped_gemm.argtypes = [ctypes.c_int, I64, P, I64, I64, I64,
                                         ctypes.POINTER(_Operand), ctypes.POINTER(_Operand),
                                         P, ctypes.c_int, I64, I64, ctypes.c_int]
@@ -254,6 +262,101 @@ def swiglu_quantize_bwd(grad, gate, up, scale=None, dirs=ROW | COL, row_off=None
     q = mx_quantize(np.concatenate([dg, du], axis=1), dirs, row_off)
     out = (*q, dg, du, ds)
     return (*out, r[3], r[4]) if want_close else out
+
+
+def srelu_fwd(x, scale=None, want_close=False):
+    """h = bf16(bf16(max(x, 0)^2) * s); returns h (uint16) and, optionally, the
+    boundary-closeness flags (uint8, bit0 the square, bit1 h)."""
+    lib = _load()
+    xv = _rowview(x, np.uint16)
+    M, K = xv.shape
+    sc = None if scale is None else _c(scale, np.float32)
+    h = np.zeros((M, K), np.uint16)
+    close = np.zeros((M, K), np.uint8) if want_close else None
+    lib.oracle_srelu_fwd(M, K, _ptr(xv), _ld(xv), _ptr(sc), _ptr(h), _ptr(close))
+    return (h, close) if want_close else h
+
+
+def srelu_bwd(grad, x, scale=None, want_close=False):
+    """Returns (dx, dscale[, close, dscale_tol]) with dx = bf16(dh*s*2*max(x,0))
+    and dscale = fp32(sum_j dh * bf16(max(x,0)^2))."""
+    lib = _load()
+    dh = _rowview(grad, np.uint16)
+    xv = _rowview(x, np.uint16)
+    M, K = xv.shape
+    sc = None if scale is None else _c(scale, np.float32)
+    dx = np.zeros((M, K), np.uint16)
+    ds = np.zeros(M, np.float32)
+    close = np.zeros((M, K), np.uint8) if want_close else None
+    tol = np.zeros(M, np.float64) if want_close else None
+    lib.oracle_srelu_bwd(M, K, _ptr(dh), _ld(dh), _ptr(xv), _ld(xv), _ptr(sc), _ptr(dx), K, _ptr(ds),
+                         _ptr(close), _ptr(tol))
+    return (dx, ds, close, tol) if want_close else (dx, ds)
+
+
+def srelu_quantize_fwd(x, scale=None, dirs=ROW | COL, row_off=None, want_close=False):
+    """Row-scaled SReLU, then the standalone quantizer.
+    Returns (row_codes, col_codes, row_scales, col_scales, h[, close])."""
+    r = srelu_fwd(x, scale, want_close)
+    h, close = r if want_close else (r, None)
+    q = mx_quantize(h, dirs, row_off)
+    return (*q, h, close) if want_close else (*q, h)
+
+
+def srelu_quantize_bwd(grad, x, scale=None, dirs=ROW | COL, row_off=None, want_close=False):
+    """Returns (row_codes, col_codes, row_scales, col_scales, dx, dscale
+    [, close, dscale_tol]); the codes cover the (M, K) matrix dx."""
+    r = srelu_bwd(grad, x, scale, want_close)
+    q = mx_quantize(r[0], dirs, row_off)
+    return (*q, *r)
+
+
+# ------------------------------------------------------- GLU interleaving ---
+# A gated input may hold gate and up interleaved in blocks of B columns:
+# columns [2Bi, 2Bi + B) are gate columns [Bi, Bi + B) and [2Bi + B, 2Bi + 2B)
+# are the matching up columns (page "Activation + GroupedLinear Fusion for MOE
+# and other MOE optimizations", Important Files Changed: the GLU interleave
+# reshaping moves into the scaled SwiGLU kernels; the pages give no block
+# size, so it is a parameter).  B = K is the plain packed [gate | up].
+
+def glu_split(packed, B):
+    """(M, 2K) interleaved with block B -> (gate, up), each (M, K)."""
+    p = np.asarray(packed)
+    M, K2 = p.shape
+    K = K2 // 2
+    assert K % B == 0
+    blocks = p.reshape(M, K // B, 2, B)
+    return (np.ascontiguousarray(blocks[:, :, 0, :].reshape(M, K)),
+            np.ascontiguousarray(blocks[:, :, 1, :].reshape(M, K)))
+
+
+def glu_join(gate, up, B):
+    """(gate, up) (M, K) -> the (M, 2K) layout interleaved with block B."""
+    g, u = np.asarray(gate), np.asarray(up)
+    M, K = g.shape
+    assert K % B == 0 and u.shape == g.shape
+    out = np.empty((M, K // B, 2, B), g.dtype)
+    out[:, :, 0, :] = g.reshape(M, K // B, B)
+    out[:, :, 1, :] = u.reshape(M, K // B, B)
+    return out.reshape(M, 2 * K)
+
+
+def swiglu_quantize_bwd_interleaved(grad, packed, B, scale=None, dirs=ROW | COL, row_off=None,
+                                    kind=SWIGLU, limit=7.0, want_close=False):
+    """The backward on a gated input interleaved with block B: the gradient
+    [dgate | dup] and its MXFP8 form take the input's interleaved layout.
+    Returns (row_codes, col_codes, row_scales, col_scales, d_packed, dscale
+    [, close, dscale_tol]) with d_packed (M, 2K) interleaved."""
+    g, u = glu_split(packed, B)
+    r = swiglu_bwd(grad, g, u, scale, kind, limit, want_close)
+    dg, du, ds = r[:3]
+    d = glu_join(dg, du, B)
+    q = mx_quantize(d, dirs, row_off)
+    out = (*q, d, ds)
+    if want_close:
+        cg, cu = r[3][:, :dg.shape[1]], r[3][:, dg.shape[1]:]
+        out = (*out, glu_join(cg, cu, B), r[4])
+    return out
 
 
 # ----------------------------------------------------------- grouped GEMM ---

@@ -381,6 +381,66 @@ EXPORT void oracle_swiglu_bwd(int kind, double limit, int64_t M, int64_t K,
 }
 
 /* ------------------------------------------------------------------------- */
+/* O2' / O4': the row-scaled SReLU (TE3238, Greptile Summary: the per-row-    */
+/* scaled activations are SReLU, SwiGLU and ClampedSwiGLU; SReLU is unary).   */
+/* The pages print no formula.  Reading: SReLU is the squared ReLU, and its   */
+/* value is rounded to bf16 before the row scale multiplies it, as SwiGLU's   */
+/* activation is (VEO1340: the activation is rounded to its dtype first).     */
+/*   forward:  a = bf16(max(x, 0)^2),  h = bf16(a * s)                        */
+/*   backward: dx = bf16(dh * s * 2 * max(x, 0)),  dscale = fp32(sum_j dh*a)  */
+/* max(x, 0) passes NaN and maps -0 and negative values (-Inf included) to   */
+/* +0; every product below is exact in fp64 (at most 8+8+24+1 significant    */
+/* bits), so each output is one rounding of the exact value.                  */
+/* ------------------------------------------------------------------------- */
+
+static double relu(double x) { return isnan(x) ? x : (x > 0.0 ? x : 0.0); }
+
+/* close (optional, M x K): bit0 = max(x,0)^2 is near a bf16 tie, bit1 = a*s is. */
+EXPORT void oracle_srelu_fwd(int64_t M, int64_t K, const uint16_t *x, int64_t ldx,
+                             const float *scale, uint16_t *h, uint8_t *close)
+{
+    for (int64_t r = 0; r < M; r++) {
+        double s = scale ? (double)scale[r] : 1.0;
+        for (int64_t j = 0; j < K; j++) {
+            double v = relu(oracle_bf16_to_double(x[r * ldx + j]));
+            double t_a = v * v;
+            double a = oracle_bf16_to_double(oracle_double_to_bf16(t_a));
+            double t_h = a * s;
+            h[r * K + j] = oracle_double_to_bf16(t_h);
+            if (close)
+                close[r * K + j] = (uint8_t)(oracle_near_bf16_tie(t_a) | (oracle_near_bf16_tie(t_h) << 1));
+        }
+    }
+}
+
+/* dx written with row stride lddx; close (optional, M x K): bit1 = the exact
+ * dx is near a bf16 tie; dscale_tol (optional, M): 64 * 2^-24 * sum|dh*a| (a
+ * is computed exactly on every path, so no term for a rounding the other way). */
+EXPORT void oracle_srelu_bwd(int64_t M, int64_t K, const uint16_t *grad, int64_t ldgr,
+                             const uint16_t *x, int64_t ldx, const float *scale,
+                             uint16_t *dx, int64_t lddx, float *dscale, uint8_t *close,
+                             double *dscale_tol)
+{
+    for (int64_t r = 0; r < M; r++) {
+        double s = scale ? (double)scale[r] : 1.0;
+        double acc = 0.0, acc_abs = 0.0;
+        for (int64_t j = 0; j < K; j++) {
+            double dh = oracle_bf16_to_double(grad[r * ldgr + j]);
+            double v = relu(oracle_bf16_to_double(x[r * ldx + j]));
+            double a = oracle_bf16_to_double(oracle_double_to_bf16(v * v));
+            double t_dx = dh * s * 2.0 * v;
+            if (dx) dx[r * lddx + j] = oracle_double_to_bf16(t_dx);
+            double term = dh * a;
+            acc += term;
+            acc_abs += fabs(term);
+            if (close) close[r * K + j] = (uint8_t)(oracle_near_bf16_tie(t_dx) << 1);
+        }
+        if (dscale) dscale[r] = (float)acc;
+        if (dscale_tol) dscale_tol[r] = ldexp(64.0, -24) * acc_abs;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* O5: grouped GEMM (TE3224 and TE2600: one grouped GEMM over per-expert      */
 /* groups of rows; TE3238 Sequence Diagram: FC1 forward, dgrad and wgrad).     */
 /* Operands are dequantized exactly (code * 2^(E-127), or the bf16 value);     */

@@ -114,6 +114,25 @@ def test_k_grouped_mxfp8_wgrad(oracle_mod):
     check(C3[0], Av[:33].T @ Bv[:33] + 0.5, "f32")
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_k_grouped_bf16_wgrad(oracle_mod, out_dtype):
+    """The bf16 K-grouped GEMM (the wgrad of the recipe that keeps the weight
+    gradients in bf16): C_g = A_g^T B_g over the rows of group g; an empty
+    group gives zeros."""
+    rng = np.random.default_rng(33)
+    splits = [40, 0, 7, 65]
+    ro, _ = oracle_mod.splits_to_offsets(splits)
+    R_, Md, N, G = int(ro[-1]), 24, 40, len(splits)
+    A = rand_bf16(rng, (R_, Md))
+    B = rand_bf16(rng, (R_, N), 0.1)
+    Av, Bv = R.bf16_bits_to_f64(A), R.bf16_bits_to_f64(B)
+    C = oracle_mod.grouped_gemm("k", ro, Md, N, 0, oracle_mod.Operand("bf16", A, 0, 1, Md),
+                                oracle_mod.Operand("bf16", B, 0, 1, N), out_dtype)
+    for g in range(G):
+        check(C[g], Av[ro[g]:ro[g + 1]].T @ Bv[ro[g]:ro[g + 1]], out_dtype)
+    assert np.all(C[1] == 0)
+
+
 def test_integer_exact_case_bit_exact(oracle_mod):
     """Codes in {-2..2} with E in {126,127,128} and K <= 64: every partial sum
     is a small dyadic number, exact in fp32 and in bf16, so the result is
