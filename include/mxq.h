@@ -82,15 +82,31 @@ typedef enum {
 
 /* ------------------------------------------------------------ descriptors */
 
-/* Gated activation (TE3238, Greptile Summary: SwiGLU and ClampedSwiGLU).
+/* Row-scaled activation (TE3238, Greptile Summary: the scaled activations are
+ * SReLU, SwiGLU and ClampedSwiGLU).
  * MXQ_ACT_SWIGLU:          a = bf16(silu(g)),  h = bf16(a * u * s)
  * MXQ_ACT_CLAMPED_SWIGLU:  the same on g' = min(g, limit), u' = clamp(u, -limit,
- *                          limit) (NaN passes through); limit is typically 7. */
-typedef enum { MXQ_ACT_SWIGLU = 0, MXQ_ACT_CLAMPED_SWIGLU = 1 } mxq_act_kind;
+ *                          limit) (NaN passes through); limit is typically 7.
+ * MXQ_ACT_SRELU:           unary: a = bf16(max(x, 0)^2),  h = bf16(a * s); the
+ *                          pages give no formula, this is the squared ReLU
+ *                          with the activation rounded before the row scale
+ *                          as for SwiGLU.  x is passed as `gate`; `up` (and
+ *                          in the backward `dup`) must be NULL.
+ * glu_interleave (SwiGLU kinds only): 0 for gate and up as given; B > 0 (a
+ * multiple of 32 dividing K) when the gated input holds gate and up
+ * interleaved in blocks of B columns (TE3238, Important Files Changed: the GLU
+ * interleave is handled inside the scaled SwiGLU kernels): logical column j
+ * of gate sits at column 2B*(j/B) + j%B of the `gate` view, and likewise for
+ * `up`, so a packed interleaved buffer p of ld 2K is passed as gate = p,
+ * up = p + B.  The backward then writes [dgate | dup] in the same layout (dup
+ * = dgate + B) and its MXFP8 form too (dup's columns B on from dgate's).  B =
+ * K is the plain packed [gate | up]. */
+typedef enum { MXQ_ACT_SWIGLU = 0, MXQ_ACT_CLAMPED_SWIGLU = 1, MXQ_ACT_SRELU = 2 } mxq_act_kind;
 
 typedef struct {
-    int32_t kind;  /* mxq_act_kind */
-    float limit;   /* clamp limit for MXQ_ACT_CLAMPED_SWIGLU, > 0 */
+    int32_t kind;            /* mxq_act_kind */
+    float limit;             /* clamp limit for MXQ_ACT_CLAMPED_SWIGLU, > 0 */
+    int32_t glu_interleave;  /* 0, or the interleave block B (see above) */
 } mxq_act;
 
 /* Row groups (experts).  Both arrays are DEVICE int64[G+1], as written by
@@ -177,7 +193,12 @@ mxq_status mxq_swiglu_quantize_bwd_workspace(int64_t M, int64_t K, uint32_t dirs
  * (clamped variant: g, u clamped as in the forward; dgate is 0 where g > limit,
  * dup is 0 where |u| > limit).  The MXFP8 outputs quantize the (M x 2K)
  * matrix [dgate | dup]: row_out codes (M x 2K) + scales (M x 2K/32); col_out
- * codes (M x 2K) + scales (n_blocks x 2K).
+ * codes (M x 2K) + scales (n_blocks x 2K).  With act->glu_interleave = B the
+ * dense and MXFP8 gradients are interleaved like the input (dup = dgate + B).
+ * MXQ_ACT_SRELU (unary, x passed as gate, up = dup = NULL):
+ *     dx = bf16(dh * s * 2 * max(x, 0)) written through dgate,
+ *     dscale[r] = sum_j dh * bf16(max(x, 0)^2),
+ * and the MXFP8 outputs quantize the (M x K) matrix dx.
  *   dgate, dup  device bf16 (M x K) outputs with pitches ld_dgate, ld_dup, or
  *               both NULL to skip the dense gradients
  *   dscale      device fp32[M] output, or NULL; needs row_scale semantics only

@@ -29,6 +29,7 @@ ROWWISE = 1
 COLWISE = 2
 ACT_SWIGLU = 0
 ACT_CLAMPED_SWIGLU = 1
+ACT_SRELU = 2
 DTYPE_BF16 = 0
 DTYPE_MXFP8 = 1
 DTYPE_F32 = 2
@@ -53,7 +54,7 @@ class MxqError(RuntimeError):
 
 
 class mxq_act(ctypes.Structure):
-    _fields_ = [("kind", ctypes.c_int32), ("limit", ctypes.c_float)]
+    _fields_ = [("kind", ctypes.c_int32), ("limit", ctypes.c_float), ("glu_interleave", ctypes.c_int32)]
 
 
 class mxq_groups(ctypes.Structure):
@@ -163,8 +164,8 @@ def _hold(t, stream):
         t.record_stream(stream)
 
 
-def make_act(kind=ACT_SWIGLU, limit=7.0):
-    return mxq_act(kind, limit)
+def make_act(kind=ACT_SWIGLU, limit=7.0, interleave=0):
+    return mxq_act(kind, limit, interleave)
 
 
 def make_groups(row_off=None, block_off=None):
@@ -193,7 +194,8 @@ def mxq_splits_to_offsets(splits, row_off, block_off=None, err_flag=None, stream
 
 def mxq_swiglu_quantize_fwd(act, gate, up, row_scale, groups, dirs, row_out, col_out, stream=None):
     M, K = gate.shape
-    return lib.mxq_swiglu_quantize_fwd(_byref(act), M, K, _ptr(gate), _ld(gate), _ptr(up), _ld(up),
+    return lib.mxq_swiglu_quantize_fwd(_byref(act), M, K, _ptr(gate), _ld(gate), _ptr(up),
+                                       _ld(up) if up is not None else 0,
                                        _ptr(row_scale), _byref(groups), dirs, _byref(row_out),
                                        _byref(col_out), _stream(stream))
 
@@ -208,10 +210,10 @@ def mxq_swiglu_quantize_bwd(act, grad, gate, up, row_scale, groups, dgate, dup, 
                             row_out, col_out, ws, stream=None):
     M, K = gate.shape
     return lib.mxq_swiglu_quantize_bwd(
-        _byref(act), M, K, _ptr(grad), _ld(grad), _ptr(gate), _ld(gate), _ptr(up), _ld(up),
-        _ptr(row_scale), _byref(groups), _ptr(dgate), _ld(dgate) if dgate is not None else 0,
-        _ptr(dup), _ld(dup) if dup is not None else 0, _ptr(dscale), dirs, _byref(row_out),
-        _byref(col_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _byref(act), M, K, _ptr(grad), _ld(grad), _ptr(gate), _ld(gate), _ptr(up),
+        _ld(up) if up is not None else 0, _ptr(row_scale), _byref(groups), _ptr(dgate),
+        _ld(dgate) if dgate is not None else 0, _ptr(dup), _ld(dup) if dup is not None else 0, _ptr(dscale),
+        dirs, _byref(row_out), _byref(col_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream))
 
 
@@ -219,7 +221,7 @@ def mxq_swiglu_quantize_bwd_noalloc(act, grad, gate, up, row_scale, groups, dgat
                                     row_out, col_out, stream=None):
     M, K = gate.shape
     return lib.mxq_swiglu_quantize_bwd_noalloc(
-        _byref(act), M, K, _ptr(grad), _ld(grad), _ptr(gate), _ld(gate), _ptr(up), _ld(up),
+        _byref(act), M, K, _ptr(grad), _ld(grad), _ptr(gate), _ld(gate), _ptr(up), _ld(up) if up is not None else 0,
         _ptr(row_scale), _byref(groups), _ptr(dgate), _ld(dgate) if dgate is not None else 0,
         _ptr(dup), _ld(dup) if dup is not None else 0, _ptr(dscale), dirs, _byref(row_out),
         _byref(col_out), _stream(stream))
@@ -280,18 +282,36 @@ def _outs(rc, cc, rs, cs, dirs):
 
 
 def swiglu_quantize_fwd(gate, up, scale=None, rowwise=True, colwise=False, row_off=None,
-                        block_off=None, n_col_blocks=None, clamped=False, limit=7.0, stream=None):
+                        block_off=None, n_col_blocks=None, clamped=False, limit=7.0, interleave=0,
+                        stream=None):
     """Returns (codes_row, codes_col, scales_row, scales_col); a disabled
     direction comes back zero-sized.  With groups, n_col_blocks must be the
-    number of colwise scale rows (sum of ceil(split/32))."""
+    number of colwise scale rows (sum of ceil(split/32)).  With interleave = B,
+    gate and up are (M, K) views p[:, :K] and p[:, B:B + K] of a packed (M, 2K)
+    buffer p holding gate and up interleaved in blocks of B columns."""
     M, K = gate.shape
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if n_col_blocks is None:
         n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
     rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, gate.device)
     ro, co = _outs(rc, cc, rs, cs, dirs)
-    act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit)
+    act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit, interleave)
     check(mxq_swiglu_quantize_fwd(act, gate, up, scale, make_groups(row_off, block_off), dirs, ro, co, stream))
+    return rc, cc, rs, cs
+
+
+def srelu_quantize_fwd(x, scale=None, rowwise=True, colwise=False, row_off=None, block_off=None,
+                       n_col_blocks=None, stream=None):
+    """The row-scaled SReLU forward, MXFP8 out: (codes_row, codes_col,
+    scales_row, scales_col) as swiglu_quantize_fwd."""
+    M, K = x.shape
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if n_col_blocks is None:
+        n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device)
+    ro, co = _outs(rc, cc, rs, cs, dirs)
+    check(mxq_swiglu_quantize_fwd(make_act(ACT_SRELU), x, None, scale, make_groups(row_off, block_off), dirs, ro,
+                                  co, stream))
     return rc, cc, rs, cs
 
 
@@ -319,10 +339,11 @@ def quantize_into(x, codes_row, codes_col, scales_row, scales_col, noop_flag=Non
 
 def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False, row_off=None,
                         block_off=None, n_col_blocks=None, clamped=False, limit=7.0, dense=True,
-                        want_dscale=True, stream=None):
+                        want_dscale=True, interleave=0, stream=None):
     """Returns (codes_row, codes_col, scales_row, scales_col, dgate_dup, dscale)
     where the codes cover the (M, 2K) [dgate | dup] matrix and dgate_dup is the
-    packed (M, 2K) bf16 gradient (None when dense=False)."""
+    packed (M, 2K) bf16 gradient (None when dense=False); with interleave = B
+    (gate, up as in swiglu_quantize_fwd) both take the interleaved layout."""
     import torch
     M, K = gate.shape
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
@@ -335,11 +356,33 @@ def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False,
     nws = mxq_swiglu_quantize_bwd_workspace(M, K, dirs)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=gate.device) if (want_dscale and nws) else None
     _hold(ws, stream)
-    act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit)
+    act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit, interleave)
+    uo = interleave if interleave else K
     check(mxq_swiglu_quantize_bwd(act, grad, gate, up, scale, make_groups(row_off, block_off),
-                                  dd[:, :K] if dense else None, dd[:, K:] if dense else None, ds,
+                                  dd[:, :K] if dense else None, dd[:, uo:uo + K] if dense else None, ds,
                                   dirs, ro, co, ws, stream))
     return rc, cc, rs, cs, dd, ds
+
+
+def srelu_quantize_bwd(grad, x, scale=None, rowwise=True, colwise=False, row_off=None, block_off=None,
+                       n_col_blocks=None, dense=True, want_dscale=True, stream=None):
+    """The row-scaled SReLU backward: (codes_row, codes_col, scales_row,
+    scales_col, dx, dscale), the codes covering the (M, K) dx."""
+    import torch
+    M, K = x.shape
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if n_col_blocks is None:
+        n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device)
+    ro, co = _outs(rc, cc, rs, cs, dirs)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if dense else None
+    ds = torch.empty(M, dtype=torch.float32, device=x.device) if want_dscale else None
+    nws = mxq_swiglu_quantize_bwd_workspace(M, K, dirs)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device) if (want_dscale and nws) else None
+    _hold(ws, stream)
+    check(mxq_swiglu_quantize_bwd(make_act(ACT_SRELU), grad, x, None, scale, make_groups(row_off, block_off), dx,
+                                  None, ds, dirs, ro, co, ws, stream))
+    return rc, cc, rs, cs, dx, ds
 
 
 def _operand(data, scales=None, group_dim=False):

@@ -1,6 +1,8 @@
 // act_quant.hip -- fused row-scaled SwiGLU + MXFP8 block quantization on gfx950:
 // forward, backward (dgate, dup, dscale and the quantized [dgate | dup]) and the
-// plain quantizer (identity activation).
+// plain quantizer (identity activation); the row-scaled SReLU through the same
+// kernels (unary: x in place of gate, dx in place of [dgate | dup]); gate and
+// up either packed or interleaved in blocks of a multiple of 32 columns.
 //
 // Pages (cited by title; each defines what is computed here):
 //   TAO4743 "[mxfp8 training] Add a fused gated-activation (SwiGLU) + MXFP8
@@ -9,8 +11,9 @@
 //           pass), API (packed [gate | up], backward returns [dGate | dUp]),
 //           Numerics and tests (bitwise match with the unfused definition).
 //   TE3238  "Activation + GroupedLinear Fusion for MOE and other MOE
-//           optimizations": Greptile Summary (per-row-scaled SwiGLU and
-//           ClampedSwiGLU; gradient of the scales).
+//           optimizations": Greptile Summary (per-row-scaled SReLU, SwiGLU and
+//           ClampedSwiGLU; gradient of the scales), Important Files Changed
+//           (the GLU interleave handled inside the scaled SwiGLU kernels).
 //   VEO1340 ByteDance-Seed/VeOmni pull 1340, "What does this PR do?": SiLU is
 //           rounded to the activation dtype before it multiplies up.
 //
@@ -361,11 +364,32 @@ constexpr int NWORDS = RPW * CPT / 32;  // risk mask words per lane
 
 // One element pair of the forward: packed gate / up words -> packed h word.
 // Returns a 2-bit mask of the elements that need the exact path.
+// max(x, 0) with NaN passed through and -0 mapped to +0
+__device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : (x != x ? x : 0.0f); }
+
+// Activations with a gate and an up input (the others read `gate` only).
+template <int ACT>
+constexpr bool gated() { return ACT == ACT_SWIGLU || ACT == ACT_CLAMPED; }
+
 template <int ACT>
 __device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, float L, uint32_t &hw) {
     if constexpr (ACT == ACT_IDENTITY) {
         hw = gw;
         return 0u;
+    } else if constexpr (ACT == ACT_SRELU) {
+        // a = bf16(v * v), v = max(x, 0): the square of a bf16 is exact in fp32
+        // unless it leaves the normal range; h = bf16(a * s) as SwiGLU's product
+        const float v0 = relu_f(lo_f(gw)), v1 = relu_f(hi_f(gw));
+        const float t0 = v0 * v0, t1 = v1 * v1;
+        const uint32_t aw = pack_bf16(t0, t1);
+        const float a0 = lo_f(aw), a1 = hi_f(aw);
+        const float h0 = a0 * s, h1 = a1 * s;
+        hw = pack_bf16(h0, h1);
+        (void)uw;
+        (void)L;
+        uint32_t risky = (uint32_t)!normal_or_zero(t0) | (uint32_t)product_risky(a0, h0);
+        risky |= ((uint32_t)!normal_or_zero(t1) | (uint32_t)product_risky(a1, h1)) << 1;
+        return risky;
     } else {
         float g0 = lo_f(gw), g1 = hi_f(gw), u0 = lo_f(uw), u1 = hi_f(uw);
         if constexpr (ACT == ACT_CLAMPED) {
@@ -387,6 +411,12 @@ __device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, 
 
 // h = bf16( bf16(silu(g)) * u * s ) in fp64 (the product is exact in fp64)
 __device__ __forceinline__ uint32_t fwd_elem_f64(float g, float u, float s, float L, int act) {
+    if (act == ACT_SRELU) {
+        // h = bf16( bf16(max(x, 0)^2) * s ): the square and the product are exact in fp64
+        const double v = (double)relu_f(g);
+        const float a = __uint_as_float(bf16_from_f64(v * v) << 16);
+        return bf16_from_f64((double)a * (double)s);
+    }
     if (act == ACT_CLAMPED) {
         g = clamp_gate(g, L);
         u = clamp_up(u, L);
@@ -399,7 +429,8 @@ __device__ __forceinline__ uint32_t fwd_elem_f64(float g, float u, float s, floa
 constexpr int FNT = 64 * NWAVE;  // forward threads per workgroup
 
 // Slow path for lanes whose marked elements overflowed the queue (their risk
-// mask is passed; other lanes pass zeros); q is the lane's queue column.
+// mask is passed; other lanes pass zeros); q is the lane's queue column; c0 is
+// the lane's first column in the gate / up arrays (interleave applied).
 template <int ACT>
 __device__ __forceinline__ void fwd_fix_slow(const FwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
                                           uint32_t (&h)[RPW][CPT / 2], uint2 *q) {
@@ -413,7 +444,7 @@ __device__ __forceinline__ void fwd_fix_slow(const FwdArgs &a, int64_t rbase, in
             const int idx = (int)q[FNT * j].x;
             const int64_t r = rbase + idx / CPT, c = c0 + idx % CPT;
             const float g = bf16_at(a.gate + r * a.ld_gate + c);
-            const float u = bf16_at(a.up + r * a.ld_up + c);
+            const float u = gated<ACT>() ? bf16_at(a.up + r * a.ld_up + c) : 0.0f;
             const float s = a.row_scale != nullptr ? a.row_scale[r] : 1.0f;
             q[FNT * j].x = fwd_elem_f64(g, u, s, a.limit, ACT);
         }
@@ -496,12 +527,16 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int co = (int)(slab * SLAB) + lane * CPT;
     const bool active = co < a.K;
+    // the lane's first column in the gate / up arrays: with gate and up
+    // interleaved in blocks of il columns (il a multiple of 32, so a lane's 8
+    // columns stay in one block), logical column j sits at 2 il (j / il) + j % il
+    const int gco = a.il ? (co / a.il) * 2 * a.il + co % a.il : co;
     const Tile T = tile_rows<TROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
     if (T.n == 0) return;  // uniform over the workgroup
     const int nrow = min(max(T.n - wave * RPW, 0), RPW);  // rows of this wave (uniform per wave)
     const int64_t rbase = T.r0 + wave * RPW;
     const uint16_t *gate0 = a.gate + rbase * a.ld_gate;
-    const uint16_t *up0 = a.up + rbase * a.ld_up;
+    const uint16_t *up0 = gated<ACT>() ? a.up + rbase * a.ld_up : nullptr;
 
     // pass 1: all loads of the wave's rows, then the fast path
     Vec<CPT> gv[RPW], uv[RPW];
@@ -510,8 +545,8 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
         gv[i] = zero_vec<CPT>();
         uv[i] = zero_vec<CPT>();
         if (i < nrow && active) {
-            gv[i] = load_vec<CPT>(gate0 + i * a.ld_gate + co);
-            if constexpr (ACT != ACT_IDENTITY) uv[i] = load_vec<CPT>(up0 + i * a.ld_up + co);
+            gv[i] = load_vec<CPT>(gate0 + i * a.ld_gate + gco);
+            if constexpr (gated<ACT>()) uv[i] = load_vec<CPT>(up0 + i * a.ld_up + gco);
         }
     }
     uint32_t h[RPW][CPT / 2];
@@ -558,7 +593,7 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
             uint32_t rk[NWORDS];
 #pragma unroll
             for (int w = 0; w < NWORDS; w++) rk[w] = nq > kQ ? risk[w] : 0u;
-            fwd_fix_slow<ACT>(a, rbase, co, rk, h, &fq[0][tid]);
+            fwd_fix_slow<ACT>(a, rbase, gco, rk, h, &fq[0][tid]);
         }
     }
 
@@ -657,8 +692,36 @@ __device__ __forceinline__ bool near_tie(float t, float bound) {
     return (bool)((int)(fabsf(t - tie) <= bound) | (int)(bound > fabsf(t) * 0x1p-10f));
 }
 
+// SReLU backward of one element pair (x in gw): dx = bf16(dh * s * 2 v),
+// v = max(x, 0), and dh * a (a = bf16(v^2)) for dscale.  dh * v and its double
+// are exact in fp32 unless they leave the normal range; the product with s is
+// the one rounding, so only its tie pattern (or a non-normal value) is risky.
+__device__ __forceinline__ BwdPair bwd_pair_srelu(uint32_t dw, uint32_t gw, float s) {
+    const float v[2] = {relu_f(lo_f(gw)), relu_f(hi_f(gw))};
+    const float dh[2] = {lo_f(dw), hi_f(dw)};
+    const uint32_t aw = pack_bf16(v[0] * v[0], v[1] * v[1]);
+    const float av[2] = {lo_f(aw), hi_f(aw)};
+    BwdPair out;
+    float vdx[2];
+    out.risky = 0u;
+    out.dsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const float q2 = (dh[j] * v[j]) * 2.0f;   // exact
+        const float tdx = q2 * s;                  // one rounding
+        vdx[j] = tdx;
+        out.dsum += dh[j] * av[j];                 // exact (8 x 8 bits)
+        uint32_t r = (uint32_t)product_risky(q2, tdx) | (uint32_t)!normal_or_zero(v[j] * v[j]);
+        out.risky |= r << j;
+    }
+    out.dg = pack_bf16(vdx[0], vdx[1]);
+    out.du = 0u;
+    return out;
+}
+
 template <int ACT>
 __device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t uw, float s, float L) {
+    if constexpr (ACT == ACT_SRELU) return bwd_pair_srelu(dw, gw, s);
     float g[2] = {lo_f(gw), hi_f(gw)}, u[2] = {lo_f(uw), hi_f(uw)};
     const float dh[2] = {lo_f(dw), hi_f(dw)};
     float mg[2] = {1.0f, 1.0f}, mu[2] = {1.0f, 1.0f};
@@ -711,6 +774,18 @@ __device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t u
 // exact a (the fast pass summed dh*a_fast*u into dscale).
 template <int ACT>
 __device__ __forceinline__ uint32_t bwd_elem_f64(float dhf, float gf, float uf, float s, float L, float *corr) {
+    if constexpr (ACT == ACT_SRELU) {
+        // dx = bf16(dh * s * 2 v) and a = bf16(v^2), v = max(x, 0): exact products in fp64
+        const float vf = relu_f(gf);
+        const double v = vf;
+        const double a = (double)__uint_as_float(bf16_from_f64(v * v) << 16);
+        const uint32_t dxb = bf16_from_f64((double)dhf * (double)s * 2.0 * v);
+        const float af = lo_f(pack_bf16(vf * vf, 0.0f));   // the fast pass's a
+        *corr = (float)a == af ? 0.0f : dhf * ((float)a - af);   // (an infinite a needs no correction)
+        (void)uf;
+        (void)L;
+        return dxb;
+    }
     double g = gf, u = uf;
     const double dh = dhf;
     double mg = 1.0, mu = 1.0;
@@ -729,7 +804,8 @@ __device__ __forceinline__ uint32_t bwd_elem_f64(float dhf, float gf, float uf, 
     const float gc = (float)g;
     const Sig z = sig_fast(gc);
     const float af = lo_f(pack_bf16(gc * z.sig, 0.0f));
-    *corr = (dhf * (float)u) * ((float)a - af);
+    // (equal values, infinite ones included, need no correction: Inf - Inf would be NaN)
+    *corr = (float)a == af ? 0.0f : (dhf * (float)u) * ((float)a - af);
     return dgb | (dub << 16);
 }
 
@@ -744,8 +820,9 @@ constexpr int BNT = 64 * BNWAVE;  // backward threads per workgroup
 
 // Slow path for lanes whose marked elements overflowed the queue (see the
 // forward's); the queue column's .x holds indices / results, .y corrections.
+// c0 is the lane's first column of grad, gc0 of gate / up (interleave applied).
 template <int ACT>
-__device__ __forceinline__ void bwd_fix_slow(const BwdArgs &a, int64_t rbase, int c0, const uint32_t *risk,
+__device__ __forceinline__ void bwd_fix_slow(const BwdArgs &a, int64_t rbase, int c0, int gc0, const uint32_t *risk,
                                              uint32_t (&hg)[BRPW][CPT / 2], uint32_t (&hu)[BRPW][CPT / 2],
                                              uint2 *q, float (&dsum)[BRPW]) {
     int total = 0;
@@ -756,10 +833,10 @@ __device__ __forceinline__ void bwd_fix_slow(const BwdArgs &a, int64_t rbase, in
 #pragma unroll 1
         for (int j = 0; j < nq; j++) {
             const int idx = (int)q[BNT * j].x;
-            const int64_t r = rbase + idx / CPT, c = c0 + idx % CPT;
+            const int64_t r = rbase + idx / CPT, c = c0 + idx % CPT, gc = gc0 + idx % CPT;
             const float d = bf16_at(a.grad + r * a.ld_grad + c);
-            const float g = bf16_at(a.gate + r * a.ld_gate + c);
-            const float u = bf16_at(a.up + r * a.ld_up + c);
+            const float g = bf16_at(a.gate + r * a.ld_gate + gc);
+            const float u = gated<ACT>() ? bf16_at(a.up + r * a.ld_up + gc) : 0.0f;
             const float s = a.row_scale != nullptr ? a.row_scale[r] : 1.0f;
             float corr;
             q[BNT * j].x = bwd_elem_f64<ACT>(d, g, u, s, a.limit, &corr);
@@ -789,8 +866,11 @@ __device__ __forceinline__ void bwd_fix_slow(const BwdArgs &a, int64_t rbase, in
 
 // Backward over one tile x slab (8 waves of 4 rows, else as the forward).  Each lane
 // owns 8 columns j of gate/up/grad and produces dgate (columns j of
-// [dgate | dup]) and dup (columns K + j).  dscale partials are reduced
-// through LDS in a fixed order (deterministic) and written per (row, slab).
+// [dgate | dup]) and dup (columns K + j); with gate and up interleaved in
+// blocks of il columns, the gradient takes the same layout (dgate at
+// 2 il (j / il) + j % il, dup il columns on).  SReLU (unary) produces dx alone,
+// at columns j of a (M x K) output.  dscale partials are reduced through LDS
+// in a fixed order (deterministic) and written per (row, slab).
 template <int ACT, int DIRS>
 __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int64_t nwork) {
     __shared__ uint2 fq[kQ + 1][BNT];   // slot kQ takes the writes of lanes whose queue is full
@@ -805,12 +885,13 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int co = (int)(slab * SLAB) + lane * CPT;
     const bool active = co < a.K;
+    const int gco = a.il ? (co / a.il) * 2 * a.il + co % a.il : co;   // gate / up / dgate / dup column
+    const int uoff = a.il ? a.il : (int)a.K;   // dup's columns of the MXFP8 [dgate | dup] lie this far on
     const Tile T = tile_rows<TROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
     if (T.n == 0) return;
     const int nrow = min(max(T.n - wave * BRPW, 0), BRPW);
     const int64_t rbase = T.r0 + wave * BRPW;
     const float L = a.limit;
-    const int K = (int)a.K;
     const bool dense = a.dgate != nullptr;
     const bool want_ds = a.dscale != nullptr;
 
@@ -823,8 +904,8 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
         if (i < nrow && active) {
             const int64_t r = rbase + i;
             db[i] = load_vec<CPT>(a.grad + r * a.ld_grad + co);
-            gb[i] = load_vec<CPT>(a.gate + r * a.ld_gate + co);
-            ub[i] = load_vec<CPT>(a.up + r * a.ld_up + co);
+            gb[i] = load_vec<CPT>(a.gate + r * a.ld_gate + gco);
+            if constexpr (gated<ACT>()) ub[i] = load_vec<CPT>(a.up + r * a.ld_up + gco);
         }
     }
     uint32_t hg[BRPW][CPT / 2], hu[BRPW][CPT / 2];
@@ -839,8 +920,8 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
         if (i + PF < BRPW && i + PF < nrow && active) {
             const int64_t r = rbase + i + PF;
             db[i % PF] = load_vec<CPT>(a.grad + r * a.ld_grad + co);
-            gb[i % PF] = load_vec<CPT>(a.gate + r * a.ld_gate + co);
-            ub[i % PF] = load_vec<CPT>(a.up + r * a.ld_up + co);
+            gb[i % PF] = load_vec<CPT>(a.gate + r * a.ld_gate + gco);
+            if constexpr (gated<ACT>()) ub[i % PF] = load_vec<CPT>(a.up + r * a.ld_up + gco);
         }
         const float s = (a.row_scale != nullptr && i < nrow) ? a.row_scale[rbase + i] : 1.0f;
         uint32_t bits = 0u;
@@ -895,7 +976,7 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
             uint32_t rk[BNWORDS];
 #pragma unroll
             for (int w = 0; w < BNWORDS; w++) rk[w] = nq > kQ ? risk[w] : 0u;
-            bwd_fix_slow<ACT>(a, rbase, co, rk, hg, hu, &fq[0][tid], dsum);
+            bwd_fix_slow<ACT>(a, rbase, co, gco, rk, hg, hu, &fq[0][tid], dsum);
         }
     }
 
@@ -924,8 +1005,8 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
             }
         }
         if (dense && active && i < nrow) {
-            store_bf16<CPT>(a.dgate + r * a.ld_dgate + co, hg[i]);
-            store_bf16<CPT>(a.dup + r * a.ld_dup + co, hu[i]);
+            store_bf16<CPT>(a.dgate + r * a.ld_dgate + gco, hg[i]);
+            if constexpr (gated<ACT>()) store_bf16<CPT>(a.dup + r * a.ld_dup + gco, hu[i]);
         }
         uint32_t mg = 0u, mu = 0u;
 #pragma unroll
@@ -952,12 +1033,12 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
                 }
                 if (active) {
                     uint8_t *rowc = a.row.codes + r * a.row.ld_codes;
-                    store_codes<CPT>(rowc + co, cg);
-                    store_codes<CPT>(rowc + K + co, cu);
+                    store_codes<CPT>(rowc + gco, cg);
+                    if constexpr (gated<ACT>()) store_codes<CPT>(rowc + gco + uoff, cu);
                     if ((lane & 3) == 0) {
                         uint8_t *rs = a.row.scales + r * a.row.ld_scales;
-                        rs[co / 32] = (uint8_t)Eg;
-                        rs[(K + co) / 32] = (uint8_t)Eu;
+                        rs[gco / 32] = (uint8_t)Eg;
+                        if constexpr (gated<ACT>()) rs[(gco + uoff) / 32] = (uint8_t)Eu;
                     }
                 }
             }
@@ -1001,14 +1082,14 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
                         cg[q] = cvt4_cols(hg[i][2 * q], hg[i][2 * q + 1], sg.s + 4 * q, sg.nan[q]);
                         cu[q] = cvt4_cols(hu[i][2 * q], hu[i][2 * q + 1], su.s + 4 * q, su.nan[q]);
                     }
-                    store_codes<CPT>(colc + i * a.col.ld_codes + co, cg);
-                    store_codes<CPT>(colc + i * a.col.ld_codes + K + co, cu);
+                    store_codes<CPT>(colc + i * a.col.ld_codes + gco, cg);
+                    if constexpr (gated<ACT>()) store_codes<CPT>(colc + i * a.col.ld_codes + gco + uoff, cu);
                 }
             }
             if (wave == 0) {
                 uint8_t *cs = a.col.scales + T.srow * a.col.ld_scales;
-                store_scale_bytes(cs + co, sg.E);
-                store_scale_bytes(cs + K + co, su.E);
+                store_scale_bytes(cs + gco, sg.E);
+                if constexpr (gated<ACT>()) store_scale_bytes(cs + gco + uoff, su.E);
             }
         }
     }
@@ -1105,12 +1186,14 @@ hipError_t launch_act_quant_fwd(const FwdArgs &a, hipStream_t stream) {
     switch (a.act) {
         case ACT_SWIGLU: return fwd_dispatch<ACT_SWIGLU>(a, stream);
         case ACT_CLAMPED: return fwd_dispatch<ACT_CLAMPED>(a, stream);
+        case ACT_SRELU: return fwd_dispatch<ACT_SRELU>(a, stream);
         default: return fwd_dispatch<ACT_IDENTITY>(a, stream);
     }
 }
 
 hipError_t launch_act_quant_bwd(const BwdArgs &a, hipStream_t stream) {
     if (a.act == ACT_CLAMPED) return bwd_dispatch<ACT_CLAMPED>(a, stream);
+    if (a.act == ACT_SRELU) return bwd_dispatch<ACT_SRELU>(a, stream);
     return bwd_dispatch<ACT_SWIGLU>(a, stream);
 }
 

@@ -141,14 +141,32 @@ mxq_status check_groups(const mxq_groups *groups, bool need_blocks, GroupsOut &o
     return MXQ_OK;
 }
 
+// Checks the GLU interleave block il of an activation kind (0: none): only
+// gated kinds take one, a positive multiple of 32 dividing K.
+mxq_status check_interleave(int act_kind, int il, int64_t K) {
+    if (il == 0) return MXQ_OK;
+    if (act_kind != mxq::ACT_SWIGLU && act_kind != mxq::ACT_CLAMPED)
+        return fail(MXQ_ERR_SHAPE, "glu_interleave applies to SwiGLU and clamped SwiGLU only");
+    if (il < 0 || il % 32 != 0 || (K > 0 && K % il != 0))
+        return fail(MXQ_ERR_SHAPE, "glu_interleave = %d must be a positive multiple of 32 dividing K = %lld", il,
+                    (long long)K);
+    return MXQ_OK;
+}
+
+// Columns one gate (or up) view spans in memory: K, or 2K - il interleaved.
+int64_t gate_span(int64_t K, int il) { return il ? 2 * K - il : K; }
+
 // Validate and pack the shared part of fwd / quantize.
-mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, int64_t K, const uint16_t *gate,
-                       int64_t ld_gate, const uint16_t *up, int64_t ld_up, const float *row_scale,
-                       const mxq_groups *groups, uint32_t dirs, const mxq_mx_out *row_out,
-                       const mxq_mx_out *col_out, bool *noop) {
+mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int il, int64_t M, int64_t K,
+                       const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
+                       const float *row_scale, const mxq_groups *groups, uint32_t dirs,
+                       const mxq_mx_out *row_out, const mxq_mx_out *col_out, bool *noop) {
     *noop = false;
     if (M < 0 || K < 0) return fail(MXQ_ERR_SHAPE, "M = %lld and K = %lld must be >= 0", (long long)M, (long long)K);
     if (K % 32 != 0) return fail(MXQ_ERR_SHAPE, "K = %lld must be a multiple of 32", (long long)K);
+    mxq_status si = check_interleave(act_kind, il, K);
+    if (si != MXQ_OK) return si;
+    if (act_kind == mxq::ACT_SRELU && up != nullptr) return fail(MXQ_ERR_SHAPE, "SReLU is unary: up must be NULL");
     if (dirs < 1 || dirs > 3) return fail(MXQ_ERR_SHAPE, "dirs = %u must be ROWWISE, COLWISE or both", dirs);
     if (act_kind == mxq::ACT_CLAMPED && !(limit > 0.0f))
         return fail(MXQ_ERR_SHAPE, "clamped SwiGLU needs a limit > 0");
@@ -164,13 +182,14 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, in
     }
     if (M > (int64_t(1) << 40) || K > (int64_t(1) << 30))
         return fail(MXQ_ERR_OVERFLOW, "M or K beyond the supported range");
-    s = check_bf16_in(gate, M, K, ld_gate, act_kind == mxq::ACT_IDENTITY ? "x" : "gate", ins);
+    const bool gated = act_kind == mxq::ACT_SWIGLU || act_kind == mxq::ACT_CLAMPED;
+    s = check_bf16_in(gate, M, gate_span(K, il), ld_gate, gated ? "gate" : "x", ins);
     if (s != MXQ_OK) return s;
-    if (act_kind != mxq::ACT_IDENTITY) {
-        s = check_bf16_in(up, M, K, ld_up, "up", ins);
+    if (gated) {
+        s = check_bf16_in(up, M, gate_span(K, il), ld_up, "up", ins);
         if (s != MXQ_OK) return s;
-        if (row_scale) ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
     }
+    if (act_kind != mxq::ACT_IDENTITY && row_scale) ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
     const int64_t G = go.g.G;
     if (dirs & 1) {
         s = check_mx_out(row_out, true, M, K, M, "rowwise", outs);
@@ -197,8 +216,9 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, in
     a.K = K;
     a.gate = gate;
     a.ld_gate = ld_gate;
-    a.up = up;
+    a.up = gated ? up : nullptr;
     a.ld_up = ld_up;
+    a.il = il;
     a.row_scale = act_kind == mxq::ACT_IDENTITY ? nullptr : row_scale;
     a.groups = go.g;
     a.dirs = dirs;
@@ -209,228 +229,21 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int64_t M, in
     return MXQ_OK;
 }
 
-int act_from(const mxq_act *act, float *limit) {
+int act_from(const mxq_act *act, float *limit, int *il) {
     *limit = 7.0f;
+    *il = 0;
     if (act == nullptr) return mxq::ACT_SWIGLU;
     *limit = act->limit;
-    return act->kind == MXQ_ACT_CLAMPED_SWIGLU ? mxq::ACT_CLAMPED : (act->kind == MXQ_ACT_SWIGLU ? mxq::ACT_SWIGLU : -1);
+    *il = act->glu_interleave;
+    switch (act->kind) {
+        case MXQ_ACT_SWIGLU: return mxq::ACT_SWIGLU;
+        case MXQ_ACT_CLAMPED_SWIGLU: return mxq::ACT_CLAMPED;
+        case MXQ_ACT_SRELU: return mxq::ACT_SRELU;
+        default: return -1;
+    }
 }
 
 }  // namespace
-
-extern "C" {
-
-const char *mxq_version(void) { return "mxq 0.1.0 (gfx950)"; }
-
-const char *mxq_last_error_message(void) { return g_last_error.c_str(); }
-
-const char *mxq_status_string(mxq_status s) {
-    switch (s) {
-        case MXQ_OK: return "MXQ_OK";
-        case MXQ_ERR_NULL: return "MXQ_ERR_NULL";
-        case MXQ_ERR_SHAPE: return "MXQ_ERR_SHAPE";
-        case MXQ_ERR_ALIGN: return "MXQ_ERR_ALIGN";
-        case MXQ_ERR_OVERFLOW: return "MXQ_ERR_OVERFLOW";
-        case MXQ_ERR_ALIAS: return "MXQ_ERR_ALIAS";
-        case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
-        case MXQ_ERR_HIP: return "MXQ_ERR_HIP";
-        case MXQ_ERR_WORKSPACE: return "MXQ_ERR_WORKSPACE";
-    }
-    return "unknown mxq_status";
-}
-
-mxq_status mxq_splits_to_offsets(const int64_t *splits, int64_t G, int64_t *row_off, int64_t *block_off,
-                                 int32_t *err_flag, void *stream) {
-    if (splits == nullptr || row_off == nullptr) return fail(MXQ_ERR_NULL, "splits and row_off are required");
-    if (G < 1 || G > (int64_t(1) << 20)) return fail(MXQ_ERR_SHAPE, "G = %lld must be in [1, 2^20]", (long long)G);
-    if (!aligned(splits, 8) || !aligned(row_off, 8) || (block_off && !aligned(block_off, 8)) ||
-        (err_flag && !aligned(err_flag, 4)))
-        return fail(MXQ_ERR_ALIGN, "offset arrays must be 8-byte aligned (err_flag 4-byte)");
-    std::vector<Range> ins{range2d(splits, 1, G, G, 8, "splits")};
-    std::vector<Range> outs{range2d(row_off, 1, G + 1, G + 1, 8, "row_off")};
-    if (block_off) outs.push_back(range2d(block_off, 1, G + 1, G + 1, 8, "block_off"));
-    if (err_flag) outs.push_back(range2d(err_flag, 1, 1, 1, 4, "err_flag"));
-    mxq_status s = check_alias(ins, outs);
-    if (s != MXQ_OK) return s;
-    return hip_status(mxq::launch_splits_to_offsets(splits, G, row_off, block_off, err_flag, (hipStream_t)stream),
-                      "mxq_splits_to_offsets launch");
-}
-
-mxq_status mxq_swiglu_quantize_fwd(const mxq_act *act, int64_t M, int64_t K, const uint16_t *gate, int64_t ld_gate,
-                                   const uint16_t *up, int64_t ld_up, const float *row_scale,
-                                   const mxq_groups *groups, uint32_t dirs, const mxq_mx_out *row_out,
-                                   const mxq_mx_out *col_out, void *stream) {
-    float limit;
-    const int kind = act_from(act, &limit);
-    if (kind < 0) return fail(MXQ_ERR_UNSUPPORTED, "unknown activation kind %d", act->kind);
-    mxq::FwdArgs a{};
-    bool noop;
-    mxq_status s = prepare_fwd(a, kind, limit, M, K, gate, ld_gate, up, ld_up, row_scale, groups, dirs, row_out,
-                               col_out, &noop);
-    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
-    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_fwd launch");
-}
-
-mxq_status mxq_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, const mxq_groups *groups,
-                        uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *stream) {
-    mxq::FwdArgs a{};
-    bool noop;
-    mxq_status s = prepare_fwd(a, mxq::ACT_IDENTITY, 0.0f, M, K, x, ld_x, nullptr, 0, nullptr, groups, dirs, row_out,
-                               col_out, &noop);
-    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
-    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_quantize launch");
-}
-
-mxq_status mxq_quantize_noop(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, const mxq_groups *groups,
-                             uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out,
-                             const int32_t *noop_flag, void *stream) {
-    if (noop_flag != nullptr && !aligned(noop_flag, 4)) return fail(MXQ_ERR_ALIGN, "noop_flag must be 4-byte aligned");
-    mxq::FwdArgs a{};
-    bool noop;
-    mxq_status s = prepare_fwd(a, mxq::ACT_IDENTITY, 0.0f, M, K, x, ld_x, nullptr, 0, nullptr, groups, dirs, row_out,
-                               col_out, &noop);
-    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
-    if (noop_flag != nullptr) {
-        // the flag is an input: no output may overlap it
-        std::vector<Range> outs;
-        if (dirs & 1) {
-            outs.push_back(range2d(row_out->codes, M, K, row_out->ld_codes, 1, "row codes"));
-            outs.push_back(range2d(row_out->scales, M, K / 32, row_out->ld_scales, 1, "row scales"));
-        }
-        if (dirs & 2) {
-            outs.push_back(range2d(col_out->codes, M, K, col_out->ld_codes, 1, "col codes"));
-            outs.push_back(range2d(col_out->scales, (M + 31) / 32, K, col_out->ld_scales, 1, "col scales"));
-        }
-        if ((s = check_alias({range2d(noop_flag, 1, 1, 1, 4, "noop_flag")}, outs)) != MXQ_OK) return s;
-    }
-    a.noop = noop_flag;
-    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_quantize_noop launch");
-}
-
-mxq_status mxq_swiglu_quantize_bwd_workspace(int64_t M, int64_t K, uint32_t dirs, size_t *bytes) {
-    (void)dirs;
-    if (bytes == nullptr) return fail(MXQ_ERR_NULL, "bytes is NULL");
-    if (M < 0 || K < 0 || K % 32 != 0) return fail(MXQ_ERR_SHAPE, "M, K must be >= 0 and K % 32 == 0");
-    *bytes = (M == 0 || K == 0) ? 0 : mxq::bwd_workspace_bytes(M, K);
-    return ok();
-}
-
-mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, const uint16_t *grad, int64_t ld_grad,
-                                   const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
-                                   const float *row_scale, const mxq_groups *groups, uint16_t *dgate,
-                                   int64_t ld_dgate, uint16_t *dup, int64_t ld_dup, float *dscale, uint32_t dirs,
-                                   const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *ws,
-                                   size_t ws_bytes, void *stream) {
-    float limit;
-    const int kind = act_from(act, &limit);
-    if (kind < 0) return fail(MXQ_ERR_UNSUPPORTED, "unknown activation kind %d", act->kind);
-    if (M < 0 || K < 0) return fail(MXQ_ERR_SHAPE, "M = %lld and K = %lld must be >= 0", (long long)M, (long long)K);
-    if (K % 32 != 0) return fail(MXQ_ERR_SHAPE, "K = %lld must be a multiple of 32", (long long)K);
-    if (dirs > 3) return fail(MXQ_ERR_SHAPE, "dirs = %u must be 0, ROWWISE, COLWISE or both", dirs);
-    if ((dgate == nullptr) != (dup == nullptr)) return fail(MXQ_ERR_NULL, "dgate and dup must both be given or both NULL");
-    if (dirs == 0 && dgate == nullptr && dscale == nullptr)
-        return fail(MXQ_ERR_SHAPE, "nothing requested: dirs = 0 with no dense output and no dscale");
-    if (kind == mxq::ACT_CLAMPED && !(limit > 0.0f)) return fail(MXQ_ERR_SHAPE, "clamped SwiGLU needs a limit > 0");
-    std::vector<Range> ins, outs;
-    GroupsOut go;
-    mxq_status s = check_groups(groups, (dirs & 2) != 0, go, ins);
-    if (s != MXQ_OK) return s;
-    if (M == 0 || K == 0) return ok();
-    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 30))
-        return fail(MXQ_ERR_OVERFLOW, "M or K beyond the supported range");
-    if ((s = check_bf16_in(grad, M, K, ld_grad, "grad", ins)) != MXQ_OK) return s;
-    if ((s = check_bf16_in(gate, M, K, ld_gate, "gate", ins)) != MXQ_OK) return s;
-    if ((s = check_bf16_in(up, M, K, ld_up, "up", ins)) != MXQ_OK) return s;
-    if (row_scale) {
-        if (!aligned(row_scale, 4)) return fail(MXQ_ERR_ALIGN, "row_scale must be 4-byte aligned");
-        ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
-    }
-    if (dgate) {
-        if (ld_dgate < K || ld_dup < K) return fail(MXQ_ERR_SHAPE, "ld_dgate / ld_dup must be >= K");
-        if (!aligned(dgate, 16) || !aligned(dup, 16) || ld_dgate % 8 != 0 || ld_dup % 8 != 0)
-            return fail(MXQ_ERR_ALIGN, "dgate / dup pointers and pitches must be multiples of 16 bytes");
-        if (!extent_ok(M, ld_dgate, 2) || !extent_ok(M, ld_dup, 2))
-            return fail(MXQ_ERR_OVERFLOW, "dgate / dup extent too large");
-        outs.push_back(range2d(dgate, M, K, ld_dgate, 2, "dgate"));
-        outs.push_back(range2d(dup, M, K, ld_dup, 2, "dup"));
-    }
-    if (dscale) {
-        if (!aligned(dscale, 4)) return fail(MXQ_ERR_ALIGN, "dscale must be 4-byte aligned");
-        outs.push_back(range2d(dscale, 1, M, M, 4, "dscale"));
-        const size_t need = mxq::bwd_workspace_bytes(M, K);
-        if (need > 0) {
-            if (ws == nullptr || ws_bytes < need)
-                return fail(MXQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? (size_t)0 : ws_bytes);
-            if (!aligned(ws, 4)) return fail(MXQ_ERR_ALIGN, "workspace must be 4-byte aligned");
-            outs.push_back(range2d(ws, 1, (int64_t)need, (int64_t)need, 1, "workspace"));
-        }
-    }
-    const int64_t G = go.g.G;
-    if (dirs & 1) {
-        if ((s = check_mx_out(row_out, true, M, 2 * K, M, "rowwise", outs)) != MXQ_OK) return s;
-    } else if (row_out != nullptr && row_out->codes != nullptr) {
-        return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");
-    }
-    if (dirs & 2) {
-        if ((s = check_mx_out(col_out, false, M, 2 * K, (M + 31) / 32, "colwise", outs)) != MXQ_OK)
-            return s;
-    } else if (col_out != nullptr && col_out->codes != nullptr) {
-        return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
-    }
-    if (mxq::act_quant_launch_threads(M, K, G, (dirs & 2) && G > 0, true) >= (int64_t(1) << 32))
-        return fail(MXQ_ERR_OVERFLOW, "launch beyond 2^32 work-items");
-    if ((s = check_alias(ins, outs)) != MXQ_OK) return s;
-
-    mxq::BwdArgs a{};
-    a.act = kind;
-    a.limit = limit;
-    a.M = M;
-    a.K = K;
-    a.grad = grad; a.ld_grad = ld_grad;
-    a.gate = gate; a.ld_gate = ld_gate;
-    a.up = up; a.ld_up = ld_up;
-    a.row_scale = row_scale;
-    a.groups = go.g;
-    a.dgate = dgate; a.ld_dgate = ld_dgate;
-    a.dup = dup; a.ld_dup = ld_dup;
-    a.dscale = dscale;
-    a.dirs = dirs;
-    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales}
-                       : mxq::MxOut{nullptr, 0, nullptr, 0};
-    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales}
-                       : mxq::MxOut{nullptr, 0, nullptr, 0};
-    a.partials = static_cast<float *>(ws);
-    return hip_status(mxq::launch_act_quant_bwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_bwd launch");
-}
-
-mxq_status mxq_swiglu_quantize_bwd_noalloc(const mxq_act *act, int64_t M, int64_t K, const uint16_t *grad,
-                                           int64_t ld_grad, const uint16_t *gate, int64_t ld_gate,
-                                           const uint16_t *up, int64_t ld_up, const float *row_scale,
-                                           const mxq_groups *groups, uint16_t *dgate, int64_t ld_dgate,
-                                           uint16_t *dup, int64_t ld_dup, float *dscale, uint32_t dirs,
-                                           const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *stream) {
-    // the size check needs no device; the scratch's address is looked up
-    // only for a call that fits it
-    const size_t need = (dscale != nullptr && M > 0 && K > 0 && K % 32 == 0) ? mxq::bwd_workspace_bytes(M, K) : 0;
-    const size_t cap = mxq::bwd_scratch_capacity();
-    if (need > cap)
-        return fail(MXQ_ERR_WORKSPACE,
-                    "the allocation-free backward needs %zu bytes of scratch for dscale at M = %lld, K = %lld; "
-                    "the library's scratch holds %zu (use mxq_swiglu_quantize_bwd with a workspace)",
-                    need, (long long)M, (long long)K, cap);
-    float *scratch = nullptr;
-    if (need > 0) {
-        const hipError_t e = mxq::bwd_scratch(&scratch);
-        if (e != hipSuccess) return hip_status(e, "mxq_swiglu_quantize_bwd_noalloc scratch lookup");
-    }
-    return mxq_swiglu_quantize_bwd(act, M, K, grad, ld_grad, gate, ld_gate, up, ld_up, row_scale, groups, dgate,
-                                   ld_dgate, dup, ld_dup, dscale, dirs, row_out, col_out, scratch,
-                                   need > 0 ? cap : 0, stream);
-}
-
-// K-grouped launches keep one counter of their dynamic tile order in the
-// workspace (256 bytes keep the allocation's alignment simple).
-static size_t gemm_ws_bytes(const mxq_gemm_args &a) { return a.mode == MXQ_GEMM_TN ? 256 : 0; }
 
 namespace {
 
@@ -485,6 +298,247 @@ mxq_status check_gemm_alias(const mxq_gemm_args &a) {
 }
 
 }  // namespace
+
+extern "C" {
+
+const char *mxq_version(void) { return "mxq 0.1.0 (gfx950)"; }
+
+const char *mxq_last_error_message(void) { return g_last_error.c_str(); }
+
+const char *mxq_status_string(mxq_status s) {
+    switch (s) {
+        case MXQ_OK: return "MXQ_OK";
+        case MXQ_ERR_NULL: return "MXQ_ERR_NULL";
+        case MXQ_ERR_SHAPE: return "MXQ_ERR_SHAPE";
+        case MXQ_ERR_ALIGN: return "MXQ_ERR_ALIGN";
+        case MXQ_ERR_OVERFLOW: return "MXQ_ERR_OVERFLOW";
+        case MXQ_ERR_ALIAS: return "MXQ_ERR_ALIAS";
+        case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
+        case MXQ_ERR_HIP: return "MXQ_ERR_HIP";
+        case MXQ_ERR_WORKSPACE: return "MXQ_ERR_WORKSPACE";
+    }
+    return "unknown mxq_status";
+}
+
+mxq_status mxq_splits_to_offsets(const int64_t *splits, int64_t G, int64_t *row_off, int64_t *block_off,
+                                 int32_t *err_flag, void *stream) {
+    if (splits == nullptr || row_off == nullptr) return fail(MXQ_ERR_NULL, "splits and row_off are required");
+    if (G < 1 || G > (int64_t(1) << 20)) return fail(MXQ_ERR_SHAPE, "G = %lld must be in [1, 2^20]", (long long)G);
+    if (!aligned(splits, 8) || !aligned(row_off, 8) || (block_off && !aligned(block_off, 8)) ||
+        (err_flag && !aligned(err_flag, 4)))
+        return fail(MXQ_ERR_ALIGN, "offset arrays must be 8-byte aligned (err_flag 4-byte)");
+    std::vector<Range> ins{range2d(splits, 1, G, G, 8, "splits")};
+    std::vector<Range> outs{range2d(row_off, 1, G + 1, G + 1, 8, "row_off")};
+    if (block_off) outs.push_back(range2d(block_off, 1, G + 1, G + 1, 8, "block_off"));
+    if (err_flag) outs.push_back(range2d(err_flag, 1, 1, 1, 4, "err_flag"));
+    mxq_status s = check_alias(ins, outs);
+    if (s != MXQ_OK) return s;
+    return hip_status(mxq::launch_splits_to_offsets(splits, G, row_off, block_off, err_flag, (hipStream_t)stream),
+                      "mxq_splits_to_offsets launch");
+}
+
+mxq_status mxq_swiglu_quantize_fwd(const mxq_act *act, int64_t M, int64_t K, const uint16_t *gate, int64_t ld_gate,
+                                   const uint16_t *up, int64_t ld_up, const float *row_scale,
+                                   const mxq_groups *groups, uint32_t dirs, const mxq_mx_out *row_out,
+                                   const mxq_mx_out *col_out, void *stream) {
+    float limit;
+    int il;
+    const int kind = act_from(act, &limit, &il);
+    if (kind < 0) return fail(MXQ_ERR_UNSUPPORTED, "unknown activation kind %d", act->kind);
+    mxq::FwdArgs a{};
+    bool noop;
+    mxq_status s = prepare_fwd(a, kind, limit, il, M, K, gate, ld_gate, up, ld_up, row_scale, groups, dirs, row_out,
+                               col_out, &noop);
+    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
+    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_fwd launch");
+}
+
+mxq_status mxq_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, const mxq_groups *groups,
+                        uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *stream) {
+    mxq::FwdArgs a{};
+    bool noop;
+    mxq_status s = prepare_fwd(a, mxq::ACT_IDENTITY, 0.0f, 0, M, K, x, ld_x, nullptr, 0, nullptr, groups, dirs,
+                               row_out, col_out, &noop);
+    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
+    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_quantize launch");
+}
+
+mxq_status mxq_quantize_noop(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, const mxq_groups *groups,
+                             uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out,
+                             const int32_t *noop_flag, void *stream) {
+    if (noop_flag != nullptr && !aligned(noop_flag, 4)) return fail(MXQ_ERR_ALIGN, "noop_flag must be 4-byte aligned");
+    mxq::FwdArgs a{};
+    bool noop;
+    mxq_status s = prepare_fwd(a, mxq::ACT_IDENTITY, 0.0f, 0, M, K, x, ld_x, nullptr, 0, nullptr, groups, dirs,
+                               row_out, col_out, &noop);
+    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
+    if (noop_flag != nullptr) {
+        // the flag is an input: no output may overlap it
+        std::vector<Range> outs;
+        if (dirs & 1) {
+            outs.push_back(range2d(row_out->codes, M, K, row_out->ld_codes, 1, "row codes"));
+            outs.push_back(range2d(row_out->scales, M, K / 32, row_out->ld_scales, 1, "row scales"));
+        }
+        if (dirs & 2) {
+            outs.push_back(range2d(col_out->codes, M, K, col_out->ld_codes, 1, "col codes"));
+            outs.push_back(range2d(col_out->scales, (M + 31) / 32, K, col_out->ld_scales, 1, "col scales"));
+        }
+        if ((s = check_alias({range2d(noop_flag, 1, 1, 1, 4, "noop_flag")}, outs)) != MXQ_OK) return s;
+    }
+    a.noop = noop_flag;
+    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_quantize_noop launch");
+}
+
+mxq_status mxq_swiglu_quantize_bwd_workspace(int64_t M, int64_t K, uint32_t dirs, size_t *bytes) {
+    (void)dirs;
+    if (bytes == nullptr) return fail(MXQ_ERR_NULL, "bytes is NULL");
+    if (M < 0 || K < 0 || K % 32 != 0) return fail(MXQ_ERR_SHAPE, "M, K must be >= 0 and K % 32 == 0");
+    *bytes = (M == 0 || K == 0) ? 0 : mxq::bwd_workspace_bytes(M, K);
+    return ok();
+}
+
+mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, const uint16_t *grad, int64_t ld_grad,
+                                   const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
+                                   const float *row_scale, const mxq_groups *groups, uint16_t *dgate,
+                                   int64_t ld_dgate, uint16_t *dup, int64_t ld_dup, float *dscale, uint32_t dirs,
+                                   const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *ws,
+                                   size_t ws_bytes, void *stream) {
+    float limit;
+    int il;
+    const int kind = act_from(act, &limit, &il);
+    if (kind < 0) return fail(MXQ_ERR_UNSUPPORTED, "unknown activation kind %d", act->kind);
+    if (M < 0 || K < 0) return fail(MXQ_ERR_SHAPE, "M = %lld and K = %lld must be >= 0", (long long)M, (long long)K);
+    if (K % 32 != 0) return fail(MXQ_ERR_SHAPE, "K = %lld must be a multiple of 32", (long long)K);
+    if (dirs > 3) return fail(MXQ_ERR_SHAPE, "dirs = %u must be 0, ROWWISE, COLWISE or both", dirs);
+    mxq_status si = check_interleave(kind, il, K);
+    if (si != MXQ_OK) return si;
+    const bool unary = kind == mxq::ACT_SRELU;
+    if (unary) {
+        if (up != nullptr || dup != nullptr) return fail(MXQ_ERR_SHAPE, "SReLU is unary: up and dup must be NULL");
+    } else if ((dgate == nullptr) != (dup == nullptr)) {
+        return fail(MXQ_ERR_NULL, "dgate and dup must both be given or both NULL");
+    }
+    if (il && dgate != nullptr && (dup != dgate + il || ld_dup != ld_dgate))
+        return fail(MXQ_ERR_SHAPE, "with glu_interleave = %d the gradient is interleaved too: dup must be dgate + %d "
+                    "with the same pitch", il, il);
+    const int64_t KO = unary ? K : 2 * K;   // columns of the MXFP8 gradient
+    if (dirs == 0 && dgate == nullptr && dscale == nullptr)
+        return fail(MXQ_ERR_SHAPE, "nothing requested: dirs = 0 with no dense output and no dscale");
+    if (kind == mxq::ACT_CLAMPED && !(limit > 0.0f)) return fail(MXQ_ERR_SHAPE, "clamped SwiGLU needs a limit > 0");
+    std::vector<Range> ins, outs;
+    GroupsOut go;
+    mxq_status s = check_groups(groups, (dirs & 2) != 0, go, ins);
+    if (s != MXQ_OK) return s;
+    if (M == 0 || K == 0) return ok();
+    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 30))
+        return fail(MXQ_ERR_OVERFLOW, "M or K beyond the supported range");
+    if ((s = check_bf16_in(grad, M, K, ld_grad, "grad", ins)) != MXQ_OK) return s;
+    if ((s = check_bf16_in(gate, M, gate_span(K, il), ld_gate, unary ? "x" : "gate", ins)) != MXQ_OK) return s;
+    if (!unary && (s = check_bf16_in(up, M, gate_span(K, il), ld_up, "up", ins)) != MXQ_OK) return s;
+    if (row_scale) {
+        if (!aligned(row_scale, 4)) return fail(MXQ_ERR_ALIGN, "row_scale must be 4-byte aligned");
+        ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
+    }
+    if (dgate && unary) {
+        if (ld_dgate < K) return fail(MXQ_ERR_SHAPE, "ld of dx must be >= K");
+        if (!aligned(dgate, 16) || ld_dgate % 8 != 0)
+            return fail(MXQ_ERR_ALIGN, "the dx pointer and pitch must be multiples of 16 bytes");
+        if (!extent_ok(M, ld_dgate, 2)) return fail(MXQ_ERR_OVERFLOW, "dx extent too large");
+        outs.push_back(range2d(dgate, M, K, ld_dgate, 2, "dx"));
+    } else if (dgate) {
+        const int64_t span = gate_span(K, il);
+        if (ld_dgate < span || ld_dup < span) return fail(MXQ_ERR_SHAPE, "ld_dgate / ld_dup too small");
+        if (!aligned(dgate, 16) || !aligned(dup, 16) || ld_dgate % 8 != 0 || ld_dup % 8 != 0)
+            return fail(MXQ_ERR_ALIGN, "dgate / dup pointers and pitches must be multiples of 16 bytes");
+        if (!extent_ok(M, ld_dgate, 2) || !extent_ok(M, ld_dup, 2))
+            return fail(MXQ_ERR_OVERFLOW, "dgate / dup extent too large");
+        if (il) {
+            // the interleaved [dgate | dup] is one (M x 2K) output
+            outs.push_back(range2d(dgate, M, 2 * K, ld_dgate, 2, "dgate|dup"));
+        } else {
+            outs.push_back(range2d(dgate, M, K, ld_dgate, 2, "dgate"));
+            outs.push_back(range2d(dup, M, K, ld_dup, 2, "dup"));
+        }
+    }
+    if (dscale) {
+        if (!aligned(dscale, 4)) return fail(MXQ_ERR_ALIGN, "dscale must be 4-byte aligned");
+        outs.push_back(range2d(dscale, 1, M, M, 4, "dscale"));
+        const size_t need = mxq::bwd_workspace_bytes(M, K);
+        if (need > 0) {
+            if (ws == nullptr || ws_bytes < need)
+                return fail(MXQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? (size_t)0 : ws_bytes);
+            if (!aligned(ws, 4)) return fail(MXQ_ERR_ALIGN, "workspace must be 4-byte aligned");
+            outs.push_back(range2d(ws, 1, (int64_t)need, (int64_t)need, 1, "workspace"));
+        }
+    }
+    const int64_t G = go.g.G;
+    if (dirs & 1) {
+        if ((s = check_mx_out(row_out, true, M, KO, M, "rowwise", outs)) != MXQ_OK) return s;
+    } else if (row_out != nullptr && row_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");
+    }
+    if (dirs & 2) {
+        if ((s = check_mx_out(col_out, false, M, KO, (M + 31) / 32, "colwise", outs)) != MXQ_OK)
+            return s;
+    } else if (col_out != nullptr && col_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
+    }
+    if (mxq::act_quant_launch_threads(M, K, G, (dirs & 2) && G > 0, true) >= (int64_t(1) << 32))
+        return fail(MXQ_ERR_OVERFLOW, "launch beyond 2^32 work-items");
+    if ((s = check_alias(ins, outs)) != MXQ_OK) return s;
+
+    mxq::BwdArgs a{};
+    a.act = kind;
+    a.limit = limit;
+    a.M = M;
+    a.K = K;
+    a.grad = grad; a.ld_grad = ld_grad;
+    a.gate = gate; a.ld_gate = ld_gate;
+    a.up = unary ? nullptr : up; a.ld_up = ld_up;
+    a.il = il;
+    a.row_scale = row_scale;
+    a.groups = go.g;
+    a.dgate = dgate; a.ld_dgate = ld_dgate;
+    a.dup = dup; a.ld_dup = ld_dup;
+    a.dscale = dscale;
+    a.dirs = dirs;
+    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.partials = static_cast<float *>(ws);
+    return hip_status(mxq::launch_act_quant_bwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_bwd launch");
+}
+
+mxq_status mxq_swiglu_quantize_bwd_noalloc(const mxq_act *act, int64_t M, int64_t K, const uint16_t *grad,
+                                           int64_t ld_grad, const uint16_t *gate, int64_t ld_gate,
+                                           const uint16_t *up, int64_t ld_up, const float *row_scale,
+                                           const mxq_groups *groups, uint16_t *dgate, int64_t ld_dgate,
+                                           uint16_t *dup, int64_t ld_dup, float *dscale, uint32_t dirs,
+                                           const mxq_mx_out *row_out, const mxq_mx_out *col_out, void *stream) {
+    // the size check needs no device; the scratch's address is looked up
+    // only for a call that fits it
+    const size_t need = (dscale != nullptr && M > 0 && K > 0 && K % 32 == 0) ? mxq::bwd_workspace_bytes(M, K) : 0;
+    const size_t cap = mxq::bwd_scratch_capacity();
+    if (need > cap)
+        return fail(MXQ_ERR_WORKSPACE,
+                    "the allocation-free backward needs %zu bytes of scratch for dscale at M = %lld, K = %lld; "
+                    "the library's scratch holds %zu (use mxq_swiglu_quantize_bwd with a workspace)",
+                    need, (long long)M, (long long)K, cap);
+    float *scratch = nullptr;
+    if (need > 0) {
+        const hipError_t e = mxq::bwd_scratch(&scratch);
+        if (e != hipSuccess) return hip_status(e, "mxq_swiglu_quantize_bwd_noalloc scratch lookup");
+    }
+    return mxq_swiglu_quantize_bwd(act, M, K, grad, ld_grad, gate, ld_gate, up, ld_up, row_scale, groups, dgate,
+                                   ld_dgate, dup, ld_dup, dscale, dirs, row_out, col_out, scratch,
+                                   need > 0 ? cap : 0, stream);
+}
+
+// K-grouped launches keep one counter of their dynamic tile order in the
+// workspace (256 bytes keep the allocation's alignment simple).
+static size_t gemm_ws_bytes(const mxq_gemm_args &a) { return a.mode == MXQ_GEMM_TN ? 256 : 0; }
+
 
 mxq_status mxq_grouped_gemm_workspace(const mxq_gemm_args *args, size_t *bytes) {
     if (args == nullptr || bytes == nullptr) return fail(MXQ_ERR_NULL, "args and bytes are required");

@@ -23,14 +23,16 @@ struct Groups {
     const int64_t *block_off;
 };
 
-enum Act { ACT_SWIGLU = 0, ACT_CLAMPED = 1, ACT_IDENTITY = 2 };
+// ACT_SRELU is unary (x in `gate`, no `up`); ACT_IDENTITY is the plain quantizer.
+enum Act { ACT_SWIGLU = 0, ACT_CLAMPED = 1, ACT_IDENTITY = 2, ACT_SRELU = 3 };
 
 struct FwdArgs {
     int act;            // Act
     float limit;
     int64_t M, K;
-    const uint16_t *gate; int64_t ld_gate;   // x for ACT_IDENTITY
-    const uint16_t *up; int64_t ld_up;       // unused for ACT_IDENTITY
+    const uint16_t *gate; int64_t ld_gate;   // x for ACT_IDENTITY / ACT_SRELU
+    const uint16_t *up; int64_t ld_up;       // unused for ACT_IDENTITY / ACT_SRELU
+    int il;                                  // GLU interleave block (0: gate and up not interleaved)
     const float *row_scale;                  // NULL => 1
     Groups groups;
     unsigned dirs;
@@ -44,10 +46,11 @@ struct BwdArgs {
     int64_t M, K;
     const uint16_t *grad; int64_t ld_grad;
     const uint16_t *gate; int64_t ld_gate;
-    const uint16_t *up; int64_t ld_up;
+    const uint16_t *up; int64_t ld_up;       // unused for ACT_SRELU
+    int il;                                  // GLU interleave block (0: none)
     const float *row_scale;
     Groups groups;
-    uint16_t *dgate; int64_t ld_dgate;
+    uint16_t *dgate; int64_t ld_dgate;       // dx for ACT_SRELU
     uint16_t *dup; int64_t ld_dup;
     float *dscale;
     unsigned dirs;

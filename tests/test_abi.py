@@ -128,6 +128,32 @@ def test_bwd_validation(m):
     assert st == 8, m.last_error()
 
 
+def test_activation_variant_validation(m):
+    """SReLU is unary (no up, no dup); the GLU interleave block must be a
+    positive multiple of 32 dividing K, applies to the SwiGLU kinds only, and
+    makes the backward's dense gradient interleaved (dup = dgate + B)."""
+    lib = m.lib
+    assert fwd(m, act=m.mxq_act(2, 7.0, 0)) == 2                  # SReLU with an up pointer
+    assert fwd(m, act=m.mxq_act(0, 7.0, 48)) == 2                 # block not a multiple of 32
+    assert fwd(m, act=m.mxq_act(0, 7.0, -32)) == 2
+    assert fwd(m, K=96, ldg=256, ldu=256, up=96 * 2, act=m.mxq_act(0, 7.0, 64)) == 2   # 96 % 64
+    # interleaved gate / up views span 2K - B columns: a pitch of K is too small
+    assert fwd(m, K=64, ldg=64, ldu=64, up=32 * 2, act=m.mxq_act(0, 7.0, 32)) == 2
+    K, M = 64, 64
+    row = m.mxq_mx_out(BASE + (4 << 24), 2 * K, BASE + (5 << 24), 2 * K // 32)
+
+    def bwd(act, dgate, dup, up=fake(64), ldd=128):
+        return lib.mxq_swiglu_quantize_bwd(ctypes.byref(act), M, K, fake(3 << 24), K, fake(0), 2 * K, up, 2 * K,
+                                           None, None, dgate, ldd, dup, ldd, None, 1, ctypes.byref(row), None,
+                                           None, 0, None)
+    il = m.mxq_act(0, 7.0, 32)
+    assert bwd(il, fake(1 << 28), fake((1 << 28) + 128)) == 2     # dup must be dgate + B elements
+    srelu = m.mxq_act(2, 7.0, 0)
+    assert bwd(srelu, fake(1 << 28), fake((1 << 28) + 128), up=None) == 2   # SReLU has no dup
+    assert bwd(srelu, fake(1 << 28), None, up=fake(64)) == 2                # nor an up input
+    assert bwd(m.mxq_act(2, 7.0, 32), fake(1 << 28), None, up=None) == 2    # nor an interleave
+
+
 def test_offsets_validation(m):
     lib = m.lib
     assert lib.mxq_splits_to_offsets(None, 4, fake(64), None, None, None) == 1
