@@ -142,6 +142,40 @@ def test_srelu_grouped_and_special_values(mxq):
     assert_exact(rep)
 
 
+def test_swiglu_backward_infinite_gate_dscale(mxq):
+    """An infinite gate makes a = bf16(silu(g)) infinite (or NaN for -Inf):
+    dscale's fast sum and its exact-path correction must give the oracle's
+    +-Inf / NaN row sums, not a NaN from Inf - Inf (regression)."""
+    M, K = 64, 128
+    p = W.packed_gate_up(M, K, seed=81)
+    pb = bits(p)
+    pb[3, 5] = 0x7F80          # +Inf gate
+    pb[7, 9] = 0xFF80          # -Inf gate
+    pb[11, 2] = 0x7F80
+    pb[11, K + 2] = 0x0000     # +Inf gate times a zero up
+    pt = W.from_bits(pb, "cuda")
+    sc = W.row_scale(M, seed=81)
+    dy = W.grad_out(M, K, seed=81)
+    r = O.swiglu_quantize_bwd(bits(dy), pb[:, :K], pb[:, K:], sc.numpy(), 3, want_close=True)
+    out = mxq.swiglu_quantize_bwd(dy.cuda(), pt[:, :K], pt[:, K:], sc.cuda(), True, True)
+    torch.cuda.synchronize()
+    rep = {}
+    closeb = r[7] != 0
+    compare_mx("row", u8(out[0]), u8(out[2]), r[0], r[2], closeb, True, report=rep)
+    compare_mx("col", u8(out[1]), u8(out[3]), r[1], r[3], closeb, False, rowblock_of(M), report=rep)
+    dd = bits(out[4])
+    compare_bf16("dgate", dd[:, :K], r[4], closeb[:, :K], rep)
+    compare_bf16("dup", dd[:, K:], r[5], closeb[:, K:], rep)
+    got, ref = out[5].cpu().numpy().astype(np.float64), r[6].astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    inf = np.isinf(ref)
+    assert inf.sum() + np.isnan(ref).sum() >= 2
+    assert np.array_equal(got[inf], ref[inf])
+    fin = np.isfinite(ref)
+    assert np.all(np.abs(got[fin] - ref[fin]) <= r[8][fin] + 1e-30)
+    assert_exact(rep)
+
+
 # ------------------------------------------------------------------ GLU interleave
 
 @pytest.mark.parametrize("B,K", [(32, 128), (128, 768), (256, 768), (64, 2048)])
