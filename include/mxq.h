@@ -347,6 +347,31 @@ mxq_status mxq_grouped_gemm_workspace(const mxq_gemm_args *args, size_t *bytes);
 mxq_status mxq_grouped_gemm(const mxq_gemm_args *args, void *ws, size_t ws_bytes,
                             void *stream);
 
+/*
+ * FC1 grouped GEMM with the row-scaled SwiGLU and its MXFP8 quantization in
+ * the epilogue (TE3238, discussion: the activation plus its grouped
+ * quantization fused with the grouped linear, the FC1 - activation - FC2
+ * module; TAO4743, Summary: the bf16 activation is never stored).  A bf16 NT
+ * grouped GEMM as mxq_grouped_gemm (args->mode = MXQ_GEMM_NT, bf16 operands
+ * and output, N a multiple of 256, no workspace), whose B rows hold gate and
+ * up interleaved in blocks of 128 (act->glu_interleave must be 128): rows
+ * 256 t .. 256 t + 127 of each B_g are gate rows 128 t .. 128 t + 127 and the
+ * next 128 the matching up rows.  It writes the bf16 product to args->out as
+ * usual (the interleaved [gate | up], kept for the backward) and, from the
+ * same registers, the MXFP8 activation of (M x N/2) with
+ *     a = bf16(silu(gate)), h = bf16(a * up * row_scale[r])
+ * (act->kind SwiGLU or clamped SwiGLU), rowwise and / or colwise with the
+ * colwise 32-row blocks restarting at every group (scale rows through
+ * args->block_off, required for MXQ_COLWISE).  The codes and scales equal
+ * those of mxq_swiglu_quantize_fwd applied to args->out with the same act.
+ *   row_scale  device fp32[M] or NULL (s = 1)
+ *   row_out, col_out as for mxq_swiglu_quantize_fwd with K = N/2
+ */
+mxq_status mxq_grouped_gemm_swiglu(const mxq_gemm_args *args, const mxq_act *act,
+                                   const float *row_scale, uint32_t dirs,
+                                   const mxq_mx_out *row_out, const mxq_mx_out *col_out,
+                                   void *stream);
+
 /* ------------------------------------------------------------------- misc */
 
 const char *mxq_status_string(mxq_status s);

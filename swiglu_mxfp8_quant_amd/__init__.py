@@ -42,7 +42,7 @@ EXPORTS = [
     "mxq_splits_to_offsets", "mxq_swiglu_quantize_fwd", "mxq_swiglu_quantize_bwd_workspace",
     "mxq_swiglu_quantize_bwd", "mxq_swiglu_quantize_bwd_noalloc", "mxq_quantize", "mxq_quantize_noop",
     "mxq_grouped_gemm_workspace",
-    "mxq_grouped_gemm",
+    "mxq_grouped_gemm", "mxq_grouped_gemm_swiglu",
     "mxq_status_string", "mxq_last_error_message", "mxq_version",
 ]
 
@@ -105,6 +105,8 @@ def _load():
                               ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P, P],
         "mxq_grouped_gemm_workspace": [ctypes.POINTER(mxq_gemm_args), ctypes.POINTER(ctypes.c_size_t)],
         "mxq_grouped_gemm": [ctypes.POINTER(mxq_gemm_args), P, ctypes.c_size_t, P],
+        "mxq_grouped_gemm_swiglu": [ctypes.POINTER(mxq_gemm_args), ctypes.POINTER(mxq_act), P, U32,
+                                    ctypes.POINTER(mxq_mx_out), ctypes.POINTER(mxq_mx_out), P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -243,6 +245,11 @@ def mxq_grouped_gemm_workspace(args):
     n = ctypes.c_size_t(0)
     check(lib.mxq_grouped_gemm_workspace(ctypes.byref(args), ctypes.byref(n)))
     return n.value
+
+
+def mxq_grouped_gemm_swiglu(args, act, row_scale, dirs, row_out, col_out, stream=None):
+    return lib.mxq_grouped_gemm_swiglu(ctypes.byref(args), _byref(act), _ptr(row_scale), dirs, _byref(row_out),
+                                       _byref(col_out), _stream(stream))
 
 
 def mxq_grouped_gemm(args, ws=None, stream=None):
@@ -438,3 +445,37 @@ def grouped_gemm(mode, row_off, A, B, out, A_scales=None, B_scales=None, block_o
         _hold(ws, stream)
     check(mxq_grouped_gemm(args, ws, stream))
     return out
+
+
+def grouped_gemm_swiglu(row_off, x, w13, out, scale=None, rowwise=True, colwise=False, block_off=None,
+                        n_col_blocks=None, clamped=False, limit=7.0, max_workgroups=0, stream=None):
+    """FC1 with the row-scaled SwiGLU + MXFP8 in its epilogue: x (R, H) bf16,
+    w13 (G, 2I, H) bf16 whose rows interleave gate and up in blocks of 128,
+    out (R, 2I) bf16 (the interleaved product).  Returns the MXFP8 activation
+    (codes_row, codes_col, scales_row, scales_col) of (R, I); a disabled
+    direction comes back zero-sized."""
+    G = row_off.numel() - 1
+    R, H = x.shape
+    N = w13.shape[1]
+    I = N // 2
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if n_col_blocks is None:
+        n_col_blocks = colwise_scale_rows_bound(R, G)
+    rc, cc, rs, cs = _alloc_mx(R, I, dirs, n_col_blocks, x.device)
+    ro, co = _outs(rc, cc, rs, cs, dirs)
+    args = mxq_gemm_args(GEMM_NT, G, row_off.data_ptr(), None if block_off is None else block_off.data_ptr(),
+                         R, N, H, R, _operand(x), _operand(w13, None, group_dim=True), DTYPE_BF16, out.data_ptr(),
+                         out.stride(0), 0, 0, int(max_workgroups))
+    act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit, 128)
+    check(mxq_grouped_gemm_swiglu(args, act, scale, dirs, ro, co, stream))
+    return rc, cc, rs, cs
+
+
+def interleave_rows(w, block=128):
+    """(G, 2I, X) with rows [gate | up] -> rows interleaved in blocks of `block`
+    (gate 0..block-1, up 0..block-1, gate block.., ...): the weight layout the
+    fused FC1 epilogue reads.  A one-time layout change of a stored weight."""
+    G, I2, X = w.shape
+    I = I2 // 2
+    nb = I // block
+    return w.view(G, 2, nb, block, X).transpose(1, 2).reshape(G, I2, X).contiguous()

@@ -564,4 +564,66 @@ mxq_status mxq_grouped_gemm(const mxq_gemm_args *args, void *ws, size_t ws_bytes
     return hip_status(mxq::launch_grouped_gemm(g, (hipStream_t)stream), "mxq_grouped_gemm launch");
 }
 
+mxq_status mxq_grouped_gemm_swiglu(const mxq_gemm_args *args, const mxq_act *act, const float *row_scale,
+                                   uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out,
+                                   void *stream) {
+    if (args == nullptr || act == nullptr) return fail(MXQ_ERR_NULL, "args and act are required");
+    mxq::GemmArgs g{};
+    std::string err;
+    const int st = mxq::gemm_prepare(*args, g, err);
+    if (st != MXQ_OK) return fail((mxq_status)st, "%s", err.c_str());
+    if (args->mode != MXQ_GEMM_NT || args->A.dtype != MXQ_DTYPE_BF16 || args->out_dtype != MXQ_DTYPE_BF16)
+        return fail(MXQ_ERR_UNSUPPORTED, "the fused SwiGLU epilogue is built for bf16 NT GEMMs with a bf16 output");
+    float limit;
+    int il;
+    const int kind = act_from(act, &limit, &il);
+    if (kind != mxq::ACT_SWIGLU && kind != mxq::ACT_CLAMPED)
+        return fail(MXQ_ERR_UNSUPPORTED, "the fused epilogue computes SwiGLU or clamped SwiGLU");
+    if (il != 128)
+        return fail(MXQ_ERR_SHAPE, "the fused epilogue needs B's gate and up rows interleaved in blocks of 128 "
+                    "(act->glu_interleave = 128), got %d", il);
+    if (args->N % 256 != 0) return fail(MXQ_ERR_SHAPE, "N = %lld must be a multiple of 256", (long long)args->N);
+    if (kind == mxq::ACT_CLAMPED && !(limit > 0.0f)) return fail(MXQ_ERR_SHAPE, "clamped SwiGLU needs a limit > 0");
+    if (dirs < 1 || dirs > 3) return fail(MXQ_ERR_SHAPE, "dirs = %u must be ROWWISE, COLWISE or both", dirs);
+    if ((dirs & 2) && args->block_off == nullptr)
+        return fail(MXQ_ERR_NULL, "colwise output needs block_off (the groups' first colwise scale rows)");
+    if (row_scale != nullptr && !aligned(row_scale, 4)) return fail(MXQ_ERR_ALIGN, "row_scale must be 4-byte aligned");
+    const int64_t M = args->M, KA = args->N / 2;
+    std::vector<Range> ins, outs;
+    mxq_status s;
+    if (dirs & 1) {
+        if ((s = check_mx_out(row_out, true, M, KA, M, "rowwise", outs)) != MXQ_OK) return s;
+    } else if (row_out != nullptr && row_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");
+    }
+    if (dirs & 2) {
+        if ((s = check_mx_out(col_out, false, M, KA, (M + 31) / 32, "colwise", outs)) != MXQ_OK) return s;
+    } else if (col_out != nullptr && col_out->codes != nullptr) {
+        return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
+    }
+    if (check_gemm_alias(*args) != MXQ_OK) return MXQ_ERR_ALIAS;
+    // the activation's outputs against every input and the bf16 output
+    ins.push_back(range2d(args->A.data, M, args->K, args->A.ld, 2, "A"));
+    ins.push_back(range_groups(args->B.data, args->G, args->B.gstride, args->N, args->K, args->B.ld, 2, "B"));
+    ins.push_back(range2d(args->row_off, 1, args->G + 1, args->G + 1, 8, "row_off"));
+    if (args->block_off) ins.push_back(range2d(args->block_off, 1, args->G + 1, args->G + 1, 8, "block_off"));
+    if (row_scale) ins.push_back(range2d(row_scale, 1, M, M, 4, "row_scale"));
+    outs.push_back(range2d(args->out, M, args->N, args->ld_out, 2, "out"));
+    if ((s = check_alias(ins, outs)) != MXQ_OK) return s;
+    if (g.noop) return ok();
+    g.epi_act = kind == mxq::ACT_CLAMPED ? 2 : 1;
+    g.epi_limit = limit;
+    g.epi_scale = row_scale;
+    g.epi_dirs = dirs;
+    if (dirs & 1) {
+        g.epi_rc = row_out->codes; g.epi_ld_rc = row_out->ld_codes;
+        g.epi_rs = row_out->scales; g.epi_ld_rs = row_out->ld_scales;
+    }
+    if (dirs & 2) {
+        g.epi_cc = col_out->codes; g.epi_ld_cc = col_out->ld_codes;
+        g.epi_cs = col_out->scales; g.epi_ld_cs = col_out->ld_scales;
+    }
+    return hip_status(mxq::launch_grouped_gemm(g, (hipStream_t)stream), "mxq_grouped_gemm_swiglu launch");
+}
+
 }  // extern "C"

@@ -32,6 +32,16 @@ struct GemmArgs {
     int max_workgroups;
     int *sched;             // K-grouped: device counter of the dynamic tile order (workspace)
     bool noop;
+    // The fused SwiGLU epilogue (bf16 NT launches whose B rows hold gate and
+    // up interleaved in blocks of 128, so that every 256-column output tile
+    // holds 128 gate and the matching 128 up columns): the activation of the
+    // tile, quantized to MXFP8 rowwise and/or colwise, besides the bf16 output.
+    int epi_act;            // 0: none; 1: SwiGLU; 2: clamped SwiGLU
+    float epi_limit;
+    const float *epi_scale; // row scale (NULL: 1)
+    unsigned epi_dirs;      // 1 rowwise, 2 colwise (scale rows through block_off), 3 both
+    uint8_t *epi_rc, *epi_rs, *epi_cc, *epi_cs;   // codes / scales of each direction
+    int64_t epi_ld_rc, epi_ld_rs, epi_ld_cc, epi_ld_cs;
 };
 
 // Validates the public arguments; returns an mxq_status and an error text.

@@ -44,6 +44,12 @@
 //     N side), so every lane owns 4 consecutive output columns of one row; a
 //     bf16 tile is staged through LDS so that each output row leaves as 512
 //     contiguous bytes, fp32 goes straight from the accumulators.
+//   * A bf16 NT launch can carry the row-scaled SwiGLU in its epilogue (FC1
+//     with the gate / up rows of its weight interleaved in blocks of 128): the
+//     staged quarter tiles that leave as the bf16 output are also turned into
+//     the MXFP8 activation, rowwise and / or colwise (page "Activation +
+//     GroupedLinear Fusion for MOE and other MOE optimizations", discussion:
+//     the activation and its quantization fused with the grouped GEMM).
 //   * Group boundaries come from the device offsets only.  Each workgroup of
 //     an M-grouped launch first builds the groups' m-tile prefix sums in LDS
 //     (for up to 1024 groups; beyond that every lookup scans the offsets), so
@@ -57,6 +63,7 @@
 //     (skewed group sizes) take their tiles largest group first from a
 //     counter in the caller's workspace instead.
 #include "gemm_internal.h"
+#include "act_math.h"
 
 #include <string>
 #include <type_traits>
@@ -519,6 +526,10 @@ struct Tile {
     int ksteps;
     int item;
     int valid;
+    // fused epilogue only: the tile's first output row and column, and the
+    // colwise scale row of its first 32-row block (tiles start at a group's
+    // first row plus a multiple of 256, so their 32-row blocks are the group's)
+    int64_t m0, n0, srow;
 };
 
 // A persistent grid (one workgroup per CU at most): workgroup j of XCD x runs
@@ -537,8 +548,12 @@ struct Tile {
 // barrier that follows the last read of that slot's earlier group; blocks
 // past the contraction take the unit scale in registers, so bytes read past a
 // row's end are harmless).
-template <int MODE, int DT, int OUT, bool TAB, int SC>
+// EPI (bf16 NT with a bf16 output only): 0, or the fused SwiGLU epilogue
+// (1 plain, 2 clamped; see fused_act below).
+template <int MODE, int DT, int OUT, bool TAB, int SC, int EPI = 0>
 __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm_ub) {
+    static_assert(EPI == 0 || (MODE == MODE_NT && DT == MXQ_DTYPE_BF16 && OUT == MXQ_DTYPE_BF16),
+                  "the fused epilogue is built for bf16 NT launches with a bf16 output");
     constexpr bool F8_ = (DT == MXQ_DTYPE_MXFP8_E4M3);
     constexpr bool XKS_ = (MODE != MODE_NT), YKS_ = (MODE == MODE_TN);
     constexpr bool XRING = F8_ && !XKS_ && SC == 2, YRING = F8_ && !YKS_ && SC == 2;
@@ -752,6 +767,11 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             T.ys = sa.A.scales + m0 * ldsa;
             T.o = static_cast<uint8_t *>(sa.out) + (m0 * sa.ld_out + n0) * OSZ;
             T.yv = (int)(r1 - m0 < BT ? r1 - m0 : BT);
+            if constexpr (EPI != 0) {
+                T.m0 = m0;
+                T.n0 = n0;
+                T.srow = (sa.epi_dirs & 2) ? sa.block_off[g] + (m0 - r0) / 32 : 0;
+            }
             T.kext = (int)(sa.K * ESZ);
             T.nblk = (int)((sa.K + 31) / 32);
             T.ksteps = (T.kext + BK - 1) / BK;
@@ -953,6 +973,148 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         }
     };
 
+    // ---- the fused SwiGLU epilogue.  Quarter h of a bf16 tile sits in the
+    // staging buffer: 64 rows x 256 columns, staging row m < 32 being tile row
+    // 32h + m and m >= 32 tile row 128 + 32h + m - 32 (so rows 0..31 and
+    // 32..63 are two whole 32-row colwise blocks).  B's rows hold gate and up
+    // interleaved in blocks of 128, so tile columns 0..127 are the gate and
+    // 128..255 the up of activation columns n0/2 .. n0/2 + 127.  Thread t
+    // takes the items (m, q) = (i / 16, i % 16), i = 256 it + t, it < 4: the 8
+    // activation columns 8q .. 8q + 7 of staging row m.  The 4 lanes of a 1x32
+    // block are then 4 consecutive lanes (a DPP quad), items 0-1 lie in the
+    // first 32-row block and 2-3 in the second, and the lanes of a wave with
+    // one q hold 8 rows of each block.  The arithmetic is the fused
+    // activation kernels' (act_math.h), exact path included, so the codes and
+    // scales are those of mxq_swiglu_quantize_fwd applied to the bf16 output.
+    __shared__ uint32_t emx[EPI ? NTHR / 64 * 2 * 16 * 4 : 1];   // per-wave colwise maxima
+    auto fused_act = [&](const Tile &T, const uint8_t *stg, int h, int yv) {
+        if constexpr (EPI != 0) {
+            constexpr int ACT = EPI == 2 ? ACT_CLAMPED : ACT_SWIGLU;
+            const unsigned dirs = sa.epi_dirs;
+            const float L = sa.epi_limit;
+            const float *scale = sa.epi_scale;
+            const int64_t j0 = T.n0 / 2, m0 = T.m0;
+            const int q = tid & 15;
+            uint32_t hv[4][4];
+            uint32_t fix = 0;   // elements the fast path may round differently (bit 8 it + k)
+#pragma unroll
+            for (int it = 0; it < 4; it++) {
+                const int m = (it * NTHR + tid) >> 4;
+                const int tr = (m < 32 ? 32 * h : 128 + 32 * h - 32) + m;
+                const bool valid = tr < yv;
+                const u32x4_t gw = *reinterpret_cast<const u32x4_t *>(stg + m * 512 + 16 * (q ^ (m & 31)));
+                const u32x4_t uw = *reinterpret_cast<const u32x4_t *>(stg + m * 512 + 16 * ((16 + q) ^ (m & 31)));
+                const uint32_t g4[4] = {gw.x, gw.y, gw.z, gw.w}, u4[4] = {uw.x, uw.y, uw.z, uw.w};
+                const float s = (valid && scale != nullptr) ? scale[m0 + tr] : 1.0f;
+                uint32_t bits = 0u;
+#pragma unroll
+                for (int k = 0; k < 4; k++) bits |= fwd_pair<ACT>(g4[k], u4[k], s, L, hv[it][k]) << (2 * k);
+                if (!normal_or_zero(s)) bits = 0xFFu;
+#pragma unroll
+                for (int k = 0; k < 4; k++) hv[it][k] = valid ? hv[it][k] : 0u;   // rows past the group
+                fix |= (valid ? bits : 0u) << (8 * it);
+            }
+            // the flagged elements in fp64, one rolled loop (one copy of that code)
+            while (fix) {
+                const int idx = __builtin_ctz(fix);
+                fix &= fix - 1u;
+                const int it = idx >> 3, k = idx & 7;
+                const int m = (it * NTHR + tid) >> 4;
+                const int tr = (m < 32 ? 32 * h : 128 + 32 * h - 32) + m;
+                const uint8_t *row = stg + m * 512;
+                const float g = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(
+                                                    row + 16 * (q ^ (m & 31)) + 2 * k) << 16);
+                const float u = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(
+                                                    row + 16 * ((16 + q) ^ (m & 31)) + 2 * k) << 16);
+                const float s = scale != nullptr ? scale[m0 + tr] : 1.0f;
+                const uint32_t v = fwd_elem_f64(g, u, s, L, ACT);
+#pragma unroll
+                for (int i2 = 0; i2 < 4; i2++)
+#pragma unroll
+                    for (int w = 0; w < 4; w++)
+                        if (i2 == it && w == (k >> 1))
+                            hv[i2][w] = (k & 1) ? ((hv[i2][w] & 0x0000FFFFu) | (v << 16))
+                                                : ((hv[i2][w] & 0xFFFF0000u) | v);
+            }
+            if (dirs & 1) {
+#pragma unroll
+                for (int it = 0; it < 4; it++) {
+                    const int m = (it * NTHR + tid) >> 4;
+                    const int tr = (m < 32 ? 32 * h : 128 + 32 * h - 32) + m;
+                    uint32_t mm = 0u;
+#pragma unroll
+                    for (int k = 0; k < 4; k++) mm = umax16x2(mm, hv[it][k] & 0x7FFF7FFFu);
+                    mm = block_max<4>(max(mm & 0xFFFFu, mm >> 16));
+                    const uint32_t E = e8m0_from_amax_bits(mm);
+                    const u32x2_t c = {cvt4_same(hv[it][0], hv[it][1], E), cvt4_same(hv[it][2], hv[it][3], E)};
+                    if (tr < yv) {
+                        const int64_t r = m0 + tr;
+                        __builtin_nontemporal_store(c, reinterpret_cast<u32x2_t *>(sa.epi_rc + r * sa.epi_ld_rc + j0 +
+                                                                                   8 * q));
+                        if ((q & 3) == 0) sa.epi_rs[r * sa.epi_ld_rs + (j0 + 8 * q) / 32] = (uint8_t)E;
+                    }
+                }
+            }
+            if (dirs & 2) {
+                // column maxima of each 32-row block: the thread's two rows, the
+                // wave's 8 (lanes q, q + 16, q + 32, q + 48), then the 4 waves
+#pragma unroll
+                for (int b = 0; b < 2; b++) {
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {
+                        uint32_t v = umax16x2(hv[2 * b][k] & 0x7FFF7FFFu, hv[2 * b + 1][k] & 0x7FFF7FFFu);
+                        v = umax16x2(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+                        v = umax16x2(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+                        if (lane < 16) emx[((wave * 2 + b) * 16 + lane) * 4 + k] = v;
+                    }
+                }
+                step_barrier<63>();
+#pragma unroll
+                for (int b = 0; b < 2; b++) {
+                    uint32_t cm[4];
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {
+                        uint32_t v = emx[(b * 16 + q) * 4 + k];
+#pragma unroll
+                        for (int w = 1; w < NTHR / 64; w++) v = umax16x2(v, emx[((w * 2 + b) * 16 + q) * 4 + k]);
+                        cm[k] = v;
+                    }
+                    uint32_t E[8];
+                    float sc[8];
+                    uint32_t nanm[2] = {0u, 0u};
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {
+                        E[2 * k] = e8m0_from_amax_bits(cm[k] & 0xFFFFu);
+                        E[2 * k + 1] = e8m0_from_amax_bits(cm[k] >> 16);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; k++) {
+                        sc[k] = scale_operand(E[k]);
+                        nanm[k >> 2] |= (E[k] == 0xFFu ? 0xFFu : 0u) << (8 * (k & 3));
+                    }
+#pragma unroll
+                    for (int i2 = 0; i2 < 2; i2++) {
+                        const int it = 2 * b + i2;
+                        const int m = (it * NTHR + tid) >> 4;
+                        const int tr = (m < 32 ? 32 * h : 128 + 32 * h - 32) + m;
+                        const u32x2_t c = {cvt4_cols(hv[it][0], hv[it][1], sc, nanm[0]),
+                                           cvt4_cols(hv[it][2], hv[it][3], sc + 4, nanm[1])};
+                        if (tr < yv)
+                            __builtin_nontemporal_store(c, reinterpret_cast<u32x2_t *>(
+                                                               sa.epi_cc + (m0 + tr) * sa.epi_ld_cc + j0 + 8 * q));
+                    }
+                    const int tb = b == 0 ? 32 * h : 128 + 32 * h;   // the block's first tile row
+                    if (tid < 16 && tb < yv) {
+                        const u32x2_t e = {E[0] | (E[1] << 8) | (E[2] << 16) | (E[3] << 24),
+                                           E[4] | (E[5] << 8) | (E[6] << 16) | (E[7] << 24)};
+                        __builtin_nontemporal_store(e, reinterpret_cast<u32x2_t *>(
+                                                           sa.epi_cs + (T.srow + tb / 32) * sa.epi_ld_cs + j0 + 8 * q));
+                    }
+                }
+            }
+        }
+    };
+
     // ---- epilogue: lane (g32, l32) holds C[m][n .. n+3] with m = wy + 32y + l32,
     // n = wx + 32x + 8q + 4 g32, in registers 4q .. 4q+3 of acc[x][y].
     const int ldo = (int)(a.ld_out * OSZ);   // output row pitch in bytes (< 2^23)
@@ -1017,6 +1179,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
                     const uint32_t off = ((row < yv) & (8 * c < xv)) ? (uint32_t)(row * ldo_r + 16 * c) : kOOB;
                     __builtin_amdgcn_raw_buffer_store_b128(v[j], ro, off, 0, 2);   // nt
                 }
+                fused_act(T, stg, h, yv);
             }
         } else {
             // fp32: straight from the accumulators
@@ -1305,6 +1468,18 @@ hipError_t launch_mode(const GemmArgs &g, hipStream_t stream) {
     const int a1 = (int)ntn, a2 = (int)ntm;
     const bool tab = g.G <= kTab;
     if (MODE == MODE_TN && g.sched != nullptr) hipLaunchKernelGGL(sched_reset, dim3(1), dim3(64), 0, stream, g.sched);
+    if constexpr (MODE == MODE_NT && DT == MXQ_DTYPE_BF16 && OUT == MXQ_DTYPE_BF16) {
+        if (g.epi_act != 0) {
+            if (g.epi_act == 2) {
+                if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 1, 2>), gd, bd, 0, stream, g, a1, a2);
+                else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 1, 2>), gd, bd, 0, stream, g, a1, a2);
+            } else {
+                if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 1, 1>), gd, bd, 0, stream, g, a1, a2);
+                else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 1, 1>), gd, bd, 0, stream, g, a1, a2);
+            }
+            return hipGetLastError();
+        }
+    }
     if constexpr (DT != MXQ_DTYPE_MXFP8_E4M3 || MODE == MODE_TN) {
         if (tab) hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, true, 1>), gd, bd, 0, stream, g, a1, a2);
         else hipLaunchKernelGGL((gemm_kernel<MODE, DT, OUT, false, 1>), gd, bd, 0, stream, g, a1, a2);

@@ -236,6 +236,37 @@ def test_gemm_output_alias_rejected(m):
     assert lib.mxq_grouped_gemm(ctypes.byref(a), None, 0, None) == 5
 
 
+def test_fused_fc1_validation(m):
+    """The fused FC1 epilogue takes bf16 NT launches with a bf16 output, N a
+    multiple of 256, the weight's gate / up rows interleaved in blocks of 128,
+    a SwiGLU kind, and block_off for colwise output; its activation outputs
+    must not overlap the inputs or the bf16 product."""
+    lib = m.lib
+
+    def args(mode=None, N=256, dtype=None):
+        a = gemm_args(m, m.GEMM_NT if mode is None else mode, N=N)
+        a.A.dtype = a.B.dtype = m.DTYPE_BF16 if dtype is None else dtype
+        a.A.scales = a.B.scales = None
+        a.A.ld, a.B.ld, a.B.gstride = 256, 256, N * 256
+        a.ld_out = N
+        return a
+    row = m.mxq_mx_out(BASE + (6 << 28), 128, BASE + (7 << 28), 4)
+    il = m.mxq_act(0, 7.0, 128)
+
+    def call(a, act=il, dirs=1, r=row):
+        return lib.mxq_grouped_gemm_swiglu(ctypes.byref(a), ctypes.byref(act), None, dirs, ctypes.byref(r), None,
+                                           None)
+    assert call(args(), act=m.mxq_act(0, 7.0, 64)) == 2            # interleave block must be 128
+    assert call(args(), act=m.mxq_act(2, 7.0, 128)) == 6           # SReLU: not a fused kind
+    assert call(args(N=384)) == 2                                   # N % 256
+    assert call(args(), dirs=2) == 1                                # colwise needs block_off
+    assert call(args(), dirs=0) == 2
+    bad = m.mxq_mx_out(BASE + (1 << 28) + 64, 128, BASE + (7 << 28), 4)
+    assert call(args(), r=bad) == 5                                 # codes overlap A
+    bad = m.mxq_mx_out(BASE + (5 << 28) + 64, 128, BASE + (7 << 28), 4)
+    assert call(args(), r=bad) == 5                                 # codes overlap the bf16 product
+
+
 def test_noalloc_backward_refuses_beyond_its_scratch(m):
     """The allocation-free backward checks its scratch size before it touches
     the device: 2^20 rows at K = 8192 need 64 MiB of dscale partials, more than
