@@ -172,10 +172,28 @@ BF16_PEAK_TFLOPS = 2500.0
 MOE_VARIANTS = (("uniform_plain", False, False), ("zipf_plain", True, False), ("zipf_clamped", True, True))
 
 
-def moe_section(m, torch, W, reps=5):
-    """Expert-layer forward + backward: per-GEMM and whole-layer timings."""
-    from swiglu_mxfp8_quant_amd.moe import Layer, gemm_flops
+def timed_alt(torch, fns, reps):
+    """Medians (us) of `reps` rounds that time each of fns once, in turn, on
+    the current stream (alternating, so that clock drift over the run falls
+    on every variant alike)."""
     stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = [[] for _ in fns]
+    for _ in range(reps):
+        for i, fn in enumerate(fns):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts[i].append(e0.elapsed_time(e1) * 1e3)
+    return [sorted(t)[len(t) // 2] for t in ts]
+
+
+def moe_section(m, torch, W, reps=5):
+    """Expert-layer forward + backward: whole-layer timings (plain, with the
+    fused FC1 epilogue, with the weight cache valid), per-GEMM timings, and
+    FC1 + activation unfused against fused."""
+    from swiglu_mxfp8_quant_amd.moe import Layer, gemm_flops
     out = {}
     for name, skewed, clamped in MOE_VARIANTS:
         moe = W.moe_layer(0, device="cuda", skewed=skewed)
@@ -183,33 +201,28 @@ def moe_section(m, torch, W, reps=5):
         H, I, G = cfg["hidden"], cfg["inter"], cfg["experts"]
         R = int(moe["splits"].sum())
         layer = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped)
+        # the same layer with FC1's fused epilogue (its W13 rows interleaved
+        # in blocks of 128)
+        fl = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, fused_fc1=True)
         dy = W.moe_grad(R, H, seed=0, device="cuda")
+        xs, sc = moe["x_perm"], moe["scale"]
 
         def full():
-            layer.forward(moe["x_perm"], moe["scale"])
+            layer.forward(xs, sc)
             layer.backward(dy)
+
+        def full_fused():
+            fl.forward(xs, sc)
+            fl.backward(dy)
         full()
+        full_fused()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ts = []
-        for _ in range(reps):
-            e0.record(stream)
-            full()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        layer_us = sorted(ts)[len(ts) // 2]
-        # the same with the MXFP8 weight cache valid (the device flag skips the
-        # weight quantizations, as on the micro-batches after a weight update)
+        layer_us, fused_us = timed_alt(torch, [full, full_fused], reps)
+        # the plain layer with the MXFP8 weight cache valid (the device flag
+        # skips the weight quantizations, as on the micro-batches after a
+        # weight update)
         layer.mark_weights_current()
-        ts = []
-        for _ in range(reps):
-            e0.record(stream)
-            full()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        cached_us = sorted(ts)[len(ts) // 2]
+        cached_us, = timed_alt(torch, [full], reps)
         layer.mark_weights_changed()
         s, gr, ro, bo = layer.saved, layer.grads, layer.row_off, layer.block_off
         h13 = torch.empty_like(s["h13"])
@@ -217,7 +230,7 @@ def moe_section(m, torch, W, reps=5):
         da, dx = torch.empty_like(gr["da"]), torch.empty_like(gr["dx"])
         dw2, dw13 = torch.empty_like(gr["dw2"]), torch.empty_like(gr["dw13"])
         calls = {
-            "fc1_fwd": (lambda: m.grouped_gemm(m.GEMM_NT, ro, moe["x_perm"], moe["w13"], h13), "bf16"),
+            "fc1_fwd": (lambda: m.grouped_gemm(m.GEMM_NT, ro, xs, moe["w13"], h13), "bf16"),
             "fc2_fwd": (lambda: m.grouped_gemm(m.GEMM_NT, ro, s["a_r"], s["w2q"], y, s["as_r"], s["w2s"]), "fp8"),
             "fc2_dgrad": (lambda: m.grouped_gemm(m.GEMM_NN, ro, gr["dy_r"], gr["w2c"], da, gr["dys_r"], gr["w2cs"]),
                           "fp8"),
@@ -232,24 +245,29 @@ def moe_section(m, torch, W, reps=5):
         per, tot_fl, tot_us = {}, 0.0, 0.0
         for k, (fn, dt) in calls.items():
             fn()
-            ts = []
-            for _ in range(reps):
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1) * 1e3)
-            us = sorted(ts)[len(ts) // 2]
+            us, = timed_alt(torch, [fn], reps)
             tf = flops[k] / us / 1e6
             peak = FP8_PEAK_TFLOPS if dt == "fp8" else BF16_PEAK_TFLOPS
             per[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": dt, "frac_peak": round(tf / peak, 4)}
             tot_fl += flops[k]
             tot_us += us
+        # FC1 + the activation's MXFP8 both ways: the bf16 FC1, then the fused
+        # activation kernel, against FC1 with the activation in its epilogue
+        unfused = lambda: (m.grouped_gemm(m.GEMM_NT, ro, xs, moe["w13"], h13),
+                           m.swiglu_quantize_fwd(h13[:, :I], h13[:, I:], sc, True, True, ro, bo,
+                                                 clamped=clamped, limit=layer.limit))
+        fused = lambda: m.grouped_gemm_swiglu(ro, xs, fl.w13, h13, sc, True, True, block_off=bo,
+                                              clamped=clamped, limit=layer.limit)
+        unfused()
+        fused()
+        fc1_act_us = [round(v, 1) for v in timed_alt(torch, [unfused, fused], reps)]
         out[name] = {"routed_rows": R, "layer_fwd_bwd_us": round(layer_us, 1),
+                     "layer_fwd_bwd_fused_fc1_us": round(fused_us, 1),
                      "layer_fwd_bwd_cached_weights_us": round(cached_us, 1),
+                     "fc1_plus_activation_fwd_us": {"unfused": fc1_act_us[0], "fused": fc1_act_us[1]},
                      "gemm_total_us": round(tot_us, 1), "gemm_TFLOPs": round(tot_fl / tot_us / 1e6, 1),
                      "per_gemm": per}
-        del layer, moe, dy
+        del layer, fl, moe, dy
         torch.cuda.empty_cache()
     return out
 
@@ -394,28 +412,40 @@ GP_ORDER = ["FC1 forward", "FC2 forward", "FC2 dgrad", "FC2 wgrad", "FC1 dgrad",
 GP_MODE = {"FC1 forward": "NT bf16", "FC2 forward": "NT MXFP8", "FC2 dgrad": "NN MXFP8", "FC2 wgrad": "TN MXFP8",
            "FC1 dgrad": "NN MXFP8", "FC1 wgrad": "TN MXFP8"}
 GP_TEMPLATE = {"FC1 forward": "0, 0", "FC2 forward": "0, 1", "FC2 dgrad": "1, 1", "FC2 wgrad": "2, 1",
-               "FC1 dgrad": "1, 1", "FC1 wgrad": "2, 1"}
+               "FC1 dgrad": "1, 1", "FC1 wgrad": "2, 1", "FC1 forward + act": "0, 0"}
+# FC1 with the SwiGLU + MXFP8 epilogue: the same (mode, dtype), a non-zero
+# epilogue argument (the last template argument; 1 SwiGLU, 2 clamped)
+GP_FUSED = "FC1 forward + act"
+GP_MODE[GP_FUSED] = "NT bf16 + act epilogue"
+GP_FUSED_ORDER = [GP_FUSED] + GP_ORDER[1:]
 _FC1, _FC2 = 2 * 65536 * 2 * 768 * 2048, 2 * 65536 * 2048 * 768   # 65,536 routed rows, hidden 2048, intermediate 768
 GP_FL = {"FC1 forward": _FC1, "FC2 forward": _FC2, "FC2 dgrad": _FC2, "FC2 wgrad": _FC2, "FC1 dgrad": _FC1,
-         "FC1 wgrad": _FC1}
+         "FC1 wgrad": _FC1, GP_FUSED: _FC1}
 # algorithmic bytes of each GEMM: operands and their E8M0 scales read once, bf16 output written once
 GP_BY = {"FC1 forward": 1275e6, "FC2 forward": 528e6, "FC2 dgrad": 447e6, "FC2 wgrad": 593e6, "FC1 dgrad": 787e6,
-         "FC1 wgrad": 1048e6}
-GP_PEAK = {"NT bf16": 2500.0}
+         "FC1 wgrad": 1048e6,
+         # + the MXFP8 activation both ways (codes and E8M0 scales) and the row scale
+         GP_FUSED: 1379e6}
+GP_PEAK = {"NT bf16": 2500.0, "NT bf16 + act epilogue": 2500.0}
 GP_FETCH_SCALE = 2.0   # FETCH_SIZE calibration against a plain copy of known size
 MOE_ONLY_REPS = 2
 
 
 def _expected_gemm_sequence():
-    """GEMM labels in the order `--moe-only` dispatches them: per routing, one
-    untimed layer, MOE_ONLY_REPS timed layers and MOE_ONLY_REPS timed layers
-    with the weight cache valid (each the six GEMMs in layer order), then
-    each GEMM once untimed and MOE_ONLY_REPS times timed."""
+    """GEMM labels in the order `--moe-only` dispatches them: per routing, the
+    plain layer and the layer with the fused FC1 in turn, once untimed and
+    MOE_ONLY_REPS times timed (each the six GEMMs in layer order), the plain
+    layer MOE_ONLY_REPS times with the weight cache valid, each GEMM once
+    untimed and MOE_ONLY_REPS times timed, then FC1 + the activation unfused
+    and fused in turn, once untimed and MOE_ONLY_REPS times."""
     one = []
-    for _ in range(1 + 2 * MOE_ONLY_REPS):
+    for _ in range(1 + MOE_ONLY_REPS):
+        one += GP_ORDER + GP_FUSED_ORDER
+    for _ in range(MOE_ONLY_REPS):
         one += GP_ORDER
     for g in GP_ORDER:
         one += [g] * (1 + MOE_ONLY_REPS)
+    one += ["FC1 forward", GP_FUSED] * (1 + MOE_ONLY_REPS)
     return one * len(MOE_VARIANTS)
 
 
@@ -428,8 +458,9 @@ def _gemm_labels(rows):
         raise SystemExit(f"GEMM profile: {len(rows)} gemm_kernel dispatches, expected {len(seq)}")
     out = {}
     for r, lab in zip(rows, seq):
-        t = re.search(r"gemm_kernel<(\d+), (\d+),", r["Kernel_Name"])
-        if t is None or f"{t.group(1)}, {t.group(2)}" != GP_TEMPLATE[lab]:
+        t = re.search(r"gemm_kernel<(\d+), (\d+),[^>]*?(\d+)>", r["Kernel_Name"])
+        if (t is None or f"{t.group(1)}, {t.group(2)}" != GP_TEMPLATE[lab]
+                or (t.group(3) != "0") != (lab == GP_FUSED)):
             raise SystemExit(f"GEMM profile: dispatch {r['Dispatch_Id']} ({r['Kernel_Name'][:60]}) is not {lab}")
         out[int(r["Dispatch_Id"])] = lab
     return out
@@ -466,7 +497,7 @@ def summarize_gemm_profile(base):
           " roofline-attainable TFLOP/s | % of attainable | L2 hit rate | HBM read MB |"
           + (" MFMA busy % |" if mfu else ""))
     print("|---|---|---|---|---|---|---|---|---|---|---|---|" + ("---|" if mfu else ""))
-    for g in GP_ORDER:
+    for g in GP_ORDER + [GP_FUSED]:
         us = statistics.median(dur[g])
         tf = GP_FL[g] / us / 1e6
         peak = GP_PEAK.get(GP_MODE[g], 5000.0)

@@ -27,8 +27,8 @@ call unless the layer's device flag says the cache holds the current weights.
 """
 import torch
 
-from . import (GEMM_NN, GEMM_NT, GEMM_TN, grouped_gemm, quantize, quantize_into, splits_to_offsets,
-               swiglu_quantize_bwd, swiglu_quantize_fwd)
+from . import (GEMM_NN, GEMM_NT, GEMM_TN, grouped_gemm, grouped_gemm_swiglu, interleave_rows, quantize,
+               quantize_into, splits_to_offsets, swiglu_quantize_bwd, swiglu_quantize_fwd)
 
 
 def weight_offsets(G, rows, device):
@@ -39,11 +39,18 @@ def weight_offsets(G, rows, device):
 class Layer:
     """One grouped expert layer; `forward` keeps what `backward` needs."""
 
-    def __init__(self, splits, w13, w2, clamped=False, limit=7.0):
+    def __init__(self, splits, w13, w2, clamped=False, limit=7.0, fused_fc1=False):
         self.splits = splits
-        self.w13, self.w2 = w13, w2
         self.G, self.I2, self.H = w13.shape
         self.I = self.I2 // 2
+        # fused_fc1: FC1 computes the activation and its MXFP8 form in its
+        # epilogue; the layer then keeps W13 with gate and up rows interleaved
+        # in blocks of 128 (a one-time layout change), H13 and [dgate | dup]
+        # take that interleaved column order, and so do dW13's rows
+        self.fused_fc1 = fused_fc1
+        self.il = 128 if fused_fc1 else 0
+        self.w13 = interleave_rows(w13, 128) if fused_fc1 else w13
+        self.w2 = w2
         self.clamped, self.limit = clamped, limit
         self.row_off, self.block_off, self.err = splits_to_offsets(splits)
         G, H, I, dev = self.G, self.H, self.I, w13.device
@@ -86,10 +93,14 @@ class Layer:
         dev = x_perm.device
         ro, bo = self.row_off, self.block_off
         h13 = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
-        grouped_gemm(GEMM_NT, ro, x_perm, self.w13, h13)
-        a_r, a_c, as_r, as_c = swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, rowwise=True, colwise=True,
-                                                   row_off=ro, block_off=bo, clamped=self.clamped,
-                                                   limit=self.limit)
+        if self.fused_fc1:
+            a_r, a_c, as_r, as_c = grouped_gemm_swiglu(ro, x_perm, self.w13, h13, scale, rowwise=True, colwise=True,
+                                                       block_off=bo, clamped=self.clamped, limit=self.limit)
+        else:
+            grouped_gemm(GEMM_NT, ro, x_perm, self.w13, h13)
+            a_r, a_c, as_r, as_c = swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, rowwise=True, colwise=True,
+                                                       row_off=ro, block_off=bo, clamped=self.clamped,
+                                                       limit=self.limit)
         # W2 in both directions from one read (the colwise copy is kept for
         # the backward's FC2 dgrad)
         self._quantize_w2()
@@ -111,9 +122,10 @@ class Layer:
         dw2 = torch.empty((G, H, I), dtype=torch.bfloat16, device=dev)
         grouped_gemm(GEMM_TN, ro, dy_c, s["a_c"], dw2, dys_c, s["as_c"], block_off=bo)
         h13 = s["h13"]
+        uo = self.il if self.il else I   # up's first column in H13
         dq_r, dq_c, dqs_r, dqs_c, dd, dscale = swiglu_quantize_bwd(
-            da, h13[:, :I], h13[:, I:], s["scale"], rowwise=True, colwise=True, row_off=ro, block_off=bo,
-            clamped=self.clamped, limit=self.limit)
+            da, h13[:, :I], h13[:, uo:uo + I], s["scale"], rowwise=True, colwise=True, row_off=ro, block_off=bo,
+            clamped=self.clamped, limit=self.limit, interleave=self.il)
         self._quantize_w13()
         w13c, w13cs = self.w13c, self.w13cs
         dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
