@@ -173,6 +173,29 @@ mxq_status mxq_swiglu_quantize_fwd(const mxq_act *act, int64_t M, int64_t K,
                                    const mxq_mx_out *col_out, void *stream);
 
 /*
+ * The activation as dense bf16, with or without its MXFP8 forms from the same
+ * pass (TAO4743, Performance: the BF16-wgrad recipe recomputes the activation
+ * in bf16 at the autograd boundary for the two wgrad GEMMs, while the kernel
+ * emits rowwise-only casts).  The same computation, arguments, rules and
+ * MXFP8 outputs as mxq_swiglu_quantize_fwd (every activation kind and the
+ * GLU interleave included), plus:
+ *   h      device bf16 (M x K) output, row pitch ld_h (elements; pointer and
+ *          pitch in bytes multiples of 16), in logical column order (not
+ *          interleaved); required unless M or K is 0
+ *   dirs   0 for the dense activation alone (row_out and col_out unused), or
+ *          ROWWISE, COLWISE or both as for mxq_swiglu_quantize_fwd
+ * h holds exactly the values the MXFP8 outputs quantize.  h may not overlap
+ * an input or another output (MXQ_ERR_ALIAS).
+ */
+mxq_status mxq_swiglu_fwd_bf16(const mxq_act *act, int64_t M, int64_t K,
+                               const uint16_t *gate, int64_t ld_gate,
+                               const uint16_t *up, int64_t ld_up,
+                               const float *row_scale, const mxq_groups *groups,
+                               uint32_t dirs, const mxq_mx_out *row_out,
+                               const mxq_mx_out *col_out, uint16_t *h, int64_t ld_h,
+                               void *stream);
+
+/*
  * Workspace bytes for mxq_swiglu_quantize_bwd at (M, K): the per-row partial
  * sums of dscale (0 if dscale is not requested, but the query always reports
  * the size needed with dscale).
@@ -296,6 +319,10 @@ typedef enum { MXQ_DTYPE_BF16 = 0, MXQ_DTYPE_MXFP8_E4M3 = 1, MXQ_DTYPE_F32 = 2 }
  *     accumulate, leaves C_g untouched).
  * For NT/NN, "M" is the total row count (= row_off[G]); for TN it is the
  * output row count, and the total row count is rows.
+ * Every mode takes bf16 or MXFP8 operands (both the same); bf16 TN is the
+ * wgrad of the BF16-wgrad recipe (TAO4743, Performance: the recipe with the
+ * activation recomputed in bf16 for the two wgrad GEMMs) and needs no
+ * block_off.
  * Every product is accumulated in fp32 and rounded once to the output dtype.
  */
 typedef enum { MXQ_GEMM_NT = 0, MXQ_GEMM_NN = 1, MXQ_GEMM_TN = 2 } mxq_gemm_mode;

@@ -39,7 +39,7 @@ GEMM_TN = 2
 
 # every symbol include/mxq.h declares
 EXPORTS = [
-    "mxq_splits_to_offsets", "mxq_swiglu_quantize_fwd", "mxq_swiglu_quantize_bwd_workspace",
+    "mxq_splits_to_offsets", "mxq_swiglu_quantize_fwd", "mxq_swiglu_fwd_bf16", "mxq_swiglu_quantize_bwd_workspace",
     "mxq_swiglu_quantize_bwd", "mxq_swiglu_quantize_bwd_noalloc", "mxq_quantize", "mxq_quantize_noop",
     "mxq_grouped_gemm_workspace",
     "mxq_grouped_gemm", "mxq_grouped_gemm_swiglu",
@@ -91,6 +91,9 @@ def _load():
         "mxq_swiglu_quantize_fwd": [ctypes.POINTER(mxq_act), I64, I64, P, I64, P, I64, P,
                                     ctypes.POINTER(mxq_groups), U32, ctypes.POINTER(mxq_mx_out),
                                     ctypes.POINTER(mxq_mx_out), P],
+        "mxq_swiglu_fwd_bf16": [ctypes.POINTER(mxq_act), I64, I64, P, I64, P, I64, P,
+                                ctypes.POINTER(mxq_groups), U32, ctypes.POINTER(mxq_mx_out),
+                                ctypes.POINTER(mxq_mx_out), P, I64, P],
         "mxq_swiglu_quantize_bwd_workspace": [I64, I64, U32, ctypes.POINTER(ctypes.c_size_t)],
         "mxq_swiglu_quantize_bwd": [ctypes.POINTER(mxq_act), I64, I64, P, I64, P, I64, P, I64, P,
                                     ctypes.POINTER(mxq_groups), P, I64, P, I64, P, U32,
@@ -202,6 +205,14 @@ def mxq_swiglu_quantize_fwd(act, gate, up, row_scale, groups, dirs, row_out, col
                                        _byref(col_out), _stream(stream))
 
 
+def mxq_swiglu_fwd_bf16(act, gate, up, row_scale, groups, dirs, row_out, col_out, h, stream=None):
+    M, K = gate.shape
+    return lib.mxq_swiglu_fwd_bf16(_byref(act), M, K, _ptr(gate), _ld(gate), _ptr(up),
+                                   _ld(up) if up is not None else 0,
+                                   _ptr(row_scale), _byref(groups), dirs, _byref(row_out),
+                                   _byref(col_out), _ptr(h), _ld(h) if h is not None else 0, _stream(stream))
+
+
 def mxq_swiglu_quantize_bwd_workspace(M, K, dirs):
     n = ctypes.c_size_t(0)
     check(lib.mxq_swiglu_quantize_bwd_workspace(M, K, dirs, ctypes.byref(n)))
@@ -305,6 +316,25 @@ def swiglu_quantize_fwd(gate, up, scale=None, rowwise=True, colwise=False, row_o
     act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit, interleave)
     check(mxq_swiglu_quantize_fwd(act, gate, up, scale, make_groups(row_off, block_off), dirs, ro, co, stream))
     return rc, cc, rs, cs
+
+
+def swiglu_bf16(gate, up, scale=None, rowwise=False, colwise=False, row_off=None, block_off=None,
+                n_col_blocks=None, clamped=False, limit=7.0, interleave=0, srelu=False, out=None, stream=None):
+    """The activation as dense bf16 h (M, K) (up None with srelu), and its
+    MXFP8 forms from the same pass when asked: returns (h, codes_row,
+    codes_col, scales_row, scales_col), a disabled direction zero-sized."""
+    import torch
+    M, K = gate.shape
+    dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if n_col_blocks is None:
+        n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, gate.device)
+    ro, co = _outs(rc, cc, rs, cs, dirs)
+    h = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=gate.device)
+    act = make_act(ACT_SRELU if srelu else (ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU), limit, interleave)
+    groups = make_groups(row_off, block_off) if row_off is not None else None
+    check(mxq_swiglu_fwd_bf16(act, gate, up, scale, groups, dirs, ro, co, h, stream))
+    return h, rc, cc, rs, cs
 
 
 def srelu_quantize_fwd(x, scale=None, rowwise=True, colwise=False, row_off=None, block_off=None,

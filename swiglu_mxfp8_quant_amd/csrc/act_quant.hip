@@ -416,6 +416,7 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
                 }
             }
         }
+        if (a.h != nullptr && i < nrow && active) store_bf16<CPT>(a.h + (rbase + i) * a.ld_h + co, h[i]);
         uint32_t m = 0u;
 #pragma unroll
         for (int k = 0; k < CPT / 2; k++) {
@@ -944,6 +945,7 @@ hipError_t fwd_launch(const FwdArgs &a, hipStream_t stream) {
 template <int ACT>
 hipError_t fwd_dispatch(const FwdArgs &a, hipStream_t stream) {
     switch (a.dirs) {
+        case 0: return fwd_launch<ACT, 0>(a, stream);   // the dense activation only
         case 1: return fwd_launch<ACT, 1>(a, stream);
         case 2: return fwd_launch<ACT, 2>(a, stream);
         default: return fwd_launch<ACT, 3>(a, stream);

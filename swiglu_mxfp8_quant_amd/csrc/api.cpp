@@ -160,14 +160,16 @@ int64_t gate_span(int64_t K, int il) { return il ? 2 * K - il : K; }
 mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int il, int64_t M, int64_t K,
                        const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
                        const float *row_scale, const mxq_groups *groups, uint32_t dirs,
-                       const mxq_mx_out *row_out, const mxq_mx_out *col_out, bool *noop) {
+                       const mxq_mx_out *row_out, const mxq_mx_out *col_out, bool *noop,
+                       bool dense = false, uint16_t *h = nullptr, int64_t ld_h = 0) {
     *noop = false;
     if (M < 0 || K < 0) return fail(MXQ_ERR_SHAPE, "M = %lld and K = %lld must be >= 0", (long long)M, (long long)K);
     if (K % 32 != 0) return fail(MXQ_ERR_SHAPE, "K = %lld must be a multiple of 32", (long long)K);
     mxq_status si = check_interleave(act_kind, il, K);
     if (si != MXQ_OK) return si;
     if (act_kind == mxq::ACT_SRELU && up != nullptr) return fail(MXQ_ERR_SHAPE, "SReLU is unary: up must be NULL");
-    if (dirs < 1 || dirs > 3) return fail(MXQ_ERR_SHAPE, "dirs = %u must be ROWWISE, COLWISE or both", dirs);
+    if (dirs > 3 || (dirs == 0 && !dense))
+        return fail(MXQ_ERR_SHAPE, "dirs = %u must be ROWWISE, COLWISE or both%s", dirs, dense ? ", or 0" : "");
     if (act_kind == mxq::ACT_CLAMPED && !(limit > 0.0f))
         return fail(MXQ_ERR_SHAPE, "clamped SwiGLU needs a limit > 0");
     if (act_kind != mxq::ACT_IDENTITY && row_scale != nullptr && !aligned(row_scale, 4))
@@ -205,6 +207,14 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int il, int64
     } else if (col_out != nullptr && col_out->codes != nullptr) {
         return fail(MXQ_ERR_SHAPE, "col_out given but dirs has no COLWISE");
     }
+    if (dense) {
+        if (h == nullptr) return fail(MXQ_ERR_NULL, "h is NULL (mxq_swiglu_quantize_fwd writes no dense output)");
+        if (ld_h < K) return fail(MXQ_ERR_SHAPE, "h ld %lld < K %lld", (long long)ld_h, (long long)K);
+        if (!aligned(h, 16) || ld_h % 8 != 0)
+            return fail(MXQ_ERR_ALIGN, "h pointer and row pitch must be multiples of 16 bytes");
+        if (!extent_ok(M, ld_h, 2)) return fail(MXQ_ERR_OVERFLOW, "h extent too large");
+        outs.push_back(range2d(h, M, K, ld_h, 2, "h"));
+    }
     // launch bound: HIP's grid x block must stay below 2^32 work-items
     if (mxq::act_quant_launch_threads(M, K, G, (dirs & 2) && G > 0, false) >= (int64_t(1) << 32))
         return fail(MXQ_ERR_OVERFLOW, "launch beyond 2^32 work-items");
@@ -226,6 +236,8 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int il, int64
                        : mxq::MxOut{nullptr, 0, nullptr, 0};
     a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales}
                        : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.h = h;
+    a.ld_h = ld_h;
     return MXQ_OK;
 }
 
@@ -351,6 +363,22 @@ mxq_status mxq_swiglu_quantize_fwd(const mxq_act *act, int64_t M, int64_t K, con
                                col_out, &noop);
     if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
     return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_fwd launch");
+}
+
+mxq_status mxq_swiglu_fwd_bf16(const mxq_act *act, int64_t M, int64_t K, const uint16_t *gate, int64_t ld_gate,
+                               const uint16_t *up, int64_t ld_up, const float *row_scale, const mxq_groups *groups,
+                               uint32_t dirs, const mxq_mx_out *row_out, const mxq_mx_out *col_out, uint16_t *h,
+                               int64_t ld_h, void *stream) {
+    float limit;
+    int il;
+    const int kind = act_from(act, &limit, &il);
+    if (kind < 0) return fail(MXQ_ERR_UNSUPPORTED, "unknown activation kind %d", act->kind);
+    mxq::FwdArgs a{};
+    bool noop;
+    mxq_status s = prepare_fwd(a, kind, limit, il, M, K, gate, ld_gate, up, ld_up, row_scale, groups, dirs, row_out,
+                               col_out, &noop, true, h, ld_h);
+    if (s != MXQ_OK || noop) return s == MXQ_OK ? ok() : s;
+    return hip_status(mxq::launch_act_quant_fwd(a, (hipStream_t)stream), "mxq_swiglu_fwd_bf16 launch");
 }
 
 mxq_status mxq_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t ld_x, const mxq_groups *groups,

@@ -234,25 +234,37 @@ __device__ __forceinline__ void stage_kc(const Src &o, const uint8_t *sb, const 
     to_lds_sel(rsrc_open(sb), dst + 1024 * J, f.v[J], in_k, oob);
 }
 
-// K-strided stage s -> LDS [64 contraction rows][256 B], chunk c of row k at c ^ (k & 15).
-// Lane l of load j covers contraction row 4 (4w + j) + l / 16.
+// K-strided stage s -> LDS, 256 output columns by 64 contraction bytes' worth
+// of rows: fp8 [64 contraction rows][256 B], chunk c of row k at c ^ (k & 15);
+// bf16 [32 contraction rows][512 B], chunk c of row k at c ^ 4 (k & 3).
+// Lane l of load j covers contraction row 4 (4w + j) + l / 16 (fp8) or
+// 2 (4w + j) + l / 32 (bf16).
+template <int ESZ>
 __device__ __forceinline__ Feed feed_ks(const Src &o, bool live, int wave, int lane) {
     Feed f;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const int kr = 4 * (4 * wave + j) + (lane >> 4);
-        const int c = (lane & 15) ^ (kr & 15);
+        int kr, c;
+        if constexpr (ESZ == 1) {
+            kr = 4 * (4 * wave + j) + (lane >> 4);
+            c = (lane & 15) ^ (kr & 15);
+        } else {
+            kr = 2 * (4 * wave + j) + (lane >> 5);
+            c = (lane & 31) ^ (4 * (kr & 3));
+        }
         f.v[j] = (live & (16 * c < o.valid)) ? (uint32_t)(kr * o.pitch + 16 * c) : kOOB;
     }
     return f;
 }
 
-// `sb`: the operand's origin advanced to stage s (o.base + s * BK * o.pitch)
-template <int J>
+// `sb`: the operand's origin advanced to stage s (o.base + s * (BK / ESZ) * o.pitch)
+template <int J, int ESZ>
 __device__ __forceinline__ void stage_ks(const Src &o, const uint8_t *sb, const Feed &f, int s, uint32_t dst, int wave,
                                          int lane, uint32_t oob) {
-    const int kr0 = s * BK;
-    const uint64_t in_k = __builtin_amdgcn_ballot_w64((lane >> 4) < o.kext - kr0 - 4 * (4 * wave + J));
+    const int kr0 = s * (BK / ESZ);
+    const bool in = ESZ == 1 ? (lane >> 4) < o.kext - kr0 - 4 * (4 * wave + J)
+                             : (lane >> 5) < o.kext - kr0 - 2 * (4 * wave + J);
+    const uint64_t in_k = __builtin_amdgcn_ballot_w64(in);
     to_lds_sel(rsrc_open(sb), dst + 1024 * J, f.v[J], in_k, oob);
 }
 
@@ -344,6 +356,31 @@ __device__ __forceinline__ i32x8_t frag_ks_f8(const uint8_t *t, int col0, int g,
     const i32x2_t c = tr8(t, 32 + 16 * g, col0, m);
     const i32x2_t d = tr8(t, 40 + 16 * g, col0, m);
     return i32x8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// bf16, K-strided tile ([32 contraction rows][256 columns], 512-byte rows):
+// ds_read_b64_tr_b16 moves a 4-row x 16-column block of 16-bit elements
+// between the 16 lanes of a group: lane m points at row k0 + m/4, bytes
+// 8 (m % 4) .. + 8 of the block's 32, and receives the 4 elements of column
+// col0 + m in rows k0 .. k0 + 3 (checked on the device with a probe of
+// known values).  The swizzle 4 (k & 3) puts the 4 rows' 32-byte pieces of
+// one group, and those of the group 16 columns on, in 8 different 32-byte
+// bank slots.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+__device__ __forceinline__ i32x2_t tr16(const uint8_t *t, int k0, int col0, int m) {
+    const int kr = k0 + (m >> 2);
+    const int chunk = (col0 >> 3) + ((m & 3) >> 1);
+    const uint8_t *p = t + kr * 512 + 16 * (chunk ^ (4 * (kr & 3))) + 8 * (m & 1);
+    return __builtin_bit_cast(i32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+}
+
+// The bf16 32x32x16 operand of column col0 + m (col0 a multiple of 16):
+// contraction elements 16 kk + 8 g .. + 8 of the stage.
+__device__ __forceinline__ bf16x8_t frag_ks_bf16(const uint8_t *t, int col0, int kk, int g, int m) {
+    const i32x2_t a = tr16(t, 16 * kk + 8 * g, col0, m);
+    const i32x2_t b = tr16(t, 16 * kk + 8 * g + 4, col0, m);
+    return __builtin_bit_cast(bf16x8_t, i32x4_t{a.x, a.y, b.x, b.y});
 }
 
 // One stage's fragments of a wave's 128 x 128 quadrant: MXFP8, 4 + 4 operand
@@ -595,6 +632,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     };
     constexpr bool F8 = (DT == MXQ_DTYPE_MXFP8_E4M3);
     constexpr int ESZ = F8 ? 1 : 2;
+    constexpr int KSR = BK / ESZ;   // contraction elements (rows of a K-strided operand) per stage
     constexpr int OSZ = OUT == MXQ_DTYPE_F32 ? 4 : 2;
     constexpr bool XKS = (MODE != MODE_NT);   // X (N side) K-strided
     constexpr bool YKS = (MODE == MODE_TN);   // Y (M side) K-strided
@@ -639,7 +677,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             const int G = (int)a.G;
             for (int g = tid; g < G; g += NTHR) {
                 const int rows = rs[g + 1] - rs[g];
-                gsteps[g] = rows > 0 ? (rows + BK - 1) / BK : 0;
+                gsteps[g] = rows > 0 ? (rows + KSR - 1) / KSR : 0;
             }
             __syncthreads();
             // thread w: the load of workgroup w in the static order; and the total
@@ -729,15 +767,15 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
                 blk0 = sa.block_off != nullptr ? sa.block_off[g] : 0;
             }
             r1 = r1 > r0 ? r1 : r0;
-            T.x = B + r0 * ldb + n0;
-            T.y = A + r0 * lda + m0;
+            T.x = B + r0 * ldb + n0 * ESZ;
+            T.y = A + r0 * lda + m0 * ESZ;
             T.xs = sa.B.scales + blk0 * ldsb + n0;
             T.ys = sa.A.scales + blk0 * ldsa + m0;
             T.o = static_cast<uint8_t *>(sa.out) + (g * sa.out_gstride + m0 * sa.ld_out + n0) * OSZ;
             T.yv = (int)(sa.M - m0 < BT ? sa.M - m0 : BT);
             T.kext = (int)(r1 - r0);
             T.nblk = (T.kext + 31) / 32;
-            T.ksteps = (T.kext + BK - 1) / BK;
+            T.ksteps = (T.kext + KSR - 1) / KSR;
         } else {
             int mt, nt;
             raster(item, ntm, ntn, mt, nt);
@@ -760,7 +798,7 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
                 T.x = B + g * sa.B.gstride * ESZ + n0 * ldb;
                 T.xs = sa.B.scales + g * sa.B.scale_gstride + n0 * ldsb;
             } else {
-                T.x = B + g * sa.B.gstride + n0;
+                T.x = B + (g * sa.B.gstride + n0) * ESZ;
                 T.xs = sa.B.scales + g * sa.B.scale_gstride + n0;
             }
             T.y = A + m0 * lda;
@@ -811,15 +849,23 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     // scale-ring groups issued (load side) and begun (compute side)
     unsigned lgrp = 0, cgrp = 0, cgrp_slot = 0;
     const int nblk_k = (int)((a.K + 31) / 32);
-    auto src_x = [&](const Tile &T) { return Src{T.x, ldb, T.kext, T.xv}; };
-    auto src_y = [&](const Tile &T) { return Src{T.y, lda, T.kext, T.yv}; };
+    // (K-strided views count the contraction in rows and the valid columns in
+    // bytes; T.kext is the group's rows for TN and K's bytes otherwise)
+    auto src_x = [&](const Tile &T) {
+        if constexpr (XKS) return Src{T.x, ldb, MODE == MODE_TN ? T.kext : T.kext / ESZ, T.xv * ESZ};
+        else return Src{T.x, ldb, T.kext, T.xv};
+    };
+    auto src_y = [&](const Tile &T) {
+        if constexpr (YKS) return Src{T.y, lda, T.kext, T.yv * ESZ};
+        else return Src{T.y, lda, T.kext, T.yv};
+    };
     // the load side's per-lane data-load offsets (of its current tile)
     const uint32_t lds_smem = lds_addr(smem);
     Feed fdx, fdy;
     // the load tile's operand and column-scale origins advanced to stage `ls`,
     // carried from stage to stage (per-stage strides are per launch)
     const uint8_t *sbx = nullptr, *sby = nullptr, *sbxs = nullptr, *sbys = nullptr;
-    const int64_t dsx = XKS ? (int64_t)BK * ldb : BK, dsy = YKS ? (int64_t)BK * lda : BK;
+    const int64_t dsx = XKS ? (int64_t)KSR * ldb : BK, dsy = YKS ? (int64_t)KSR * lda : BK;
     const int64_t dsxs = 2 * (int64_t)ldsb, dsys = 2 * (int64_t)ldsa;
 
     // Load instruction p of stage s of tile T into stage buffer st (live
@@ -831,10 +877,10 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
         uint8_t *st = smem + slot * STAGE;
         const uint32_t dst = lds_smem + slot * STAGE + 4096 * wave;   // this wave's blocks
         if constexpr (p < 4) {
-            if constexpr (XKS) stage_ks<p>(src_x(T), sbx, fdx, s, dst, wave, lane, kOOB);
+            if constexpr (XKS) stage_ks<p, ESZ>(src_x(T), sbx, fdx, s, dst, wave, lane, kOOB);
             else stage_kc<p>(src_x(T), sbx, fdx, s, dst, lane, kOOB);
         } else if constexpr (p < 8) {
-            if constexpr (YKS) stage_ks<p - 4>(src_y(T), sby, fdy, s, dst + OPB, wave, lane, kOOB);
+            if constexpr (YKS) stage_ks<p - 4, ESZ>(src_y(T), sby, fdy, s, dst + OPB, wave, lane, kOOB);
             else stage_kc<p - 4>(src_y(T), sby, fdy, s, dst + OPB, lane, kOOB);
         } else if constexpr (p == 8 && XSB > 0) {
             if constexpr (XKS)
@@ -938,8 +984,13 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
             }
         } else {
             constexpr int kk = j / 8;
-            if constexpr (isx) F.fx[kk][idx] = kc_bf16(kk ? v.xh : v.xl, idx);
-            else F.fy[kk][idx] = kc_bf16(kk ? v.yh : v.yl, idx);
+            if constexpr (isx) {
+                if constexpr (XKS) F.fx[kk][idx] = frag_ks_bf16(tx, wx + 32 * idx + 16 * ((lane >> 4) & 1), kk, g32, l16);
+                else F.fx[kk][idx] = kc_bf16(kk ? v.xh : v.xl, idx);
+            } else {
+                if constexpr (YKS) F.fy[kk][idx] = frag_ks_bf16(ty, wy + 32 * idx + 16 * ((lane >> 4) & 1), kk, g32, l16);
+                else F.fy[kk][idx] = kc_bf16(kk ? v.yh : v.yl, idx);
+            }
         }
     };
     // Ring scale bytes of blocks past the contraction are whatever follows
@@ -1214,9 +1265,9 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     int ls = 0;
     auto make_feeds = [&]() {
         const bool live = ld.valid != 0;
-        if constexpr (XKS) fdx = feed_ks(src_x(ld), live, wave, lane);
+        if constexpr (XKS) fdx = feed_ks<ESZ>(src_x(ld), live, wave, lane);
         else fdx = feed_kc(src_x(ld), live, wave, lane);
-        if constexpr (YKS) fdy = feed_ks(src_y(ld), live, wave, lane);
+        if constexpr (YKS) fdy = feed_ks<ESZ>(src_y(ld), live, wave, lane);
         else fdy = feed_kc(src_y(ld), live, wave, lane);
         sbx = ld.x;
         sby = ld.y;
@@ -1530,7 +1581,6 @@ int gemm_prepare(const mxq_gemm_args &in, GemmArgs &g, std::string &err) {
     if (in.A.dtype != in.B.dtype) { err = "A and B must have the same dtype"; return MXQ_ERR_UNSUPPORTED; }
     const bool f8 = in.A.dtype == MXQ_DTYPE_MXFP8_E4M3;
     if (!f8 && in.A.dtype != MXQ_DTYPE_BF16) { err = "operand dtype must be BF16 or MXFP8_E4M3"; return MXQ_ERR_UNSUPPORTED; }
-    if (!f8 && in.mode != MXQ_GEMM_NT) { err = "bf16 operands are built for the NT mode only"; return MXQ_ERR_UNSUPPORTED; }
     if (in.out_dtype != MXQ_DTYPE_BF16 && in.out_dtype != MXQ_DTYPE_F32) { err = "out_dtype must be BF16 or F32"; return MXQ_ERR_UNSUPPORTED; }
     if (in.accumulate && !(in.mode == MXQ_GEMM_TN && in.out_dtype == MXQ_DTYPE_F32)) {
         err = "accumulate is supported for TN with an F32 output";
@@ -1590,11 +1640,15 @@ hipError_t launch_grouped_gemm(const GemmArgs &g, hipStream_t stream) {
             return o32 ? launch_mode<MODE_NT, MXQ_DTYPE_BF16, MXQ_DTYPE_F32>(g, stream)
                        : launch_mode<MODE_NT, MXQ_DTYPE_BF16, MXQ_DTYPE_BF16>(g, stream);
         case MXQ_GEMM_NN:
-            return o32 ? launch_mode<MODE_NN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_F32>(g, stream)
-                       : launch_mode<MODE_NN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_BF16>(g, stream);
+            if (f8) return o32 ? launch_mode<MODE_NN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_F32>(g, stream)
+                               : launch_mode<MODE_NN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_BF16>(g, stream);
+            return o32 ? launch_mode<MODE_NN, MXQ_DTYPE_BF16, MXQ_DTYPE_F32>(g, stream)
+                       : launch_mode<MODE_NN, MXQ_DTYPE_BF16, MXQ_DTYPE_BF16>(g, stream);
         default:
-            return o32 ? launch_mode<MODE_TN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_F32>(g, stream)
-                       : launch_mode<MODE_TN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_BF16>(g, stream);
+            if (f8) return o32 ? launch_mode<MODE_TN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_F32>(g, stream)
+                               : launch_mode<MODE_TN, MXQ_DTYPE_MXFP8_E4M3, MXQ_DTYPE_BF16>(g, stream);
+            return o32 ? launch_mode<MODE_TN, MXQ_DTYPE_BF16, MXQ_DTYPE_F32>(g, stream)
+                       : launch_mode<MODE_TN, MXQ_DTYPE_BF16, MXQ_DTYPE_BF16>(g, stream);
     }
 }
 

@@ -38,6 +38,7 @@ struct FwdArgs {
     unsigned dirs;
     MxOut row, col;
     const int32_t *noop;                     // device flag or NULL: non-zero => the launch does nothing
+    uint16_t *h; int64_t ld_h;               // the activation as dense bf16 (logical columns), or NULL
 };
 
 struct BwdArgs {

@@ -21,6 +21,12 @@ rowwise and colwise (per expert); Y = FC2(A) (R, H) bf16.
 Backward from dY (R, H): dA = dY . W2_g (MXFP8 NN), dW2_g = dY_g^T A_g (MXFP8
 TN), [dgate | dup], dscale and MXFP8 dact from the fused backward,
 dX = dact . W13_g (MXFP8 NN), dW13_g = dact_g^T X_g (MXFP8 TN).
+The BF16-wgrad recipe (page "[mxfp8 training] Add a fused gated-activation
+(SwiGLU) + MXFP8 quantization kernel", Performance: rowwise-only casts, the
+activation recomputed in bf16 for the two wgrad GEMMs) casts A, dY and dact
+rowwise only, recomputes A in bf16 from H13 in the backward, and runs both
+wgrads as bf16 TN GEMMs: dW2_g = dY_g^T A_bf16_g, dW13_g = [dgate | dup]_g^T
+X_g.
 The MXFP8 weights (W2 rowwise along I and colwise along H, W13 colwise along
 2I) live in buffers the layer owns and are re-quantized in place on every
 call unless the layer's device flag says the cache holds the current weights.
@@ -28,7 +34,7 @@ call unless the layer's device flag says the cache holds the current weights.
 import torch
 
 from . import (GEMM_NN, GEMM_NT, GEMM_TN, grouped_gemm, grouped_gemm_swiglu, interleave_rows, quantize,
-               quantize_into, splits_to_offsets, swiglu_quantize_bwd, swiglu_quantize_fwd)
+               quantize_into, splits_to_offsets, swiglu_bf16, swiglu_quantize_bwd, swiglu_quantize_fwd)
 
 
 def weight_offsets(G, rows, device):
@@ -39,7 +45,10 @@ def weight_offsets(G, rows, device):
 class Layer:
     """One grouped expert layer; `forward` keeps what `backward` needs."""
 
-    def __init__(self, splits, w13, w2, clamped=False, limit=7.0, fused_fc1=False):
+    def __init__(self, splits, w13, w2, clamped=False, limit=7.0, fused_fc1=False, recipe="mxfp8"):
+        if recipe not in ("mxfp8", "bf16_wgrad"):
+            raise ValueError(f"unknown recipe {recipe!r}")
+        self.recipe = recipe
         self.splits = splits
         self.G, self.I2, self.H = w13.shape
         self.I = self.I2 // 2
@@ -93,12 +102,13 @@ class Layer:
         dev = x_perm.device
         ro, bo = self.row_off, self.block_off
         h13 = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
+        col = self.recipe == "mxfp8"   # the colwise cast feeds the MXFP8 FC2 wgrad only
         if self.fused_fc1:
-            a_r, a_c, as_r, as_c = grouped_gemm_swiglu(ro, x_perm, self.w13, h13, scale, rowwise=True, colwise=True,
+            a_r, a_c, as_r, as_c = grouped_gemm_swiglu(ro, x_perm, self.w13, h13, scale, rowwise=True, colwise=col,
                                                        block_off=bo, clamped=self.clamped, limit=self.limit)
         else:
             grouped_gemm(GEMM_NT, ro, x_perm, self.w13, h13)
-            a_r, a_c, as_r, as_c = swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, rowwise=True, colwise=True,
+            a_r, a_c, as_r, as_c = swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, rowwise=True, colwise=col,
                                                        row_off=ro, block_off=bo, clamped=self.clamped,
                                                        limit=self.limit)
         # W2 in both directions from one read (the colwise copy is kept for
@@ -115,27 +125,40 @@ class Layer:
         R, I, H, G = dy.shape[0], self.I, self.H, self.G
         dev = dy.device
         ro, bo = self.row_off, self.block_off
-        dy_r, dy_c, dys_r, dys_c = quantize(dy, rowwise=True, colwise=True, row_off=ro, block_off=bo)
+        mx = self.recipe == "mxfp8"
+        dy_r, dy_c, dys_r, dys_c = quantize(dy, rowwise=True, colwise=mx, row_off=ro, block_off=bo)
         w2c, w2cs = s["w2c"], s["w2cs"]
         da = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
         grouped_gemm(GEMM_NN, ro, dy_r, w2c, da, dys_r, w2cs)
         dw2 = torch.empty((G, H, I), dtype=torch.bfloat16, device=dev)
-        grouped_gemm(GEMM_TN, ro, dy_c, s["a_c"], dw2, dys_c, s["as_c"], block_off=bo)
         h13 = s["h13"]
         uo = self.il if self.il else I   # up's first column in H13
+        gate, up = h13[:, :I], h13[:, uo:uo + I]
+        a_bf16 = None
+        if mx:
+            grouped_gemm(GEMM_TN, ro, dy_c, s["a_c"], dw2, dys_c, s["as_c"], block_off=bo)
+        else:
+            # the activation recomputed in bf16 for the FC2 wgrad
+            a_bf16 = swiglu_bf16(gate, up, s["scale"], clamped=self.clamped, limit=self.limit,
+                                 interleave=self.il)[0]
+            grouped_gemm(GEMM_TN, ro, dy, a_bf16, dw2)
         dq_r, dq_c, dqs_r, dqs_c, dd, dscale = swiglu_quantize_bwd(
-            da, h13[:, :I], h13[:, uo:uo + I], s["scale"], rowwise=True, colwise=True, row_off=ro, block_off=bo,
+            da, gate, up, s["scale"], rowwise=True, colwise=mx, row_off=ro, block_off=bo,
             clamped=self.clamped, limit=self.limit, interleave=self.il)
         self._quantize_w13()
         w13c, w13cs = self.w13c, self.w13cs
         dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         grouped_gemm(GEMM_NN, ro, dq_r, w13c, dx, dqs_r, w13cs)
-        _, x_c, _, xs_c = quantize(s["x_perm"], rowwise=False, colwise=True, row_off=ro, block_off=bo)
         dw13 = torch.empty((G, 2 * I, H), dtype=torch.bfloat16, device=dev)
-        grouped_gemm(GEMM_TN, ro, dq_c, x_c, dw13, dqs_c, xs_c, block_off=bo)
+        x_c = xs_c = None
+        if mx:
+            _, x_c, _, xs_c = quantize(s["x_perm"], rowwise=False, colwise=True, row_off=ro, block_off=bo)
+            grouped_gemm(GEMM_TN, ro, dq_c, x_c, dw13, dqs_c, xs_c, block_off=bo)
+        else:
+            grouped_gemm(GEMM_TN, ro, dd, s["x_perm"], dw13)
         self.grads = dict(dy_r=dy_r, dy_c=dy_c, dys_r=dys_r, dys_c=dys_c, w2c=w2c, w2cs=w2cs, da=da, dw2=dw2,
                           dq_r=dq_r, dq_c=dq_c, dqs_r=dqs_r, dqs_c=dqs_c, dd=dd, dscale=dscale, w13c=w13c,
-                          w13cs=w13cs, dx=dx, x_c=x_c, xs_c=xs_c, dw13=dw13)
+                          w13cs=w13cs, dx=dx, x_c=x_c, xs_c=xs_c, dw13=dw13, a_bf16=a_bf16)
         return dx, dw13, dw2, dscale
 
 

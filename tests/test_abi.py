@@ -275,3 +275,47 @@ def test_noalloc_backward_refuses_beyond_its_scratch(m):
     st = m.lib.mxq_swiglu_quantize_bwd_noalloc(None, 1 << 20, 8192, f, 16384, f, 16384, f, 16384, None, None,
                                                None, 0, None, 0, fake(1 << 30), 1, None, None, None)
     assert st == 8 and "scratch" in m.last_error()
+
+
+def fwd_dense(m, M=64, K=64, dirs=0, h=8 << 24, ldh=64, act=None, row=None):
+    return m.lib.mxq_swiglu_fwd_bf16(
+        None if act is None else ctypes.byref(act), M, K, fake(0), 128, fake(128), 128, None, None, dirs,
+        None if row is None else ctypes.byref(row), None, None if h is None else fake(h), ldh, None)
+
+
+def test_dense_forward_validation(m):
+    """mxq_swiglu_fwd_bf16 (the activation recomputed as dense bf16): dirs may
+    be 0 there (and only there), h is required, aligned, at least K wide and
+    may not overlap an input; an empty call succeeds without h."""
+    assert fwd(m, dirs=0) == 2                              # the quantizing forward needs a direction
+    assert fwd_dense(m, dirs=4) == 2
+    assert fwd_dense(m, h=None) == 1
+    assert fwd_dense(m, h=(8 << 24) + 8) == 3               # misaligned h
+    assert fwd_dense(m, ldh=68) == 3                        # pitch not 16 bytes
+    assert fwd_dense(m, ldh=32) == 2                        # ld_h < K
+    assert fwd_dense(m, h=64) == 5                          # h overlaps gate
+    row = m.mxq_mx_out(BASE + (8 << 24) + 64, 64, BASE + (5 << 24), 2)
+    assert fwd_dense(m, dirs=1, row=row) == 5               # codes overlap h
+    assert fwd_dense(m, M=0, h=None) == 0
+    act = m.mxq_act(m.ACT_SRELU, 0.0, 0)
+    assert m.lib.mxq_swiglu_fwd_bf16(ctypes.byref(act), 64, 64, fake(0), 128, fake(128), 128, None, None, 0, None,
+                                     None, fake(8 << 24), 64, None) == 2   # SReLU is unary: up must be NULL
+
+
+def test_gemm_bf16_every_mode_validates(m):
+    """bf16 operands are accepted in every mode (NN and TN read them strided
+    along the contraction); bf16 TN needs no block_off.  Only validation runs
+    here: the calls stop at an alias before anything is launched."""
+    lib = m.lib
+    bf = m.DTYPE_BF16
+    for mode in (m.GEMM_NN, m.GEMM_TN):
+        a = gemm_args(m, mode)
+        a.A.dtype = a.B.dtype = bf
+        a.A.scales = a.B.scales = None
+        a.block_off = None
+        if mode == m.GEMM_NN:
+            a.B.ld, a.B.gstride = 256, 256 * 256
+        a.out = BASE + (1 << 28) + 64                       # on top of A
+        ws = fake(6 << 28) if mode == m.GEMM_TN else None
+        assert lib.mxq_grouped_gemm(ctypes.byref(a), ws, 256 if ws else 0, None) == 5, mode
+        assert "overlaps" in m.last_error()
