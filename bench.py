@@ -202,8 +202,9 @@ def moe_section(m, torch, W, reps=5):
         R = int(moe["splits"].sum())
         layer = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped)
         # the same layer with FC1's fused epilogue (its W13 rows interleaved
-        # in blocks of 128)
+        # in blocks of 128), and under the BF16-wgrad recipe
         fl = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, fused_fc1=True)
+        bl = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, recipe="bf16_wgrad")
         dy = W.moe_grad(R, H, seed=0, device="cuda")
         xs, sc = moe["x_perm"], moe["scale"]
 
@@ -214,10 +215,15 @@ def moe_section(m, torch, W, reps=5):
         def full_fused():
             fl.forward(xs, sc)
             fl.backward(dy)
+
+        def full_bf16():
+            bl.forward(xs, sc)
+            bl.backward(dy)
         full()
         full_fused()
+        full_bf16()
         torch.cuda.synchronize()
-        layer_us, fused_us = timed_alt(torch, [full, full_fused], reps)
+        layer_us, fused_us, bf16_us = timed_alt(torch, [full, full_fused, full_bf16], reps)
         # the plain layer with the MXFP8 weight cache valid (the device flag
         # skips the weight quantizations, as on the micro-batches after a
         # weight update)
@@ -251,6 +257,19 @@ def moe_section(m, torch, W, reps=5):
             per[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": dt, "frac_peak": round(tf / peak, 4)}
             tot_fl += flops[k]
             tot_us += us
+        # the recipe's two bf16 wgrads
+        bs, bg = bl.saved, bl.grads
+        bcalls = {
+            "fc2_wgrad_bf16": lambda: m.grouped_gemm(m.GEMM_TN, ro, dy, bg["a_bf16"], dw2),
+            "fc1_wgrad_bf16": lambda: m.grouped_gemm(m.GEMM_TN, ro, bg["dd"], bs["x_perm"], dw13),
+        }
+        per_bf16 = {}
+        for k, fn in bcalls.items():
+            fn()
+            us, = timed_alt(torch, [fn], reps)
+            tf = flops[k[:-5]] / us / 1e6
+            per_bf16[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": "bf16",
+                           "frac_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
         # FC1 + the activation's MXFP8 both ways: the bf16 FC1, then the fused
         # activation kernel, against FC1 with the activation in its epilogue
         unfused = lambda: (m.grouped_gemm(m.GEMM_NT, ro, xs, moe["w13"], h13),
@@ -263,11 +282,12 @@ def moe_section(m, torch, W, reps=5):
         fc1_act_us = [round(v, 1) for v in timed_alt(torch, [unfused, fused], reps)]
         out[name] = {"routed_rows": R, "layer_fwd_bwd_us": round(layer_us, 1),
                      "layer_fwd_bwd_fused_fc1_us": round(fused_us, 1),
+                     "layer_fwd_bwd_bf16_wgrad_recipe_us": round(bf16_us, 1),
                      "layer_fwd_bwd_cached_weights_us": round(cached_us, 1),
                      "fc1_plus_activation_fwd_us": {"unfused": fc1_act_us[0], "fused": fc1_act_us[1]},
                      "gemm_total_us": round(tot_us, 1), "gemm_TFLOPs": round(tot_fl / tot_us / 1e6, 1),
-                     "per_gemm": per}
-        del layer, fl, moe, dy
+                     "per_gemm": per, "per_gemm_bf16_wgrad_recipe": per_bf16}
+        del layer, fl, bl, moe, dy
         torch.cuda.empty_cache()
     return out
 
@@ -418,32 +438,42 @@ GP_TEMPLATE = {"FC1 forward": "0, 0", "FC2 forward": "0, 1", "FC2 dgrad": "1, 1"
 GP_FUSED = "FC1 forward + act"
 GP_MODE[GP_FUSED] = "NT bf16 + act epilogue"
 GP_FUSED_ORDER = [GP_FUSED] + GP_ORDER[1:]
+# the BF16-wgrad recipe's wgrads: bf16 TN
+GP_BF16_WGRADS = ["FC2 wgrad bf16", "FC1 wgrad bf16"]
+GP_BF16_ORDER = GP_ORDER[:3] + [GP_BF16_WGRADS[0], GP_ORDER[4], GP_BF16_WGRADS[1]]
+for _g in GP_BF16_WGRADS:
+    GP_MODE[_g] = "TN bf16"
+    GP_TEMPLATE[_g] = "2, 0"
 _FC1, _FC2 = 2 * 65536 * 2 * 768 * 2048, 2 * 65536 * 2048 * 768   # 65,536 routed rows, hidden 2048, intermediate 768
 GP_FL = {"FC1 forward": _FC1, "FC2 forward": _FC2, "FC2 dgrad": _FC2, "FC2 wgrad": _FC2, "FC1 dgrad": _FC1,
-         "FC1 wgrad": _FC1, GP_FUSED: _FC1}
+         "FC1 wgrad": _FC1, GP_FUSED: _FC1, "FC2 wgrad bf16": _FC2, "FC1 wgrad bf16": _FC1}
 # algorithmic bytes of each GEMM: operands and their E8M0 scales read once, bf16 output written once
 GP_BY = {"FC1 forward": 1275e6, "FC2 forward": 528e6, "FC2 dgrad": 447e6, "FC2 wgrad": 593e6, "FC1 dgrad": 787e6,
          "FC1 wgrad": 1048e6,
          # + the MXFP8 activation both ways (codes and E8M0 scales) and the row scale
-         GP_FUSED: 1379e6}
-GP_PEAK = {"NT bf16": 2500.0, "NT bf16 + act epilogue": 2500.0}
+         GP_FUSED: 1379e6,
+         # bf16 operands (dY and the recomputed A; [dgate | dup] and X) and the bf16 dW
+         "FC2 wgrad bf16": 771e6, "FC1 wgrad bf16": 1275e6}
+GP_PEAK = {"NT bf16": 2500.0, "NT bf16 + act epilogue": 2500.0, "TN bf16": 2500.0}
 GP_FETCH_SCALE = 2.0   # FETCH_SIZE calibration against a plain copy of known size
 MOE_ONLY_REPS = 2
 
 
 def _expected_gemm_sequence():
     """GEMM labels in the order `--moe-only` dispatches them: per routing, the
-    plain layer and the layer with the fused FC1 in turn, once untimed and
-    MOE_ONLY_REPS times timed (each the six GEMMs in layer order), the plain
-    layer MOE_ONLY_REPS times with the weight cache valid, each GEMM once
-    untimed and MOE_ONLY_REPS times timed, then FC1 + the activation unfused
-    and fused in turn, once untimed and MOE_ONLY_REPS times."""
+    plain layer, the layer with the fused FC1 and the layer under the
+    BF16-wgrad recipe in turn, once untimed and MOE_ONLY_REPS times timed
+    (each the six GEMMs in layer order), the plain layer MOE_ONLY_REPS times
+    with the weight cache valid, each GEMM of the plain layer and then each
+    bf16 wgrad once untimed and MOE_ONLY_REPS times timed, then FC1 + the
+    activation unfused and fused in turn, once untimed and MOE_ONLY_REPS
+    times."""
     one = []
     for _ in range(1 + MOE_ONLY_REPS):
-        one += GP_ORDER + GP_FUSED_ORDER
+        one += GP_ORDER + GP_FUSED_ORDER + GP_BF16_ORDER
     for _ in range(MOE_ONLY_REPS):
         one += GP_ORDER
-    for g in GP_ORDER:
+    for g in GP_ORDER + GP_BF16_WGRADS:
         one += [g] * (1 + MOE_ONLY_REPS)
     one += ["FC1 forward", GP_FUSED] * (1 + MOE_ONLY_REPS)
     return one * len(MOE_VARIANTS)
@@ -497,7 +527,7 @@ def summarize_gemm_profile(base):
           " roofline-attainable TFLOP/s | % of attainable | L2 hit rate | HBM read MB |"
           + (" MFMA busy % |" if mfu else ""))
     print("|---|---|---|---|---|---|---|---|---|---|---|---|" + ("---|" if mfu else ""))
-    for g in GP_ORDER + [GP_FUSED]:
+    for g in GP_ORDER + [GP_FUSED] + GP_BF16_WGRADS:
         us = statistics.median(dur[g])
         tf = GP_FL[g] / us / 1e6
         peak = GP_PEAK.get(GP_MODE[g], 5000.0)
