@@ -296,3 +296,92 @@ def test_full_size_layer_sampled(mxq, routing):
         same(u8(gr["w13cs"][g]), q[3], "W13 col scales")
     del layer, moe, dy, y
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("routing", ["uniform_plain", "zipf_clamped"])
+def test_full_size_layer_modes_sampled(mxq, routing):
+    """The full-size expert layer (65,536 routed rows, the benchmark's launch
+    configuration) with FC1's fused epilogue and under the BF16-wgrad recipe,
+    against the plain layer on the same inputs (which the test above checks
+    against the oracle):
+      * fused FC1: H13, [dgate | dup], its MXFP8 forms and dW13 equal the plain
+        layer's bit for bit up to the gate / up column interleave; the MXFP8
+        activation, Y, dA, dW2 and dscale equal them outright; dX (its
+        contraction runs over 2I in another order) to fp32-sum rounding;
+      * the recipe: Y, dA, [dgate | dup], its rowwise MXFP8, dscale and dX
+        equal the plain layer's bit for bit; the recomputed bf16 activation
+        equals the oracle's on the sampled experts' rows, and each bf16 wgrad
+        on a 64 x 64 block over each sampled expert's whole row range is
+        within the GEMM tolerance of the oracle's K-grouped GEMM."""
+    from swiglu_mxfp8_quant_amd.moe import Layer
+    skewed, clamped = routing.startswith("zipf"), routing.endswith("clamped")
+    print(routing, flush=True)
+    moe = W.moe_layer(0, device="cuda", skewed=skewed)
+    cfg = moe["cfg"]
+    H, I = cfg["hidden"], cfg["inter"]
+    splits = moe["splits"].cpu().numpy()
+    R = int(splits.sum())
+    ro, bo = O.splits_to_offsets(splits)
+    ncb = int(bo[-1])
+    dy = W.moe_grad(R, H, seed=0, device="cuda")
+    out = {}
+    for mode in ("plain", "fused", "recipe"):
+        L = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, fused_fc1=mode == "fused",
+                  recipe="bf16_wgrad" if mode == "recipe" else "mxfp8")
+        y = L.forward(moe["x_perm"], moe["scale"])
+        L.backward(dy)
+        torch.cuda.synchronize()
+        out[mode] = (L, y)
+        print("  ran", mode, flush=True)
+    (lp, yp), (lf, yf), (lr, yr) = out["plain"], out["fused"], out["recipe"]
+    sp, gp = lp.saved, lp.grads
+
+    def eq(a, b, what):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                           b.view(torch.uint8) if b.dtype != torch.uint8 else b), what
+
+    # fused FC1: logical column j of 2I at interleaved column perm[j]
+    j = np.arange(2 * I)
+    g = j % I
+    perm = torch.as_tensor(np.where(j < I, (g // 128) * 256 + g % 128, (g // 128) * 256 + 128 + g % 128),
+                           device="cuda")
+    sf, gf = lf.saved, lf.grads
+    eq(sp["h13"], sf["h13"][:, perm], "fused: H13")
+    for k in ("a_r", "a_c", "as_r"):
+        eq(sp[k], sf[k], f"fused: {k}")
+    eq(sp["as_c"][:ncb], sf["as_c"][:ncb], "fused: as_c")
+    eq(yp, yf, "fused: Y")
+    for k in ("da", "dw2", "dscale"):
+        eq(gp[k], gf[k], f"fused: {k}")
+    eq(gp["dd"], gf["dd"][:, perm], "fused: [dgate | dup]")
+    eq(gp["dq_r"], gf["dq_r"][:, perm], "fused: dact rowwise codes")
+    eq(gp["dq_c"], gf["dq_c"][:, perm], "fused: dact colwise codes")
+    eq(gp["dqs_c"][:ncb], gf["dqs_c"][:ncb][:, perm], "fused: dact colwise scales")
+    eq(gp["dw13"], gf["dw13"][:, perm, :], "fused: dW13")
+    a, b = gp["dx"].double(), gf["dx"].double()
+    assert torch.all((a - b).abs() <= 1e-2 * a.abs().max() + 1e-2 * a.abs()).item(), "fused: dX"
+    # the recipe
+    gr_ = lr.grads
+    eq(yp, yr, "recipe: Y")
+    for k in ("da", "dd", "dq_r", "dqs_r", "dscale", "dx"):
+        eq(gp[k], gr_[k], f"recipe: {k}")
+    kind = O.CLAMPED_SWIGLU if clamped else O.SWIGLU
+    scale = moe["scale"].cpu().numpy()
+    dyb_dev = dy
+    for gi in _pick_experts(splits):
+        r0, r1 = int(ro[gi]), int(ro[gi + 1])
+        allr = np.arange(r0, r1)
+        h13 = _host(lr.saved["h13"], allr)
+        a_ref = O.swiglu_fwd(h13[:, :I], h13[:, I:], scale[r0:r1], kind, 7.0)
+        a_got = _host(gr_["a_bf16"], allr)
+        same(a_got, a_ref, f"recipe: bf16 activation, expert {gi}")
+        grp = np.array([0, r1 - r0], np.int64)
+        for name, Ah, Bh, outt, ms, ns in (
+                ("FC2 wgrad", _host(dyb_dev, allr), a_got, gr_["dw2"], slice(224, 288), slice(224, 288)),
+                ("FC1 wgrad", _host(gr_["dd"], allr), _host(moe["x_perm"], allr), gr_["dw13"], slice(736, 800),
+                 slice(224, 288))):
+            A = np.ascontiguousarray(Ah[:, ms])
+            B = np.ascontiguousarray(Bh[:, ns])
+            ref = O.grouped_gemm("k", grp, 64, 64, 0, O.Operand("bf16", A, 0, 1, 64), O.Operand("bf16", B, 0, 1, 64),
+                                 "bf16")
+            close(bits(outt[gi, ms, ns]), ref[0], f"recipe: {name} expert {gi}")
