@@ -23,8 +23,11 @@ Outside the timed region, for the record:
     128 experts, top-8, intermediate 768) forward + backward through
     swiglu_mxfp8_quant_amd.moe with uniform softmax top-8 routing and plain
     SwiGLU, and with skewed Zipf(1.2) routing (8 empty experts) and the plain
-    and the clamped SwiGLU: each grouped GEMM's median time and TFLOP/s, and
-    the whole layer's wall time;
+    and the clamped SwiGLU: the whole layer's wall time (plain, with FC1's
+    fused activation epilogue, and under the BF16-wgrad recipe, timed in
+    turn; and the plain layer with its MXFP8 weight cache valid), each
+    grouped GEMM's median time and TFLOP/s, the recipe's bf16 wgrads, and
+    FC1 + activation unfused against fused;
   * gemm_supplementary: a compute-bound grouped GEMM outside the workload
     configurations, labelled as such;
   * clocks: the GPU's current sclk / mclk as rocm-smi reports them;
