@@ -247,8 +247,10 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K,
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same computation, arguments and results, with no workspace argument.  The
  * dscale partial sums go to a scratch array built into the library, 16 MiB
- * per GPU (held until the process ends), which covers M * ceil(K / 512) <=
- * 4,194,304 (e.g. M = 131072 at K = 8192); a larger call with dscale != NULL
+ * per GPU (held until the process ends), which covers every call whose
+ * mxq_swiglu_quantize_bwd_workspace is at most 16 MiB (one fp32 per row and
+ * column slab of 512, or of 256 when K mod 512 is in (0, 256]; e.g. M = 131072
+ * at K = 8192, M = 1,398,101 at K = 768); a larger call with dscale != NULL
  * returns MXQ_ERR_WORKSPACE before touching the device.  Every call on one
  * GPU shares that GPU's scratch: calls that overlap on one GPU (two streams,
  * two threads) race on it and must be ordered by the caller.  The stream must
