@@ -145,8 +145,8 @@ def measured_traffic():
     tf = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         rec = json.load(open(tf))["bwd_both_131072x8192"]
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])
+        if hashlib.sha256(src).hexdigest() != rec["sources_sha256"]:
             return None
         return int(rec["traffic_bytes"])
     except (OSError, KeyError, ValueError):
