@@ -27,7 +27,8 @@ Outside the timed region, for the record:
     fused activation epilogue, and under the BF16-wgrad recipe, timed in
     turn; and the plain layer with its MXFP8 weight cache valid), each
     grouped GEMM's median time and TFLOP/s, the recipe's bf16 wgrads, and
-    FC1 + activation unfused against fused;
+    FC1 + activation unfused against fused; and (gemm.graph) the plain layer
+    eager against a HIP-graph replay of the same step;
   * gemm_supplementary: a compute-bound grouped GEMM outside the workload
     configurations, labelled as such;
   * clocks: the GPU's current sclk / mclk as rocm-smi reports them;
@@ -292,6 +293,38 @@ def moe_section(m, torch, W, reps=5):
                      "per_gemm": per, "per_gemm_bf16_wgrad_recipe": per_bf16}
         del layer, fl, bl, moe, dy
         torch.cuda.empty_cache()
+    return out
+
+
+def graph_section(torch, W, reps=10):
+    """The plain expert layer (uniform routing), forward + backward, eager
+    against one HIP-graph replay of the same step (moe.capture_step), timed
+    in turn; with the weight cache invalid (re-quantized every step) and
+    valid."""
+    from swiglu_mxfp8_quant_amd.moe import Layer, capture_step
+    moe = W.moe_layer(0, device="cuda")
+    H = moe["cfg"]["hidden"]
+    R = int(moe["splits"].sum())
+    dy = W.moe_grad(R, H, seed=0, device="cuda")
+    eager = Layer(moe["splits"], moe["w13"], moe["w2"])
+    captured = Layer(moe["splits"], moe["w13"], moe["w2"])
+    graph, _ = capture_step(captured, moe["x_perm"], moe["scale"], dy)
+
+    def step():
+        eager.forward(moe["x_perm"], moe["scale"])
+        eager.backward(dy)
+    step()
+    graph.replay()
+    torch.cuda.synchronize()
+    e_us, g_us = timed_alt(torch, [step, graph.replay], reps)
+    eager.mark_weights_current()
+    captured.mark_weights_current()
+    ec_us, gc_us = timed_alt(torch, [step, graph.replay], reps)
+    out = {"routing": "uniform_plain", "layer_fwd_bwd_eager_us": round(e_us, 1),
+           "layer_fwd_bwd_graph_us": round(g_us, 1), "cached_weights_eager_us": round(ec_us, 1),
+           "cached_weights_graph_us": round(gc_us, 1)}
+    del graph, eager, captured, moe, dy
+    torch.cuda.empty_cache()
     return out
 
 
@@ -684,6 +717,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_moe:
         out["gemm"] = moe_section(m, torch, W)
+        out["gemm"]["graph"] = graph_section(torch, W)
         out["gemm_supplementary"] = supplementary_gemm(m, torch)
         print("bench: grouped GEMM record done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:

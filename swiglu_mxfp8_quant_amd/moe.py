@@ -162,6 +162,30 @@ class Layer:
         return dx, dw13, dw2, dscale
 
 
+def capture_step(layer, x_perm, scale, dy):
+    """One forward + backward of `layer` captured into a HIP graph through
+    torch's graph API: the library's launches go to the capturing stream, and
+    the outputs and workspaces the calls allocate come from the graph's memory
+    pool, so every replay recomputes them in place (reachable afterwards as
+    layer.saved, layer.grads and the returned y).  x_perm, scale and dy are
+    read where they lie: new data is copied into them before a replay.  The
+    weight quantizations stay under the layer's device flag, so replays after
+    mark_weights_current() skip them.  One untimed step runs on a side stream
+    first, as graph capture asks.  Returns (graph, y)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x_perm, scale)
+        layer.backward(dy)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y = layer.forward(x_perm, scale)
+        layer.backward(dy)
+    return graph, y
+
+
 def gemm_flops(R, H, I, G=None):
     """FLOPs of the six grouped GEMMs of one forward + backward (2 per MAC)."""
     fc1 = 2 * R * (2 * I) * H
