@@ -19,15 +19,17 @@
 //
 // Design (MI355X-first; the pages' CuTe DSL kernel for GB200 is prior art only):
 //   * A workgroup owns one row tile (a colwise 32-row block, restarting at
-//     every group) and a 512-column slab: the forward splits the 32 rows over
+//     every group) and a column slab: the forward splits the 32 rows over
 //     4 waves of 8, the backward over 8 waves of 4; each lane owns 8
-//     consecutive columns and issues 16-byte coalesced loads of gate and up
-//     (and grad), all rows' loads before any arithmetic.  Work items are laid
-//     out so that each XCD takes a contiguous range of them.
+//     consecutive columns (a 512-column slab, 16-byte coalesced loads of gate
+//     and up, and grad), or 4 (a 256-column slab, 8-byte loads) when the last
+//     512-column slab would be at most half full; all rows' loads before any
+//     arithmetic.  Work items are laid out so that each XCD takes a
+//     contiguous range of them.
 //   * Colwise: each wave keeps its rows' bf16 results in registers and the
 //     32x1 amax combines the waves' partial maxima through LDS, so no second
-//     HBM pass.  Rowwise: the 1x32 amax is a DPP max over the 4 lanes of the
-//     block.
+//     HBM pass.  Rowwise: the 1x32 amax is a DPP max over the 4 (or 8) lanes
+//     of the block.
 //   * amax is an integer max of |bf16| bit patterns (NaN/Inf patterns sort
 //     above every finite value), the scale byte comes straight from the amax
 //     exponent bits, and gfx950's v_cvt_scalef32_pk_fp8_bf16 converts bf16
@@ -668,7 +670,7 @@ __device__ __forceinline__ void bwd_fix_slow(const BwdArgs &a, int64_t rbase, in
 }
 
 // Backward over one tile x slab (8 waves of 4 rows, else as the forward).  Each lane
-// owns 8 columns j of gate/up/grad and produces dgate (columns j of
+// owns CPT columns j of gate/up/grad and produces dgate (columns j of
 // [dgate | dup]) and dup (columns K + j); with gate and up interleaved in
 // blocks of il columns, the gradient takes the same layout (dgate at
 // 2 il (j / il) + j % il, dup il columns on).  SReLU (unary) produces dx alone,
