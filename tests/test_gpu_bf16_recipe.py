@@ -306,3 +306,42 @@ def test_layer_bf16_wgrad_recipe(mxq, skewed, clamped, fused):
     ref13 = O.grouped_gemm("k", ro_np, 2 * I, H, 0, O.Operand("bf16", ddb, 0, 1, 2 * I),
                            O.Operand("bf16", xb, 0, 1, H), "bf16")
     check_close(out_np(lb.grads["dw13"]), ref_np(ref13, "bf16"))
+
+
+def many_splits(rng, G, busy, top):
+    splits = [0] * G
+    for g in rng.choice(G, busy, replace=False):
+        splits[int(g)] = int(rng.integers(1, top))
+    splits[G - 1] = 257
+    return splits
+
+
+def test_bf16_many_groups_scan_path(mxq):
+    """More groups than the LDS group tables hold (1024): the launches look
+    every tile's group up by scanning the offsets (NN) or read them from
+    global memory (TN, static order: the dynamic order needs the tables);
+    mostly empty groups, a few of several tiles."""
+    rng = np.random.default_rng(37)
+    G, N, K = 1500, 48, 96
+    splits = many_splits(rng, G, 30, 300)
+    ro, _, ro_np = offsets(mxq, splits)
+    R = sum(splits)
+    A = rand_bf16(rng, (R, K))
+    B = rand_bf16(rng, (G, K, N), 0.05)
+    ref = O.grouped_gemm("m", ro_np, 0, N, K, O.Operand("bf16", A, 0, K, 1), O.Operand("bf16", B, K * N, 1, N), "bf16")
+    for max_wg in (0, 8):
+        out = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+        mxq.grouped_gemm(mxq.GEMM_NN, ro, dev(A), dev(B), out, max_workgroups=max_wg)
+        torch.cuda.synchronize()
+        check_close(out_np(out), ref_np(ref, "bf16"))
+    M, N2 = 32, 48
+    At = rand_bf16(rng, (R, M))
+    Bt = rand_bf16(rng, (R, N2), 0.05)
+    ref = O.grouped_gemm("k", ro_np, M, N2, 0, O.Operand("bf16", At, 0, 1, M), O.Operand("bf16", Bt, 0, 1, N2), "f32")
+    out = torch.full((G, M, N2), 7.0, dtype=torch.float32, device="cuda")
+    mxq.grouped_gemm(mxq.GEMM_TN, ro, dev(At), dev(Bt), out)
+    torch.cuda.synchronize()
+    got = out_np(out)
+    check_close(got, ref_np(ref, "f32"))
+    empty = [g for g in range(G) if splits[g] == 0]
+    assert np.all(got[empty] == 0)

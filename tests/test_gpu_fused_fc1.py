@@ -182,3 +182,16 @@ def test_layer_fused_fc1_matches_unfused(mxq, skewed, clamped):
     assert np.array_equal(bits(dw13p), bits(dw13f)[:, perm, :])
     a, b = dxp.double().cpu().numpy(), dxf.double().cpu().numpy()
     assert np.all(np.abs(a - b) <= 1e-2 * np.abs(a).max() + 1e-2 * np.abs(a)), np.abs(a - b).max()
+
+
+def test_fused_fc1_many_groups_scan_path(mxq):
+    """More groups than the LDS group tables hold (1024): the fused epilogue
+    in the launches that scan the offsets for every tile's group (and find
+    each tile's colwise scale row through block_off)."""
+    rng = np.random.default_rng(41)
+    G = 1100
+    splits = [0] * G
+    for g in rng.choice(G, 12, replace=False):
+        splits[int(g)] = int(rng.integers(1, 300))
+    splits[G - 1] = 290
+    run_case(mxq, splits, H=96, I=128, clamped=False, seed=41)
