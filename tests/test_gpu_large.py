@@ -1,7 +1,7 @@
 """GPU checks past the 32-bit boundaries: the fused forward and backward on
 more than 2^31 elements (row offsets past 2^32 bytes), the MXFP8 NT grouped
 GEMM with an operand of more than 4 GiB, and the bf16 K-grouped GEMM over a
-group of more than a million rows (operand bytes past 2^31), each checked
+group whose operand spans more than 2^31 bytes, each checked
 against the oracle on rows or blocks lying past the boundary.
 
 Page "[mxfp8 training] Add a fused gated-activation (SwiGLU) + MXFP8
@@ -128,13 +128,13 @@ def small_ints(M, K, seed):
 
 
 def test_bf16_wgrad_group_past_2_31_bytes(mxq):
-    """bf16 K-grouped (TN) over a group of 1,100,000 rows of 1024 columns
-    (2.1 GiB per operand, contraction offsets past 2^31 bytes).  Inputs are
-    integers in [-2, 2], so every partial sum (at most 4.4e6 < 2^24) is exact
-    in fp32 and the result equals the oracle's bit for bit in any order: a
-    64 x 64 block of the weight gradient, summed over every row."""
-    splits = [3, 1100000, 0]
-    R, M, N, G = sum(splits), 1024, 256, len(splits)
+    """bf16 K-grouped (TN) over a group of 300,000 rows of 4096 columns
+    (2.3 GiB for that operand, contraction offsets past 2^31 bytes).  Inputs
+    are integers in [-2, 2], so every partial sum (at most 1.2e6 < 2^24) is
+    exact in fp32 and the result equals the oracle's bit for bit in any
+    order: a 64 x 64 block of the weight gradient, summed over every row."""
+    splits = [3, 300000, 0]
+    R, M, N, G = sum(splits), 4096, 256, len(splits)
     print("bf16 wgrad", R, flush=True)
     ro, _, _ = mxq.splits_to_offsets(torch.tensor(splits, dtype=torch.int64, device="cuda"))
     A = small_ints(R, M, 81)
@@ -142,10 +142,10 @@ def test_bf16_wgrad_group_past_2_31_bytes(mxq):
     out = torch.empty((G, M, N), dtype=torch.float32, device="cuda")
     mxq.grouped_gemm(mxq.GEMM_TN, ro, A, B, out)
     torch.cuda.synchronize()
-    ms, ns = slice(960, 1024), slice(192, 256)
-    a = np.ascontiguousarray(bits(A[3:3 + 1100000, ms]))
-    bb = np.ascontiguousarray(bits(B[3:3 + 1100000, ns]))
-    ref = O.grouped_gemm("k", np.array([0, 1100000], np.int64), 64, 64, 0, O.Operand("bf16", a, 0, 1, 64),
+    ms, ns = slice(4032, 4096), slice(192, 256)
+    a = np.ascontiguousarray(bits(A[3:3 + 300000, ms]))
+    bb = np.ascontiguousarray(bits(B[3:3 + 300000, ns]))
+    ref = O.grouped_gemm("k", np.array([0, 300000], np.int64), 64, 64, 0, O.Operand("bf16", a, 0, 1, 64),
                          O.Operand("bf16", bb, 0, 1, 64), "f32")[0]
     got = out[1, ms, ns].cpu().numpy()
     assert np.array_equal(got, ref)
