@@ -209,6 +209,9 @@ def moe_section(m, torch, W, reps=5):
         # in blocks of 128), and under the BF16-wgrad recipe
         fl = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, fused_fc1=True)
         bl = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, recipe="bf16_wgrad")
+        # the recipe with the fused FC1 (its epilogue then writes the rowwise
+        # cast only)
+        fbl = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, fused_fc1=True, recipe="bf16_wgrad")
         dy = W.moe_grad(R, H, seed=0, device="cuda")
         xs, sc = moe["x_perm"], moe["scale"]
 
@@ -223,11 +226,17 @@ def moe_section(m, torch, W, reps=5):
         def full_bf16():
             bl.forward(xs, sc)
             bl.backward(dy)
+
+        def full_bf16_fused():
+            fbl.forward(xs, sc)
+            fbl.backward(dy)
         full()
         full_fused()
         full_bf16()
+        full_bf16_fused()
         torch.cuda.synchronize()
-        layer_us, fused_us, bf16_us = timed_alt(torch, [full, full_fused, full_bf16], reps)
+        layer_us, fused_us, bf16_us, bf16_fused_us = timed_alt(torch, [full, full_fused, full_bf16, full_bf16_fused],
+                                                                reps)
         # the plain layer with the MXFP8 weight cache valid (the device flag
         # skips the weight quantizations, as on the micro-batches after a
         # weight update)
@@ -281,17 +290,26 @@ def moe_section(m, torch, W, reps=5):
                                                  clamped=clamped, limit=layer.limit))
         fused = lambda: m.grouped_gemm_swiglu(ro, xs, fl.w13, h13, sc, True, True, block_off=bo,
                                               clamped=clamped, limit=layer.limit)
-        unfused()
-        fused()
-        fc1_act_us = [round(v, 1) for v in timed_alt(torch, [unfused, fused], reps)]
+        # rowwise only (the BF16-wgrad recipe's cast)
+        unfused_r = lambda: (m.grouped_gemm(m.GEMM_NT, ro, xs, moe["w13"], h13),
+                             m.swiglu_quantize_fwd(h13[:, :I], h13[:, I:], sc, True, False,
+                                                   clamped=clamped, limit=layer.limit))
+        fused_r = lambda: m.grouped_gemm_swiglu(ro, xs, fl.w13, h13, sc, True, False, clamped=clamped,
+                                                limit=layer.limit)
+        for fn in (unfused, fused, unfused_r, fused_r):
+            fn()
+        fc1_act_us = [round(v, 1) for v in timed_alt(torch, [unfused, fused, unfused_r, fused_r], reps)]
         out[name] = {"routed_rows": R, "layer_fwd_bwd_us": round(layer_us, 1),
                      "layer_fwd_bwd_fused_fc1_us": round(fused_us, 1),
                      "layer_fwd_bwd_bf16_wgrad_recipe_us": round(bf16_us, 1),
+                     "layer_fwd_bwd_bf16_wgrad_recipe_fused_fc1_us": round(bf16_fused_us, 1),
                      "layer_fwd_bwd_cached_weights_us": round(cached_us, 1),
-                     "fc1_plus_activation_fwd_us": {"unfused": fc1_act_us[0], "fused": fc1_act_us[1]},
+                     "fc1_plus_activation_fwd_us": {"unfused": fc1_act_us[0], "fused": fc1_act_us[1],
+                                                    "unfused_rowwise": fc1_act_us[2],
+                                                    "fused_rowwise": fc1_act_us[3]},
                      "gemm_total_us": round(tot_us, 1), "gemm_TFLOPs": round(tot_fl / tot_us / 1e6, 1),
                      "per_gemm": per, "per_gemm_bf16_wgrad_recipe": per_bf16}
-        del layer, fl, bl, moe, dy
+        del layer, fl, bl, fbl, moe, dy
         torch.cuda.empty_cache()
     return out
 
@@ -477,6 +495,7 @@ GP_FUSED_ORDER = [GP_FUSED] + GP_ORDER[1:]
 # the BF16-wgrad recipe's wgrads: bf16 TN
 GP_BF16_WGRADS = ["FC2 wgrad bf16", "FC1 wgrad bf16"]
 GP_BF16_ORDER = GP_ORDER[:3] + [GP_BF16_WGRADS[0], GP_ORDER[4], GP_BF16_WGRADS[1]]
+GP_BF16_FUSED_ORDER = [GP_FUSED] + GP_BF16_ORDER[1:]
 for _g in GP_BF16_WGRADS:
     GP_MODE[_g] = "TN bf16"
     GP_TEMPLATE[_g] = "2, 0"
@@ -497,21 +516,21 @@ MOE_ONLY_REPS = 2
 
 def _expected_gemm_sequence():
     """GEMM labels in the order `--moe-only` dispatches them: per routing, the
-    plain layer, the layer with the fused FC1 and the layer under the
-    BF16-wgrad recipe in turn, once untimed and MOE_ONLY_REPS times timed
-    (each the six GEMMs in layer order), the plain layer MOE_ONLY_REPS times
-    with the weight cache valid, each GEMM of the plain layer and then each
-    bf16 wgrad once untimed and MOE_ONLY_REPS times timed, then FC1 + the
-    activation unfused and fused in turn, once untimed and MOE_ONLY_REPS
-    times."""
+    plain layer, the layer with the fused FC1, the layer under the BF16-wgrad
+    recipe and the recipe with the fused FC1 in turn, once untimed and
+    MOE_ONLY_REPS times timed (each the six GEMMs in layer order), the plain
+    layer MOE_ONLY_REPS times with the weight cache valid, each GEMM of the
+    plain layer and then each bf16 wgrad once untimed and MOE_ONLY_REPS times
+    timed, then FC1 + the activation unfused and fused, both directions and
+    rowwise only, in turn, once untimed and MOE_ONLY_REPS times."""
     one = []
     for _ in range(1 + MOE_ONLY_REPS):
-        one += GP_ORDER + GP_FUSED_ORDER + GP_BF16_ORDER
+        one += GP_ORDER + GP_FUSED_ORDER + GP_BF16_ORDER + GP_BF16_FUSED_ORDER
     for _ in range(MOE_ONLY_REPS):
         one += GP_ORDER
     for g in GP_ORDER + GP_BF16_WGRADS:
         one += [g] * (1 + MOE_ONLY_REPS)
-    one += ["FC1 forward", GP_FUSED] * (1 + MOE_ONLY_REPS)
+    one += ["FC1 forward", GP_FUSED, "FC1 forward", GP_FUSED] * (1 + MOE_ONLY_REPS)
     return one * len(MOE_VARIANTS)
 
 

@@ -312,7 +312,9 @@ def test_full_size_layer_modes_sampled(mxq, routing):
         equal the plain layer's bit for bit; the recomputed bf16 activation
         equals the oracle's on the sampled experts' rows, and each bf16 wgrad
         on a 64 x 64 block over each sampled expert's whole row range is
-        within the GEMM tolerance of the oracle's K-grouped GEMM."""
+        within the GEMM tolerance of the oracle's K-grouped GEMM;
+      * the recipe with the fused FC1: the recipe's results bit for bit, up
+        to the gate / up interleave."""
     from swiglu_mxfp8_quant_amd.moe import Layer
     skewed, clamped = routing.startswith("zipf"), routing.endswith("clamped")
     print(routing, flush=True)
@@ -325,15 +327,15 @@ def test_full_size_layer_modes_sampled(mxq, routing):
     ncb = int(bo[-1])
     dy = W.moe_grad(R, H, seed=0, device="cuda")
     out = {}
-    for mode in ("plain", "fused", "recipe"):
-        L = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, fused_fc1=mode == "fused",
-                  recipe="bf16_wgrad" if mode == "recipe" else "mxfp8")
+    for mode in ("plain", "fused", "recipe", "fused_recipe"):
+        L = Layer(moe["splits"], moe["w13"], moe["w2"], clamped=clamped, fused_fc1=mode.startswith("fused"),
+                  recipe="bf16_wgrad" if mode.endswith("recipe") else "mxfp8")
         y = L.forward(moe["x_perm"], moe["scale"])
         L.backward(dy)
         torch.cuda.synchronize()
         out[mode] = (L, y)
         print("  ran", mode, flush=True)
-    (lp, yp), (lf, yf), (lr, yr) = out["plain"], out["fused"], out["recipe"]
+    (lp, yp), (lf, yf), (lr, yr), (lfr, yfr) = out["plain"], out["fused"], out["recipe"], out["fused_recipe"]
     sp, gp = lp.saved, lp.grads
 
     def eq(a, b, what):
@@ -385,3 +387,14 @@ def test_full_size_layer_modes_sampled(mxq, routing):
             ref = O.grouped_gemm("k", grp, 64, 64, 0, O.Operand("bf16", A, 0, 1, 64), O.Operand("bf16", B, 0, 1, 64),
                                  "bf16")
             close(bits(outt[gi, ms, ns]), ref[0], f"recipe: {name} expert {gi}")
+    # the recipe with the fused FC1 (rowwise cast in the epilogue): the
+    # recipe's results up to the interleave of the gate / up columns
+    gfr = lfr.grads
+    eq(yr, yfr, "fused recipe: Y")
+    eq(lr.saved["a_r"], lfr.saved["a_r"], "fused recipe: a_r")
+    eq(lr.saved["h13"], lfr.saved["h13"][:, perm], "fused recipe: H13")
+    for k in ("da", "dscale", "dw2", "a_bf16"):
+        eq(gr_[k], gfr[k], f"fused recipe: {k}")
+    eq(gr_["dd"], gfr["dd"][:, perm], "fused recipe: [dgate | dup]")
+    eq(gr_["dq_r"], gfr["dq_r"][:, perm], "fused recipe: dact rowwise codes")
+    eq(gr_["dw13"], gfr["dw13"][:, perm, :], "fused recipe: dW13")
