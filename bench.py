@@ -492,24 +492,31 @@ GP_TEMPLATE = {"FC1 forward": "0, 0", "FC2 forward": "0, 1", "FC2 dgrad": "1, 1"
 GP_FUSED = "FC1 forward + act"
 GP_MODE[GP_FUSED] = "NT bf16 + act epilogue"
 GP_FUSED_ORDER = [GP_FUSED] + GP_ORDER[1:]
+# the same epilogue writing the rowwise cast only (the BF16-wgrad recipe's)
+GP_FUSED_ROW = "FC1 forward + rowwise act"
+GP_MODE[GP_FUSED_ROW] = "NT bf16 + rowwise act epilogue"
+GP_TEMPLATE[GP_FUSED_ROW] = "0, 0"
 # the BF16-wgrad recipe's wgrads: bf16 TN
 GP_BF16_WGRADS = ["FC2 wgrad bf16", "FC1 wgrad bf16"]
 GP_BF16_ORDER = GP_ORDER[:3] + [GP_BF16_WGRADS[0], GP_ORDER[4], GP_BF16_WGRADS[1]]
-GP_BF16_FUSED_ORDER = [GP_FUSED] + GP_BF16_ORDER[1:]
+GP_BF16_FUSED_ORDER = [GP_FUSED_ROW] + GP_BF16_ORDER[1:]
 for _g in GP_BF16_WGRADS:
     GP_MODE[_g] = "TN bf16"
     GP_TEMPLATE[_g] = "2, 0"
 _FC1, _FC2 = 2 * 65536 * 2 * 768 * 2048, 2 * 65536 * 2048 * 768   # 65,536 routed rows, hidden 2048, intermediate 768
 GP_FL = {"FC1 forward": _FC1, "FC2 forward": _FC2, "FC2 dgrad": _FC2, "FC2 wgrad": _FC2, "FC1 dgrad": _FC1,
-         "FC1 wgrad": _FC1, GP_FUSED: _FC1, "FC2 wgrad bf16": _FC2, "FC1 wgrad bf16": _FC1}
+         "FC1 wgrad": _FC1, GP_FUSED: _FC1, GP_FUSED_ROW: _FC1, "FC2 wgrad bf16": _FC2, "FC1 wgrad bf16": _FC1}
 # algorithmic bytes of each GEMM: operands and their E8M0 scales read once, bf16 output written once
 GP_BY = {"FC1 forward": 1275e6, "FC2 forward": 528e6, "FC2 dgrad": 447e6, "FC2 wgrad": 593e6, "FC1 dgrad": 787e6,
          "FC1 wgrad": 1048e6,
          # + the MXFP8 activation both ways (codes and E8M0 scales) and the row scale
          GP_FUSED: 1379e6,
+         # + the rowwise MXFP8 activation and the row scale
+         GP_FUSED_ROW: 1327e6,
          # bf16 operands (dY and the recomputed A; [dgate | dup] and X) and the bf16 dW
          "FC2 wgrad bf16": 771e6, "FC1 wgrad bf16": 1275e6}
-GP_PEAK = {"NT bf16": 2500.0, "NT bf16 + act epilogue": 2500.0, "TN bf16": 2500.0}
+GP_PEAK = {"NT bf16": 2500.0, "NT bf16 + act epilogue": 2500.0, "NT bf16 + rowwise act epilogue": 2500.0,
+           "TN bf16": 2500.0}
 GP_FETCH_SCALE = 2.0   # FETCH_SIZE calibration against a plain copy of known size
 MOE_ONLY_REPS = 2
 
@@ -530,7 +537,7 @@ def _expected_gemm_sequence():
         one += GP_ORDER
     for g in GP_ORDER + GP_BF16_WGRADS:
         one += [g] * (1 + MOE_ONLY_REPS)
-    one += ["FC1 forward", GP_FUSED, "FC1 forward", GP_FUSED] * (1 + MOE_ONLY_REPS)
+    one += ["FC1 forward", GP_FUSED, "FC1 forward", GP_FUSED_ROW] * (1 + MOE_ONLY_REPS)
     return one * len(MOE_VARIANTS)
 
 
@@ -545,7 +552,7 @@ def _gemm_labels(rows):
     for r, lab in zip(rows, seq):
         t = re.search(r"gemm_kernel<(\d+), (\d+),[^>]*?(\d+)>", r["Kernel_Name"])
         if (t is None or f"{t.group(1)}, {t.group(2)}" != GP_TEMPLATE[lab]
-                or (t.group(3) != "0") != (lab == GP_FUSED)):
+                or (t.group(3) != "0") != (lab in (GP_FUSED, GP_FUSED_ROW))):
             raise SystemExit(f"GEMM profile: dispatch {r['Dispatch_Id']} ({r['Kernel_Name'][:60]}) is not {lab}")
         out[int(r["Dispatch_Id"])] = lab
     return out
@@ -582,7 +589,7 @@ def summarize_gemm_profile(base):
           " roofline-attainable TFLOP/s | % of attainable | L2 hit rate | HBM read MB |"
           + (" MFMA busy % |" if mfu else ""))
     print("|---|---|---|---|---|---|---|---|---|---|---|---|" + ("---|" if mfu else ""))
-    for g in GP_ORDER + [GP_FUSED] + GP_BF16_WGRADS:
+    for g in GP_ORDER + [GP_FUSED, GP_FUSED_ROW] + GP_BF16_WGRADS:
         us = statistics.median(dur[g])
         tf = GP_FL[g] / us / 1e6
         peak = GP_PEAK.get(GP_MODE[g], 5000.0)
