@@ -45,6 +45,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// x rounded to bf16 (RNE), as an fp32: converting x into the high half of a
+// packed pair whose low half is +0 gives exactly those bits, in one
+// instruction.  (Written out: from the pair's plain form the compiler makes a
+// convert into the low half and a shift or permute, two instructions per
+// element, as it does when a packed pair is unpacked.)
+__device__ __forceinline__ float bf16_round(float x) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+    return __uint_as_float(r);
+}
+
 // Materialize x here: keeps the compiler from sinking the packing of a result
 // word past later code (which would keep two fp32 values live instead of one word).
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
@@ -181,8 +192,7 @@ __device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, 
         // unless it leaves the normal range; h = bf16(a * s) as SwiGLU's product
         const float v0 = relu_f(lo_f(gw)), v1 = relu_f(hi_f(gw));
         const float t0 = v0 * v0, t1 = v1 * v1;
-        const uint32_t aw = pack_bf16(t0, t1);
-        const float a0 = lo_f(aw), a1 = hi_f(aw);
+        const float a0 = bf16_round(t0), a1 = bf16_round(t1);
         const float h0 = a0 * s, h1 = a1 * s;
         hw = pack_bf16(h0, h1);
         (void)uw;
@@ -198,8 +208,7 @@ __device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, 
         }
         const Sig s0 = sig_fast(g0), s1 = sig_fast(g1);
         const float t0 = g0 * s0.sig, t1 = g1 * s1.sig;
-        const uint32_t aw = pack_bf16(t0, t1);
-        const float p0 = lo_f(aw) * u0, p1 = hi_f(aw) * u1;
+        const float p0 = bf16_round(t0) * u0, p1 = bf16_round(t1) * u1;
         const float h0 = p0 * s, h1 = p1 * s;
         hw = pack_bf16(h0, h1);
         uint32_t risky = 0u;

@@ -504,8 +504,7 @@ __device__ __forceinline__ bool near_tie(float t, float bound) {
 __device__ __forceinline__ BwdPair bwd_pair_srelu(uint32_t dw, uint32_t gw, float s) {
     const float v[2] = {relu_f(lo_f(gw)), relu_f(hi_f(gw))};
     const float dh[2] = {lo_f(dw), hi_f(dw)};
-    const uint32_t aw = pack_bf16(v[0] * v[0], v[1] * v[1]);
-    const float av[2] = {lo_f(aw), hi_f(aw)};
+    const float av[2] = {bf16_round(v[0] * v[0]), bf16_round(v[1] * v[1])};
     BwdPair out;
     float vdx[2];
     out.risky = 0u;
@@ -548,8 +547,7 @@ __device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t u
         om[j] = z.e * z.sig;           // 1 - sigma without cancellation
         t[j] = g[j] * z.sig;
     }
-    const uint32_t aw = pack_bf16(t[0], t[1]);
-    const float av[2] = {lo_f(aw), hi_f(aw)};
+    const float av[2] = {bf16_round(t[0]), bf16_round(t[1])};
     float vdg[2], vdu[2];
     out.risky = 0u;
     out.dsum = 0.0f;
