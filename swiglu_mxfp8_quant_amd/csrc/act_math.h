@@ -103,6 +103,21 @@ __device__ __forceinline__ Sig sig_fast(float g) {
     return r;
 }
 
+// A comparison's lanes as a wave mask.  The checks below return such masks,
+// combined with scalar ORs: a mask taken of a single comparison is that
+// comparison's own result, whereas a flag made of several comparisons would
+// be turned into a 0 / 1 vector value and compared again.
+__device__ __forceinline__ uint64_t lanes(bool cmp) { return __builtin_amdgcn_ballot_w64(cmp); }
+
+// Lanes where x is not normal-or-zero: the class test's own lane mask (written
+// out, since the mask of the class intrinsic is not taken directly either),
+// inverted within the active lanes.
+__device__ __forceinline__ uint64_t odd_lanes(float x) {
+    uint64_t m;
+    asm("v_cmp_class_f32_e64 %0, %1, %2" : "=s"(m) : "v"(x), "s"(kNormalOrZero));
+    return __builtin_amdgcn_read_exec() & ~m;
+}
+
 // May the fast fp32 silu t of g round to bf16 differently from the exact
 // silu?  Measured against the exact silu for every bf16 g >= -80, the fast
 // value is within 2.03 fp32 ulps for g >= 0 and within 2.25 + 0.7|g| ulps for
@@ -117,17 +132,17 @@ __device__ __forceinline__ Sig sig_fast(float g) {
 // t = g/2 is exact, which is either a bf16 number that the exact silu
 // (larger by ~g^2/4) also rounds to, or sits exactly on a tie (distance 0).
 // For g > 80 the fast value is g itself, also the correctly rounded one.
-__device__ __forceinline__ bool silu_risky(float g, float t) {
+// (Returns the lanes where it may.)
+__device__ __forceinline__ uint64_t silu_risky(float g, float t) {
     const float z = fabsf((float)(short)__float_as_uint(t));
-    return (bool)((int)(g < -80.0f) | (int)((z + fabsf(g)) - g >= 32764.0f));
+    return lanes(g < -80.0f) | lanes((z + fabsf(g)) - g >= 32764.0f);
 }
 
 // May bf16(hs), hs = fl32(p * s) with p exact, differ from the bf16 rounding of
 // the exact product?  Only if hs sits exactly on a bf16 tie, or p / hs are not
-// normal-or-zero (underflow, overflow, NaN/Inf inputs).
-__device__ __forceinline__ bool product_risky(float p, float hs) {
-    const bool tie = (__float_as_uint(hs) & 0xFFFFu) == 0x8000u;
-    return (bool)((int)tie | (int)!normal_or_zero(p) | (int)!normal_or_zero(hs));
+// normal-or-zero (underflow, overflow, NaN/Inf inputs).  (Returns the lanes.)
+__device__ __forceinline__ uint64_t product_risky(float p, float hs) {
+    return lanes((__float_as_uint(hs) & 0xFFFFu) == 0x8000u) | odd_lanes(p) | odd_lanes(hs);
 }
 
 // ------------------------------------------------------------------ quantizer
@@ -180,13 +195,24 @@ __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : (x != x
 template <int ACT>
 constexpr bool gated() { return ACT == ACT_SWIGLU || ACT == ACT_CLAMPED; }
 
+// 2 bits + this lane's bit of `mask`, in one instruction (an add with the
+// mask as the carry in): shifting the flags of a row's elements in, last
+// element first, leaves element k's flag in bit k.
+__device__ __forceinline__ uint32_t shift_in(uint32_t bits, uint64_t mask) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(bits), "s"(mask));
+    return r;
+}
+
 // One element pair of the forward: packed gate / up words -> packed h word.
-// Returns a 2-bit mask of the elements that need the exact path.
+// m0 / m1: the lanes whose low / high element needs the exact path.
 template <int ACT>
-__device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, float L, uint32_t &hw) {
+__device__ __forceinline__ void fwd_pair_r(uint32_t gw, uint32_t uw, float s, float L, uint32_t &hw, uint64_t &m0,
+                                           uint64_t &m1) {
     if constexpr (ACT == ACT_IDENTITY) {
         hw = gw;
-        return 0u;
+        m0 = m1 = 0ull;
     } else if constexpr (ACT == ACT_SRELU) {
         // a = bf16(v * v), v = max(x, 0): the square of a bf16 is exact in fp32
         // unless it leaves the normal range; h = bf16(a * s) as SwiGLU's product
@@ -197,9 +223,8 @@ __device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, 
         hw = pack_bf16(h0, h1);
         (void)uw;
         (void)L;
-        uint32_t risky = (uint32_t)!normal_or_zero(t0) | (uint32_t)product_risky(a0, h0);
-        risky |= ((uint32_t)!normal_or_zero(t1) | (uint32_t)product_risky(a1, h1)) << 1;
-        return risky;
+        m0 = odd_lanes(t0) | product_risky(a0, h0);
+        m1 = odd_lanes(t1) | product_risky(a1, h1);
     } else {
         float g0 = lo_f(gw), g1 = hi_f(gw), u0 = lo_f(uw), u1 = hi_f(uw);
         if constexpr (ACT == ACT_CLAMPED) {
@@ -211,11 +236,17 @@ __device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, 
         const float p0 = bf16_round(t0) * u0, p1 = bf16_round(t1) * u1;
         const float h0 = p0 * s, h1 = p1 * s;
         hw = pack_bf16(h0, h1);
-        uint32_t risky = 0u;
-        risky |= (uint32_t)silu_risky(g0, t0) | (uint32_t)product_risky(p0, h0);
-        risky |= ((uint32_t)silu_risky(g1, t1) | (uint32_t)product_risky(p1, h1)) << 1;
-        return risky;
+        m0 = silu_risky(g0, t0) | product_risky(p0, h0);
+        m1 = silu_risky(g1, t1) | product_risky(p1, h1);
     }
+}
+
+// The same, returning a 2-bit mask of the elements that need the exact path.
+template <int ACT>
+__device__ __forceinline__ uint32_t fwd_pair(uint32_t gw, uint32_t uw, float s, float L, uint32_t &hw) {
+    uint64_t m0, m1;
+    fwd_pair_r<ACT>(gw, uw, s, L, hw, m0, m1);
+    return shift_in(shift_in(0u, m1), m0);
 }
 
 // h = bf16( bf16(silu(g)) * u * s ) in fp64 (the product is exact in fp64)

@@ -365,7 +365,11 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
             if (a.row_scale != nullptr && i < nrow) s = a.row_scale[rbase + i];
         uint32_t bits = 0u;
 #pragma unroll
-        for (int k = 0; k < CPT / 2; k++) bits |= fwd_pair<ACT>(gv[i].w[k], uv[i].w[k], s, a.limit, h[i][k]) << (2 * k);
+        for (int k = CPT / 2 - 1; k >= 0; k--) {   // last pair first: its flags end in the top bits
+            uint64_t m0, m1;
+            fwd_pair_r<ACT>(gv[i].w[k], uv[i].w[k], s, a.limit, h[i][k], m0, m1);
+            if constexpr (ACT != ACT_IDENTITY) bits = shift_in(shift_in(bits, m1), m0);
+        }
         if constexpr (ACT != ACT_IDENTITY) {
             if (!scale_ok(s)) bits = (1u << CPT) - 1u;
             if (!active || i >= nrow) bits = 0u;
@@ -471,7 +475,7 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
 struct BwdPair {
     uint32_t dg, du;     // packed bf16 dgate / dup
     float dsum;          // dh*a*u of both elements
-    uint32_t risky;      // 2-bit mask
+    uint64_t m[2];       // lanes whose low / high element needs the exact path
 };
 
 // Absolute error bound of the fast dgate tdg = fl(P * ds'), ds' =
@@ -491,10 +495,11 @@ __device__ __forceinline__ float dgate_err(float tdg, float P, float g, float si
 // Could an error of at most `bound` move t across a bf16 rounding tie?  The
 // tie of t's own bf16 interval is tested directly; a bound that is not small
 // against the bf16 quantum (2^-8 relative) is treated as risky outright, which
-// covers the ties of the neighbouring intervals.
-__device__ __forceinline__ bool near_tie(float t, float bound) {
+// covers the ties of the neighbouring intervals.  (Returns the lanes where it
+// could.)
+__device__ __forceinline__ uint64_t near_tie(float t, float bound) {
     const float tie = __uint_as_float((__float_as_uint(t) & 0xFFFF0000u) | 0x8000u);
-    return (bool)((int)(fabsf(t - tie) <= bound) | (int)(bound > fabsf(t) * 0x1p-10f));
+    return lanes(fabsf(t - tie) <= bound) | lanes(bound > fabsf(t) * 0x1p-10f);
 }
 
 // SReLU backward of one element pair (x in gw): dx = bf16(dh * s * 2 v),
@@ -507,7 +512,6 @@ __device__ __forceinline__ BwdPair bwd_pair_srelu(uint32_t dw, uint32_t gw, floa
     const float av[2] = {bf16_round(v[0] * v[0]), bf16_round(v[1] * v[1])};
     BwdPair out;
     float vdx[2];
-    out.risky = 0u;
     out.dsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 2; j++) {
@@ -515,8 +519,7 @@ __device__ __forceinline__ BwdPair bwd_pair_srelu(uint32_t dw, uint32_t gw, floa
         const float tdx = q2 * s;                  // one rounding
         vdx[j] = tdx;
         out.dsum += dh[j] * av[j];                 // exact (8 x 8 bits)
-        uint32_t r = (uint32_t)product_risky(q2, tdx) | (uint32_t)!normal_or_zero(v[j] * v[j]);
-        out.risky |= r << j;
+        out.m[j] = product_risky(q2, tdx) | odd_lanes(v[j] * v[j]);
     }
     out.dg = pack_bf16(vdx[0], vdx[1]);
     out.du = 0u;
@@ -549,7 +552,6 @@ __device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t u
     }
     const float av[2] = {bf16_round(t[0]), bf16_round(t[1])};
     float vdg[2], vdu[2];
-    out.risky = 0u;
     out.dsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 2; j++) {
@@ -562,10 +564,11 @@ __device__ __forceinline__ BwdPair bwd_pair(uint32_t dw, uint32_t gw, uint32_t u
         const float ds = sg[j] * (1.0f + g[j] * om[j]);
         const float tdg = P * ds * mg[j];
         vdg[j] = tdg;
-        uint32_t r = (uint32_t)silu_risky(g[j], t[j]) | (uint32_t)product_risky(q, qs);
-        r |= (uint32_t)!normal_or_zero(du_) | (uint32_t)!normal_or_zero(P) | (uint32_t)!normal_or_zero(tdg);
-        r |= (uint32_t)(mg[j] != 0.0f) & (uint32_t)near_tie(tdg, dgate_err(tdg, P, g[j], sg[j], om[j]));
-        out.risky |= r << j;
+        uint64_t m = silu_risky(g[j], t[j]) | product_risky(q, qs) | odd_lanes(du_) | odd_lanes(P) | odd_lanes(tdg);
+        const uint64_t nt = near_tie(tdg, dgate_err(tdg, P, g[j], sg[j], om[j]));
+        if constexpr (ACT == ACT_CLAMPED) m |= lanes(mg[j] != 0.0f) & nt;   // a clamped gate has dgate 0
+        else m |= nt;
+        out.m[j] = m;
     }
     out.dg = pack_bf16(vdg[0], vdg[1]);
     out.du = pack_bf16(vdu[0], vdu[1]);
@@ -730,14 +733,17 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
         const float s = (a.row_scale != nullptr && i < nrow) ? a.row_scale[rbase + i] : 1.0f;
         uint32_t bits = 0u;
         float ds = 0.0f;
+        float pd[CPT / 2];
 #pragma unroll
-        for (int k = 0; k < CPT / 2; k++) {
+        for (int k = CPT / 2 - 1; k >= 0; k--) {   // last pair first: its flags end in the top bits
             const BwdPair p = bwd_pair<ACT>(dv.w[k], gv.w[k], uv.w[k], s, L);
             hg[i][k] = p.dg;
             hu[i][k] = p.du;
-            ds += p.dsum;
-            bits |= p.risky << (2 * k);
+            pd[k] = p.dsum;
+            bits = shift_in(shift_in(bits, p.m[1]), p.m[0]);
         }
+#pragma unroll
+        for (int k = 0; k < CPT / 2; k++) ds += pd[k];   // the pairs' partial sums in column order
         if (!scale_ok(s)) bits = (1u << CPT) - 1u;
         if (!active || i >= nrow) {
             bits = 0u;
