@@ -64,14 +64,23 @@ struct Vec<4> {
     uint32_t w[2];
 };
 
+// One row's CPT columns of a lane, nontemporal, through a buffer resource
+// made from wave-uniform values only: `row` is the row's first element,
+// `row_ok` whether the row lies inside the tile, `off` the lane's byte offset
+// (kOffOut for lanes past the columns).  Rows and lanes outside load zeros
+// (the resource's range is 0, or the offset lies past it) with no vector
+// instruction spent on addresses or zero fills.
+constexpr uint32_t kOffOut = 0x80000000u;   // past every range below
 template <int CPT>
-__device__ __forceinline__ Vec<CPT> load_vec(const uint16_t *p) {
+__device__ __forceinline__ Vec<CPT> load_row(const uint16_t *row, bool row_ok, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(row), (short)0,
+                                                                       row_ok ? 0x7FFFFFF0 : 0, 0x00020000);
     Vec<CPT> v;
     if constexpr (CPT == 8) {
-        const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+        const u32x4_t q = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
         v.w[0] = q.x; v.w[1] = q.y; v.w[2] = q.z; v.w[3] = q.w;
     } else {
-        const u32x2_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+        const u32x2_t q = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2));
         v.w[0] = q.x; v.w[1] = q.y;
     }
     return v;
@@ -344,14 +353,12 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
 
     // pass 1: all loads of the wave's rows, then the fast path
     Vec<CPT> gv[RPW], uv[RPW];
+    const uint32_t goff = active ? (uint32_t)gco * 2u : kOffOut;
 #pragma unroll
     for (int i = 0; i < RPW; i++) {
-        gv[i] = zero_vec<CPT>();
-        uv[i] = zero_vec<CPT>();
-        if (i < nrow && active) {
-            gv[i] = load_vec<CPT>(gate0 + i * a.ld_gate + gco);
-            if constexpr (gated<ACT>()) uv[i] = load_vec<CPT>(up0 + i * a.ld_up + gco);
-        }
+        gv[i] = load_row<CPT>(gate0 + i * a.ld_gate, i < nrow, goff);
+        if constexpr (gated<ACT>()) uv[i] = load_row<CPT>(up0 + i * a.ld_up, i < nrow, goff);
+        else uv[i] = zero_vec<CPT>();
     }
     uint32_t h[RPW][CPT / 2];
     uint32_t risk[NWORDS];
@@ -705,16 +712,17 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
     // pass 1: the fast path, PF rows of loads kept in flight
     constexpr int PF = 4;
     Vec<CPT> db[PF], gb[PF], ub[PF];
+    const uint32_t doff = active ? (uint32_t)co * 2u : kOffOut, goff = active ? (uint32_t)gco * 2u : kOffOut;
+    const uint16_t *grad0 = a.grad + rbase * a.ld_grad, *gate0 = a.gate + rbase * a.ld_gate;
+    const uint16_t *up0 = gated<ACT>() ? a.up + rbase * a.ld_up : nullptr;
+    auto load3 = [&](int j, int i) {   // row i of the wave into prefetch slot j
+        db[j] = load_row<CPT>(grad0 + i * a.ld_grad, i < nrow, doff);
+        gb[j] = load_row<CPT>(gate0 + i * a.ld_gate, i < nrow, goff);
+        if constexpr (gated<ACT>()) ub[j] = load_row<CPT>(up0 + i * a.ld_up, i < nrow, goff);
+        else ub[j] = zero_vec<CPT>();
+    };
 #pragma unroll
-    for (int i = 0; i < PF; i++) {
-        db[i] = gb[i] = ub[i] = zero_vec<CPT>();
-        if (i < nrow && active) {
-            const int64_t r = rbase + i;
-            db[i] = load_vec<CPT>(a.grad + r * a.ld_grad + co);
-            gb[i] = load_vec<CPT>(a.gate + r * a.ld_gate + gco);
-            if constexpr (gated<ACT>()) ub[i] = load_vec<CPT>(a.up + r * a.ld_up + gco);
-        }
-    }
+    for (int i = 0; i < PF; i++) load3(i, i);
     uint32_t hg[BRPW][CPT / 2], hu[BRPW][CPT / 2];
     uint32_t risk[BNWORDS];
     float dsum[BRPW];
@@ -724,12 +732,7 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
 #pragma unroll
     for (int i = 0; i < BRPW; i++) {
         const Vec<CPT> dv = db[i % PF], gv = gb[i % PF], uv = ub[i % PF];
-        if (i + PF < BRPW && i + PF < nrow && active) {
-            const int64_t r = rbase + i + PF;
-            db[i % PF] = load_vec<CPT>(a.grad + r * a.ld_grad + co);
-            gb[i % PF] = load_vec<CPT>(a.gate + r * a.ld_gate + gco);
-            if constexpr (gated<ACT>()) ub[i % PF] = load_vec<CPT>(a.up + r * a.ld_up + gco);
-        }
+        if (i + PF < BRPW) load3(i % PF, i + PF);
         const float s = (a.row_scale != nullptr && i < nrow) ? a.row_scale[rbase + i] : 1.0f;
         uint32_t bits = 0u;
         float ds = 0.0f;
