@@ -86,6 +86,33 @@ __device__ __forceinline__ Vec<CPT> load_row(const uint16_t *row, bool row_ok, u
     return v;
 }
 
+// Stores through the same kind of resource: `row` wave-uniform, lanes with an
+// offset of kOffOut (or rows with row_ok false) write nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(void *row, bool row_ok) {
+    return __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_ok ? 0x7FFFFFF0 : 0, 0x00020000);
+}
+
+// CPT bf16 (CPT / 2 packed words) at byte offset `off`, nontemporal
+template <int CPT>
+__device__ __forceinline__ void store_row_bf16(uint16_t *row, bool row_ok, uint32_t off, const uint32_t *w) {
+    const __amdgpu_buffer_rsrc_t r = row_rsrc(row, row_ok);
+    if constexpr (CPT == 8)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w[0], w[1], w[2], w[3]}, r, off, 0, 2);
+    else __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w[0], w[1]}, r, off, 0, 2);
+}
+
+// CPT codes (CPT / 4 words) at byte offset `off`, nontemporal
+template <int CPT>
+__device__ __forceinline__ void store_row_codes(uint8_t *row, bool row_ok, uint32_t off, const uint32_t *c) {
+    const __amdgpu_buffer_rsrc_t r = row_rsrc(row, row_ok);
+    if constexpr (CPT == 8) __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{c[0], c[1]}, r, off, 0, 2);
+    else __builtin_amdgcn_raw_buffer_store_b32(c[0], r, off, 0, 2);
+}
+
+__device__ __forceinline__ void store_row_byte(uint8_t *row, uint32_t off, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, row_rsrc(row, true), off, 0, 0);
+}
+
 template <int CPT>
 __device__ __forceinline__ Vec<CPT> zero_vec() {
     Vec<CPT> v;
@@ -99,12 +126,6 @@ template <int CPT>
 __device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t *c) {
     if constexpr (CPT == 8) __builtin_nontemporal_store(u32x2_t{c[0], c[1]}, reinterpret_cast<u32x2_t *>(p));
     else __builtin_nontemporal_store(c[0], reinterpret_cast<uint32_t *>(p));
-}
-
-template <int CPT>
-__device__ __forceinline__ void store_bf16(uint16_t *p, const uint32_t *w) {
-    if constexpr (CPT == 8) __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4_t *>(p));
-    else __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, reinterpret_cast<u32x2_t *>(p));
 }
 
 // ------------------------------------------------------------------ tiles
@@ -434,7 +455,7 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
                 }
             }
         }
-        if (a.h != nullptr && i < nrow && active) store_bf16<CPT>(a.h + (rbase + i) * a.ld_h + co, h[i]);
+        if (a.h != nullptr) store_row_bf16<CPT>(a.h + (rbase + i) * a.ld_h, i < nrow, active ? (uint32_t)co * 2u : kOffOut, h[i]);
         uint32_t m = 0u;
 #pragma unroll
         for (int k = 0; k < CPT / 2; k++) {
@@ -449,11 +470,10 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
                 uint32_t c[CPT / 4];
 #pragma unroll
                 for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_same(h[i][2 * q], h[i][2 * q + 1], E);
-                if (active) {
-                    const int64_t r = rbase + i;
-                    store_codes<CPT>(a.row.codes + r * a.row.ld_codes + co, c);
-                    if ((lane & (32 / CPT - 1)) == 0) a.row.scales[r * a.row.ld_scales + co / 32] = (uint8_t)E;
-                }
+                const int64_t r = rbase + i;
+                store_row_codes<CPT>(a.row.codes + r * a.row.ld_codes, true, active ? (uint32_t)co : kOffOut, c);
+                store_row_byte(a.row.scales + r * a.row.ld_scales,
+                               active && (lane & (32 / CPT - 1)) == 0 ? (uint32_t)co / 32u : kOffOut, E);
             }
         }
     }
@@ -470,7 +490,7 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
                 uint32_t c[CPT / 4];
 #pragma unroll
                 for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_cols(h[i][2 * q], h[i][2 * q + 1], cs.s + 4 * q, cs.nan[q]);
-                store_codes<CPT>(colc + i * a.col.ld_codes + co, c);
+                store_row_codes<CPT>(colc + i * a.col.ld_codes, true, (uint32_t)co, c);
             }
         }
         if (wave == 0) store_scale_bytes<CPT>(a.col.scales + T.srow * a.col.ld_scales + co, cs.E);
@@ -713,6 +733,11 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
     constexpr int PF = 4;
     Vec<CPT> db[PF], gb[PF], ub[PF];
     const uint32_t doff = active ? (uint32_t)co * 2u : kOffOut, goff = active ? (uint32_t)gco * 2u : kOffOut;
+    // output offsets: the codes of dgate / dup (bytes), and their rowwise scale bytes (one lane per 32 columns)
+    const uint32_t coff_g = active ? (uint32_t)gco : kOffOut, coff_u = active ? (uint32_t)(gco + uoff) : kOffOut;
+    const bool scale_lane = active && (lane & (32 / CPT - 1)) == 0;
+    const uint32_t soff_g = scale_lane ? (uint32_t)gco / 32u : kOffOut;
+    const uint32_t soff_u = scale_lane ? (uint32_t)(gco + uoff) / 32u : kOffOut;
     const uint16_t *grad0 = a.grad + rbase * a.ld_grad, *gate0 = a.gate + rbase * a.ld_gate;
     const uint16_t *up0 = gated<ACT>() ? a.up + rbase * a.ld_up : nullptr;
     auto load3 = [&](int j, int i) {   // row i of the wave into prefetch slot j
@@ -817,9 +842,9 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
                 }
             }
         }
-        if (dense && active && i < nrow) {
-            store_bf16<CPT>(a.dgate + r * a.ld_dgate + gco, hg[i]);
-            if constexpr (gated<ACT>()) store_bf16<CPT>(a.dup + r * a.ld_dup + gco, hu[i]);
+        if (dense) {
+            store_row_bf16<CPT>(a.dgate + r * a.ld_dgate, i < nrow, goff, hg[i]);
+            if constexpr (gated<ACT>()) store_row_bf16<CPT>(a.dup + r * a.ld_dup, i < nrow, goff, hu[i]);
         }
         uint32_t mg = 0u, mu = 0u;
 #pragma unroll
@@ -844,16 +869,12 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
                     cg[q] = cvt4_same(hg[i][2 * q], hg[i][2 * q + 1], Eg);
                     cu[q] = cvt4_same(hu[i][2 * q], hu[i][2 * q + 1], Eu);
                 }
-                if (active) {
-                    uint8_t *rowc = a.row.codes + r * a.row.ld_codes;
-                    store_codes<CPT>(rowc + gco, cg);
-                    if constexpr (gated<ACT>()) store_codes<CPT>(rowc + gco + uoff, cu);
-                    if ((lane & (32 / CPT - 1)) == 0) {
-                        uint8_t *rs = a.row.scales + r * a.row.ld_scales;
-                        rs[gco / 32] = (uint8_t)Eg;
-                        if constexpr (gated<ACT>()) rs[(gco + uoff) / 32] = (uint8_t)Eu;
-                    }
-                }
+                uint8_t *rowc = a.row.codes + r * a.row.ld_codes;
+                store_row_codes<CPT>(rowc, true, coff_g, cg);
+                if constexpr (gated<ACT>()) store_row_codes<CPT>(rowc, true, coff_u, cu);
+                uint8_t *rs = a.row.scales + r * a.row.ld_scales;
+                store_row_byte(rs, soff_g, Eg);
+                if constexpr (gated<ACT>()) store_row_byte(rs, soff_u, Eu);
             }
         }
     }
@@ -895,8 +916,8 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
                         cg[q] = cvt4_cols(hg[i][2 * q], hg[i][2 * q + 1], sg.s + 4 * q, sg.nan[q]);
                         cu[q] = cvt4_cols(hu[i][2 * q], hu[i][2 * q + 1], su.s + 4 * q, su.nan[q]);
                     }
-                    store_codes<CPT>(colc + i * a.col.ld_codes + gco, cg);
-                    if constexpr (gated<ACT>()) store_codes<CPT>(colc + i * a.col.ld_codes + gco + uoff, cu);
+                    store_row_codes<CPT>(colc + i * a.col.ld_codes, true, coff_g, cg);
+                    if constexpr (gated<ACT>()) store_row_codes<CPT>(colc + i * a.col.ld_codes, true, coff_u, cu);
                 }
             }
             if (wave == 0) {
