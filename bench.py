@@ -266,7 +266,7 @@ def moe_section(m, torch, W, reps=5):
             fn()
             us, = timed_alt(torch, [fn], reps)
             tf = flops[k] / us / 1e6
-            peak = FP8_PEAK_TFLOPS if dt == "fp8" else BF16_PEAK_TFLOPS
+            peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP8_PEAK_TFLOPS
             per[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": dt, "frac_peak": round(tf / peak, 4)}
             tot_fl += flops[k]
             tot_us += us
@@ -363,13 +363,19 @@ def supplementary_gemm(m, torch, reps=5):
     res = {"shape": f"{G} groups x {rows} rows, N = K = {N}, NT", "configuration": "supplementary, not a workload config"}
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for dt in ("fp8", "bf16"):
+    for dt in ("fp8", "fp8_kblock", "bf16"):
         if dt == "fp8":
             A = torch.randint(0, 0x70, (R, K), dtype=torch.uint8, device=dev, generator=g)
             B = torch.randint(0, 0x70, (G, N, K), dtype=torch.uint8, device=dev, generator=g)
             As = torch.full((R, K // 32), 120, dtype=torch.uint8, device=dev)
             Bs = torch.full((G, N, K // 32), 120, dtype=torch.uint8, device=dev)
             fn = lambda: m.grouped_gemm(m.GEMM_NT, ro, A, B, out, As, Bs)
+        elif dt == "fp8_kblock":
+            # the same codes K-blocked by 64 (the layout the quantizers can
+            # write directly): every stage load covers whole cache lines
+            Ak, Bk = m.KBlocked.from_rowmajor(A), m.KBlocked.from_rowmajor(B)
+            A = B = None
+            fn = lambda: m.grouped_gemm(m.GEMM_NT, ro, Ak, Bk, out, As, Bs)
         else:
             A = torch.randn((R, K), device=dev, generator=g).to(torch.bfloat16)
             B = torch.randn((G, N, K), device=dev, generator=g).to(torch.bfloat16)
@@ -385,11 +391,13 @@ def supplementary_gemm(m, torch, reps=5):
             ts.append(e0.elapsed_time(e1) * 1e3)
         us = sorted(ts)[len(ts) // 2]
         tf = 2.0 * R * N * K / us / 1e6
-        peak = FP8_PEAK_TFLOPS if dt == "fp8" else BF16_PEAK_TFLOPS
+        peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP8_PEAK_TFLOPS
         res[dt] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "frac_peak": round(tf / peak, 4)}
-        del A, B
-        if dt == "fp8":
-            del As, Bs
+        fn = None
+        if dt == "fp8_kblock":
+            del Ak, Bk, As, Bs
+        elif dt == "bf16":
+            del A, B
     del out
     torch.cuda.empty_cache()
     return res

@@ -121,12 +121,19 @@ typedef struct {
 } mxq_groups;
 
 /* One direction of an MXFP8 output: codes (rows x cols, row pitch ld_codes
- * bytes) and scales (row pitch ld_scales bytes). */
+ * bytes) and scales (row pitch ld_scales bytes).  Rowwise codes may instead
+ * be K-blocked by 64 for the grouped GEMM (kblock_plane = P > 0: code (r, c)
+ * at byte (c / 64) * P + r * 64 + c % 64; ld_codes must be 64, cols a
+ * multiple of 64, P a multiple of 16 and at least 64 * rows, and the codes
+ * must span less than 2^31 bytes, else MXQ_ERR_SHAPE / _ALIGN / _OVERFLOW);
+ * colwise codes are always row-major (MXQ_ERR_UNSUPPORTED otherwise), and the
+ * fused FC1 epilogue writes row-major codes only. */
 typedef struct {
     uint8_t *codes;
     int64_t ld_codes;
     uint8_t *scales;
     int64_t ld_scales;
+    int64_t kblock_plane;   /* 0: row-major codes; P > 0: K-blocked (rowwise only) */
 } mxq_mx_out;
 
 /* ------------------------------------------------------------ entry points */
@@ -326,6 +333,19 @@ typedef enum { MXQ_DTYPE_BF16 = 0, MXQ_DTYPE_MXFP8_E4M3 = 1, MXQ_DTYPE_F32 = 2 }
  * activation recomputed in bf16 for the two wgrad GEMMs) and needs no
  * block_off.
  * Every product is accumulated in fp32 and rounded once to the output dtype.
+ *
+ * K-blocked MXFP8 codes (an operand read along the contraction: A of NT and
+ * NN, B of NT).  With kblock_plane = P > 0 the codes are stored in planes of
+ * 64 contraction bytes: code (r, k) of row r lies at byte
+ * (k / 64) * P + r * 64 + k % 64 of data (for B of NT, r = g * gstride / 64
+ * + n, i.e. gstride is the byte distance of group g's rows within a plane).
+ * ld must then be 64, K a multiple of 64, P a multiple of 16 and at least
+ * the rows' extent within a plane.  The values and results are those of the
+ * row-major layout; what changes is that a 64-byte stage of 16 rows is one
+ * contiguous kilobyte, so every load of the GEMM covers whole cache lines.
+ * The fused activation kernels and the quantizer write their rowwise codes in
+ * this layout when their mxq_mx_out asks for it (mxq_mx_out.kblock_plane).
+ * Scales keep their row-major layout.
  */
 typedef enum { MXQ_GEMM_NT = 0, MXQ_GEMM_NN = 1, MXQ_GEMM_TN = 2 } mxq_gemm_mode;
 
@@ -337,6 +357,8 @@ typedef struct {
     const uint8_t *scales;  /* E8M0 bytes (MXFP8 only) */
     int64_t ld_scales;      /* scale row pitch, bytes */
     int64_t scale_gstride;  /* scale group stride, bytes (B of NT/NN only) */
+    int64_t kblock_plane;   /* 0: row-major codes; P > 0: K-blocked MXFP8 codes
+                               with plane stride P bytes (see above) */
 } mxq_operand;
 
 typedef struct {

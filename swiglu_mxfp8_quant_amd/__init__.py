@@ -63,13 +63,15 @@ class mxq_groups(ctypes.Structure):
 
 class mxq_mx_out(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
-                ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64)]
+                ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64),
+                ("kblock_plane", ctypes.c_int64)]
 
 
 class mxq_operand(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p), ("ld", ctypes.c_int64),
                 ("gstride", ctypes.c_int64), ("scales", ctypes.c_void_p),
-                ("ld_scales", ctypes.c_int64), ("scale_gstride", ctypes.c_int64)]
+                ("ld_scales", ctypes.c_int64), ("scale_gstride", ctypes.c_int64),
+                ("kblock_plane", ctypes.c_int64)]
 
 
 class mxq_gemm_args(ctypes.Structure):
@@ -183,7 +185,9 @@ def make_groups(row_off=None, block_off=None):
 def make_mx_out(codes, scales):
     if codes is None:
         return None
-    return mxq_mx_out(codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales))
+    if isinstance(codes, KBlocked):
+        return mxq_mx_out(codes.data.data_ptr(), 64, scales.data_ptr(), _ld(scales), codes.plane)
+    return mxq_mx_out(codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales), 0)
 
 
 def _byref(x):
@@ -285,9 +289,12 @@ def splits_to_offsets(splits, stream=None):
     return row_off, block_off, err
 
 
-def _alloc_mx(M, K, dirs, n_col_blocks, device):
+def _alloc_mx(M, K, dirs, n_col_blocks, device, kblock=False):
     import torch
-    rc = torch.empty((M, K) if dirs & ROWWISE else (0, 0), dtype=torch.uint8, device=device)
+    if kblock and dirs & ROWWISE:
+        rc = KBlocked.empty((M, K), device)
+    else:
+        rc = torch.empty((M, K) if dirs & ROWWISE else (0, 0), dtype=torch.uint8, device=device)
     rs = torch.empty((M, K // 32) if dirs & ROWWISE else (0, 0), dtype=torch.uint8, device=device)
     cc = torch.empty((M, K) if dirs & COLWISE else (0, 0), dtype=torch.uint8, device=device)
     cs = torch.empty((n_col_blocks, K) if dirs & COLWISE else (0, 0), dtype=torch.uint8, device=device)
@@ -301,17 +308,18 @@ def _outs(rc, cc, rs, cs, dirs):
 
 def swiglu_quantize_fwd(gate, up, scale=None, rowwise=True, colwise=False, row_off=None,
                         block_off=None, n_col_blocks=None, clamped=False, limit=7.0, interleave=0,
-                        stream=None):
+                        kblock=False, stream=None):
     """Returns (codes_row, codes_col, scales_row, scales_col); a disabled
     direction comes back zero-sized.  With groups, n_col_blocks must be the
     number of colwise scale rows (sum of ceil(split/32)).  With interleave = B,
     gate and up are (M, K) views p[:, :K] and p[:, B:B + K] of a packed (M, 2K)
-    buffer p holding gate and up interleaved in blocks of B columns."""
+    buffer p holding gate and up interleaved in blocks of B columns.  With
+    kblock the rowwise codes come back K-blocked (a KBlocked)."""
     M, K = gate.shape
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if n_col_blocks is None:
         n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
-    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, gate.device)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, gate.device, kblock)
     ro, co = _outs(rc, cc, rs, cs, dirs)
     act = make_act(ACT_CLAMPED_SWIGLU if clamped else ACT_SWIGLU, limit, interleave)
     check(mxq_swiglu_quantize_fwd(act, gate, up, scale, make_groups(row_off, block_off), dirs, ro, co, stream))
@@ -352,12 +360,13 @@ def srelu_quantize_fwd(x, scale=None, rowwise=True, colwise=False, row_off=None,
     return rc, cc, rs, cs
 
 
-def quantize(x, rowwise=True, colwise=False, row_off=None, block_off=None, n_col_blocks=None, stream=None):
+def quantize(x, rowwise=True, colwise=False, row_off=None, block_off=None, n_col_blocks=None, kblock=False,
+             stream=None):
     M, K = x.shape
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if n_col_blocks is None:
         n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
-    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device, kblock)
     ro, co = _outs(rc, cc, rs, cs, dirs)
     check(mxq_quantize(x, make_groups(row_off, block_off), dirs, ro, co, stream))
     return rc, cc, rs, cs
@@ -376,7 +385,7 @@ def quantize_into(x, codes_row, codes_col, scales_row, scales_col, noop_flag=Non
 
 def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False, row_off=None,
                         block_off=None, n_col_blocks=None, clamped=False, limit=7.0, dense=True,
-                        want_dscale=True, interleave=0, stream=None):
+                        want_dscale=True, interleave=0, kblock=False, stream=None):
     """Returns (codes_row, codes_col, scales_row, scales_col, dgate_dup, dscale)
     where the codes cover the (M, 2K) [dgate | dup] matrix and dgate_dup is the
     packed (M, 2K) bf16 gradient (None when dense=False); with interleave = B
@@ -386,7 +395,7 @@ def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False,
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if n_col_blocks is None:
         n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
-    rc, cc, rs, cs = _alloc_mx(M, 2 * K, dirs, n_col_blocks, gate.device)
+    rc, cc, rs, cs = _alloc_mx(M, 2 * K, dirs, n_col_blocks, gate.device, kblock)
     ro, co = _outs(rc, cc, rs, cs, dirs)
     dd = torch.empty((M, 2 * K), dtype=torch.bfloat16, device=gate.device) if dense else None
     ds = torch.empty(M, dtype=torch.float32, device=gate.device) if want_dscale else None
@@ -422,17 +431,70 @@ def srelu_quantize_bwd(grad, x, scale=None, rowwise=True, colwise=False, row_off
     return rc, cc, rs, cs, dx, ds
 
 
+class KBlocked:
+    """MXFP8 codes K-blocked by 64 (the layout of mxq_operand.kblock_plane):
+    code (r, k) of a (rows, K) matrix sits at [k // 64, r, k % 64] of `data`,
+    a (K/64, rows, 64) uint8 tensor whose plane stride is data.stride(0); a
+    (G, N, K) stack of per-group matrices is blocked over its G * N rows.
+    `shape` is the logical (row-major) shape."""
+
+    def __init__(self, data, shape):
+        if shape[-1] % 64 != 0:
+            raise ValueError("K-blocked codes need a multiple of 64 columns")
+        self.data = data
+        self.shape = tuple(shape)
+
+    @property
+    def plane(self):
+        """Bytes between planes (at least 64, so that an empty matrix still
+        reads as K-blocked)."""
+        return max(self.data.stride(0), 64)
+
+    @classmethod
+    def from_rowmajor(cls, t):
+        """Blocked copy of row-major codes (R, K) or (G, N, K): a layout
+        change done by torch, for tests and for codes that were not written
+        blocked by the kernels."""
+        K = t.shape[-1]
+        rows = t.numel() // K
+        d = t.reshape(rows, K // 64, 64).transpose(0, 1).contiguous()
+        return cls(d, t.shape)
+
+    def to_rowmajor(self):
+        K = self.shape[-1]
+        return self.data.transpose(0, 1).reshape(self.shape).contiguous()
+
+    @classmethod
+    def empty(cls, shape, device):
+        K = shape[-1]
+        rows = 1
+        for d in shape[:-1]:
+            rows *= d
+        return cls(_torch().empty((K // 64, rows, 64), dtype=_torch().uint8, device=device), shape)
+
+
+def rowmajor(codes):
+    """Row-major view of codes that may be K-blocked (a layout change by
+    torch, for inspection)."""
+    return codes.to_rowmajor() if isinstance(codes, KBlocked) else codes
+
+
 def _operand(data, scales=None, group_dim=False):
-    """mxq_operand from a data tensor (2-D, or 3-D stacked per group) and its
-    E8M0 scale tensor (same rank)."""
-    f8 = data.dtype == _torch().uint8
-    if group_dim:
-        ld = data.stride(1)
-        gs = data.stride(0)
+    """mxq_operand from a data tensor (2-D, or 3-D stacked per group), or
+    KBlocked codes, and its E8M0 scale tensor (same rank as the logical
+    shape)."""
+    if isinstance(data, KBlocked):
+        gs = data.shape[1] * 64 if group_dim else 0
+        op = mxq_operand(DTYPE_MXFP8, data.data.data_ptr(), 64, gs, None, 0, 0, data.plane)
     else:
-        ld = data.stride(0)
-        gs = 0
-    op = mxq_operand(DTYPE_MXFP8 if f8 else DTYPE_BF16, data.data_ptr(), ld, gs, None, 0, 0)
+        f8 = data.dtype == _torch().uint8
+        if group_dim:
+            ld = data.stride(1)
+            gs = data.stride(0)
+        else:
+            ld = data.stride(0)
+            gs = 0
+        op = mxq_operand(DTYPE_MXFP8 if f8 else DTYPE_BF16, data.data_ptr(), ld, gs, None, 0, 0, 0)
     if scales is not None:
         op.scales = scales.data_ptr()
         op.ld_scales = scales.stride(1) if group_dim else scales.stride(0)

@@ -101,12 +101,24 @@ __device__ __forceinline__ void store_row_bf16(uint16_t *row, bool row_ok, uint3
     else __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w[0], w[1]}, r, off, 0, 2);
 }
 
-// CPT codes (CPT / 4 words) at byte offset `off`, nontemporal
-template <int CPT>
+// CPT codes (CPT / 4 words) at byte offset `off`, nontemporal (NT), or
+// through the cache: a K-blocked row's codes are 64-byte pieces, half lines
+// whose other halves (the next row of the plane) the same wave writes next,
+// which the L2 merges only if the stores go through it
+template <int CPT, bool NT = true>
 __device__ __forceinline__ void store_row_codes(uint8_t *row, bool row_ok, uint32_t off, const uint32_t *c) {
     const __amdgpu_buffer_rsrc_t r = row_rsrc(row, row_ok);
-    if constexpr (CPT == 8) __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{c[0], c[1]}, r, off, 0, 2);
-    else __builtin_amdgcn_raw_buffer_store_b32(c[0], r, off, 0, 2);
+    constexpr int aux = NT ? 2 : 0;
+    if constexpr (CPT == 8) __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{c[0], c[1]}, r, off, 0, aux);
+    else __builtin_amdgcn_raw_buffer_store_b32(c[0], r, off, 0, aux);
+}
+
+// Byte offset of column c's code from its row's start: c itself, or, with
+// the codes K-blocked by 64 (row r's bytes k at (k / 64) plane + 64 r + k % 64,
+// so the row's start is 64 r), (c / 64) plane + c % 64.  A lane's CPT
+// columns never straddle a 64-column plane.
+__device__ __forceinline__ uint32_t code_off(int c, int64_t plane) {
+    return plane ? (uint32_t)((int64_t)(c >> 6) * plane + (c & 63)) : (uint32_t)c;
 }
 
 __device__ __forceinline__ void store_row_byte(uint8_t *row, uint32_t off, uint32_t v) {
@@ -471,7 +483,9 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
 #pragma unroll
                 for (int q = 0; q < CPT / 4; q++) c[q] = cvt4_same(h[i][2 * q], h[i][2 * q + 1], E);
                 const int64_t r = rbase + i;
-                store_row_codes<CPT>(a.row.codes + r * a.row.ld_codes, true, active ? (uint32_t)co : kOffOut, c);
+                const uint32_t off = active ? code_off(co, a.row.plane) : kOffOut;
+                if (a.row.plane) store_row_codes<CPT, false>(a.row.codes + r * a.row.ld_codes, true, off, c);
+                else store_row_codes<CPT>(a.row.codes + r * a.row.ld_codes, true, off, c);
                 store_row_byte(a.row.scales + r * a.row.ld_scales,
                                active && (lane & (32 / CPT - 1)) == 0 ? (uint32_t)co / 32u : kOffOut, E);
             }
@@ -735,6 +749,8 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
     const uint32_t doff = active ? (uint32_t)co * 2u : kOffOut, goff = active ? (uint32_t)gco * 2u : kOffOut;
     // output offsets: the codes of dgate / dup (bytes), and their rowwise scale bytes (one lane per 32 columns)
     const uint32_t coff_g = active ? (uint32_t)gco : kOffOut, coff_u = active ? (uint32_t)(gco + uoff) : kOffOut;
+    const uint32_t rcoff_g = active ? code_off(gco, a.row.plane) : kOffOut;          // (rowwise codes, maybe K-blocked)
+    const uint32_t rcoff_u = active ? code_off(gco + uoff, a.row.plane) : kOffOut;
     const bool scale_lane = active && (lane & (32 / CPT - 1)) == 0;
     const uint32_t soff_g = scale_lane ? (uint32_t)gco / 32u : kOffOut;
     const uint32_t soff_u = scale_lane ? (uint32_t)(gco + uoff) / 32u : kOffOut;
@@ -870,8 +886,13 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
                     cu[q] = cvt4_same(hu[i][2 * q], hu[i][2 * q + 1], Eu);
                 }
                 uint8_t *rowc = a.row.codes + r * a.row.ld_codes;
-                store_row_codes<CPT>(rowc, true, coff_g, cg);
-                if constexpr (gated<ACT>()) store_row_codes<CPT>(rowc, true, coff_u, cu);
+                if (a.row.plane) {
+                    store_row_codes<CPT, false>(rowc, true, rcoff_g, cg);
+                    if constexpr (gated<ACT>()) store_row_codes<CPT, false>(rowc, true, rcoff_u, cu);
+                } else {
+                    store_row_codes<CPT>(rowc, true, rcoff_g, cg);
+                    if constexpr (gated<ACT>()) store_row_codes<CPT>(rowc, true, rcoff_u, cu);
+                }
                 uint8_t *rs = a.row.scales + r * a.row.ld_scales;
                 store_row_byte(rs, soff_g, Eg);
                 if constexpr (gated<ACT>()) store_row_byte(rs, soff_u, Eu);

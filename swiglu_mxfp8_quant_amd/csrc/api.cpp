@@ -63,6 +63,17 @@ Range range2d(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t esi
     return r;
 }
 
+// Footprint of K-blocked codes: `planes` planes `plane` bytes apart, each
+// holding `extent` bytes from its start.
+Range range_kblock(const void *p, int64_t planes, int64_t plane, int64_t extent, const char *name) {
+    Range r;
+    r.name = name;
+    if (p == nullptr || planes <= 0 || extent <= 0) return r;
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + (uintptr_t)((planes - 1) * plane + extent);
+    return r;
+}
+
 bool overlap(const Range &a, const Range &b) {
     if (!(a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi)) return false;
     if (a.pitch != 0 && a.pitch == b.pitch) {
@@ -97,7 +108,22 @@ mxq_status check_mx_out(const mxq_mx_out *o, bool rowwise, int64_t rows, int64_t
                         const char *name, std::vector<Range> &outs) {
     if (o == nullptr || o->codes == nullptr || o->scales == nullptr)
         return fail(MXQ_ERR_NULL, "%s output (codes and scales) is required for this direction", name);
-    if (o->ld_codes < cols) return fail(MXQ_ERR_SHAPE, "%s ld_codes %lld < %lld", name, (long long)o->ld_codes, (long long)cols);
+    const int64_t plane = o->kblock_plane;
+    if (plane != 0) {
+        // K-blocked rowwise codes: (k / 64) plane + 64 r + k % 64, stored
+        // with 32-bit offsets from each row's start
+        if (!rowwise) return fail(MXQ_ERR_UNSUPPORTED, "%s: only rowwise codes can be K-blocked", name);
+        if (plane < 0) return fail(MXQ_ERR_SHAPE, "%s kblock_plane %lld < 0", name, (long long)plane);
+        if (o->ld_codes != 64) return fail(MXQ_ERR_SHAPE, "%s: K-blocked codes have ld_codes = 64", name);
+        if (cols % 64 != 0) return fail(MXQ_ERR_SHAPE, "%s: K-blocked codes need a multiple of 64 columns", name);
+        if (plane % 16 != 0 || !aligned(o->codes, 16))
+            return fail(MXQ_ERR_ALIGN, "%s codes pointer and kblock_plane must be multiples of 16 bytes", name);
+        if (plane < rows * 64) return fail(MXQ_ERR_SHAPE, "%s kblock_plane %lld < 64 x %lld rows", name, (long long)plane, (long long)rows);
+        if (cols > 0 && (plane > (int64_t(1) << 31) || (cols / 64 - 1) * plane + 64 > int64_t(0x7FFFFFF0)))
+            return fail(MXQ_ERR_OVERFLOW, "%s: K-blocked codes must span less than 2^31 bytes", name);
+    } else if (o->ld_codes < cols) {
+        return fail(MXQ_ERR_SHAPE, "%s ld_codes %lld < %lld", name, (long long)o->ld_codes, (long long)cols);
+    }
     const int64_t scols = rowwise ? cols / 32 : cols;
     if (o->ld_scales < scols)
         return fail(MXQ_ERR_SHAPE, "%s ld_scales %lld < %lld", name, (long long)o->ld_scales, (long long)scols);
@@ -107,7 +133,8 @@ mxq_status check_mx_out(const mxq_mx_out *o, bool rowwise, int64_t rows, int64_t
         return fail(MXQ_ERR_ALIGN, "%s colwise scales pointer and ld_scales must be multiples of 8 bytes", name);
     if (!extent_ok(rows, o->ld_codes, 1) || !extent_ok(srows, o->ld_scales, 1))
         return fail(MXQ_ERR_OVERFLOW, "%s output extent too large", name);
-    outs.push_back(range2d(o->codes, rows, cols, o->ld_codes, 1, rowwise ? "row codes" : "col codes"));
+    if (plane != 0) outs.push_back(range_kblock(o->codes, cols / 64, plane, rows * 64, "row codes"));
+    else outs.push_back(range2d(o->codes, rows, cols, o->ld_codes, 1, rowwise ? "row codes" : "col codes"));
     outs.push_back(range2d(o->scales, srows, scols, o->ld_scales, 1, rowwise ? "row scales" : "col scales"));
     return MXQ_OK;
 }
@@ -232,10 +259,10 @@ mxq_status prepare_fwd(mxq::FwdArgs &a, int act_kind, float limit, int il, int64
     a.row_scale = act_kind == mxq::ACT_IDENTITY ? nullptr : row_scale;
     a.groups = go.g;
     a.dirs = dirs;
-    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales}
-                       : mxq::MxOut{nullptr, 0, nullptr, 0};
-    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales}
-                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales, row_out->kblock_plane}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0, 0};
+    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales, 0}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0, 0};
     a.h = h;
     a.ld_h = ld_h;
     return MXQ_OK;
@@ -295,10 +322,13 @@ mxq_status check_gemm_alias(const mxq_gemm_args &a) {
         out = range_groups(a.out, a.G, a.out_gstride, a.M, a.N, a.ld_out, osz, "out");
     } else {
         const int64_t kb = (a.K + 31) / 32;
-        ins.push_back(range2d(a.A.data, a.M, a.K, a.A.ld, esz, "A"));
+        if (a.A.kblock_plane > 0) ins.push_back(range_kblock(a.A.data, a.K / 64, a.A.kblock_plane, a.M * 64, "A"));
+        else ins.push_back(range2d(a.A.data, a.M, a.K, a.A.ld, esz, "A"));
         if (f8) ins.push_back(range2d(a.A.scales, a.M, kb, a.A.ld_scales, 1, "A scales"));
         if (a.mode == MXQ_GEMM_NT) {
-            ins.push_back(range_groups(a.B.data, a.G, a.B.gstride, a.N, a.K, a.B.ld, esz, "B"));
+            if (a.B.kblock_plane > 0)
+                ins.push_back(range_kblock(a.B.data, a.K / 64, a.B.kblock_plane, (a.G - 1) * a.B.gstride + a.N * 64, "B"));
+            else ins.push_back(range_groups(a.B.data, a.G, a.B.gstride, a.N, a.K, a.B.ld, esz, "B"));
             if (f8) ins.push_back(range_groups(a.B.scales, a.G, a.B.scale_gstride, a.N, kb, a.B.ld_scales, 1, "B scales"));
         } else {
             ins.push_back(range_groups(a.B.data, a.G, a.B.gstride, a.K, a.N, a.B.ld, esz, "B"));
@@ -404,7 +434,9 @@ mxq_status mxq_quantize_noop(int64_t M, int64_t K, const uint16_t *x, int64_t ld
         // the flag is an input: no output may overlap it
         std::vector<Range> outs;
         if (dirs & 1) {
-            outs.push_back(range2d(row_out->codes, M, K, row_out->ld_codes, 1, "row codes"));
+            if (row_out->kblock_plane > 0)
+                outs.push_back(range_kblock(row_out->codes, K / 64, row_out->kblock_plane, M * 64, "row codes"));
+            else outs.push_back(range2d(row_out->codes, M, K, row_out->ld_codes, 1, "row codes"));
             outs.push_back(range2d(row_out->scales, M, K / 32, row_out->ld_scales, 1, "row scales"));
         }
         if (dirs & 2) {
@@ -530,10 +562,10 @@ mxq_status mxq_swiglu_quantize_bwd(const mxq_act *act, int64_t M, int64_t K, con
     a.dup = dup; a.ld_dup = ld_dup;
     a.dscale = dscale;
     a.dirs = dirs;
-    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales}
-                       : mxq::MxOut{nullptr, 0, nullptr, 0};
-    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales}
-                       : mxq::MxOut{nullptr, 0, nullptr, 0};
+    a.row = (dirs & 1) ? mxq::MxOut{row_out->codes, row_out->ld_codes, row_out->scales, row_out->ld_scales, row_out->kblock_plane}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0, 0};
+    a.col = (dirs & 2) ? mxq::MxOut{col_out->codes, col_out->ld_codes, col_out->scales, col_out->ld_scales, 0}
+                       : mxq::MxOut{nullptr, 0, nullptr, 0, 0};
     a.partials = static_cast<float *>(ws);
     return hip_status(mxq::launch_act_quant_bwd(a, (hipStream_t)stream), "mxq_swiglu_quantize_bwd launch");
 }
@@ -620,6 +652,8 @@ mxq_status mxq_grouped_gemm_swiglu(const mxq_gemm_args *args, const mxq_act *act
     std::vector<Range> ins, outs;
     mxq_status s;
     if (dirs & 1) {
+        if (row_out != nullptr && row_out->kblock_plane != 0)
+            return fail(MXQ_ERR_UNSUPPORTED, "the fused FC1 epilogue writes row-major rowwise codes (kblock_plane 0)");
         if ((s = check_mx_out(row_out, true, M, KA, M, "rowwise", outs)) != MXQ_OK) return s;
     } else if (row_out != nullptr && row_out->codes != nullptr) {
         return fail(MXQ_ERR_SHAPE, "row_out given but dirs has no ROWWISE");

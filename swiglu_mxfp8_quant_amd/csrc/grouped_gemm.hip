@@ -865,7 +865,9 @@ __global__ void __launch_bounds__(NTHR) gemm_kernel(GemmArgs a, int ntn, int ntm
     // the load tile's operand and column-scale origins advanced to stage `ls`,
     // carried from stage to stage (per-stage strides are per launch)
     const uint8_t *sbx = nullptr, *sby = nullptr, *sbxs = nullptr, *sbys = nullptr;
-    const int64_t dsx = XKS ? (int64_t)KSR * ldb : BK, dsy = YKS ? (int64_t)KSR * lda : BK;
+    // (K-blocked codes: the next stage is the next 64-byte plane)
+    const int64_t dsx = XKS ? (int64_t)KSR * ldb : (a.B.plane ? a.B.plane : BK);
+    const int64_t dsy = YKS ? (int64_t)KSR * lda : (a.A.plane ? a.A.plane : BK);
     const int64_t dsxs = 2 * (int64_t)ldsb, dsys = 2 * (int64_t)ldsa;
 
     // Load instruction p of stage s of tile T into stage buffer st (live
@@ -1552,6 +1554,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+// bound on a K-blocked operand's planes (bytes), far below 2^62
+constexpr int64_t kMaxPlaneExtent = int64_t(1) << 60;
+
 int gemm_prepare(const mxq_gemm_args &in, GemmArgs &g, std::string &err) {
     g = GemmArgs{};
     g.mode = in.mode;
@@ -1562,8 +1567,10 @@ int gemm_prepare(const mxq_gemm_args &in, GemmArgs &g, std::string &err) {
     g.N = in.N;
     g.K = in.K;
     g.rows = in.rows;
-    g.A = GemmOperand{in.A.dtype, in.A.data, in.A.ld, in.A.gstride, in.A.scales, in.A.ld_scales, in.A.scale_gstride};
-    g.B = GemmOperand{in.B.dtype, in.B.data, in.B.ld, in.B.gstride, in.B.scales, in.B.ld_scales, in.B.scale_gstride};
+    g.A = GemmOperand{in.A.dtype, in.A.data, in.A.ld, in.A.gstride, in.A.scales, in.A.ld_scales, in.A.scale_gstride,
+                      in.A.kblock_plane};
+    g.B = GemmOperand{in.B.dtype, in.B.data, in.B.ld, in.B.gstride, in.B.scales, in.B.ld_scales, in.B.scale_gstride,
+                      in.B.kblock_plane};
     g.out_dtype = in.out_dtype;
     g.out = in.out;
     g.ld_out = in.ld_out;
@@ -1603,13 +1610,39 @@ int gemm_prepare(const mxq_gemm_args &in, GemmArgs &g, std::string &err) {
         err = "out pointer and pitches must be 16-byte aligned";
         return MXQ_ERR_ALIGN;
     }
+    // K-blocked codes: MXFP8 operands read along the contraction only
+    const bool kba = in.A.kblock_plane != 0, kbb = in.B.kblock_plane != 0;
+    if (kba || kbb) {
+        if (in.A.kblock_plane < 0 || in.B.kblock_plane < 0) { err = "kblock_plane must be >= 0"; return MXQ_ERR_SHAPE; }
+        if (!f8) { err = "K-blocked operands are MXFP8 codes"; return MXQ_ERR_UNSUPPORTED; }
+        if (in.mode == MXQ_GEMM_TN || (in.mode == MXQ_GEMM_NN && kbb)) {
+            err = "only operands contiguous along the contraction (A of NT / NN, B of NT) can be K-blocked";
+            return MXQ_ERR_UNSUPPORTED;
+        }
+        if (in.K % 64 != 0) { err = "K-blocked operands need K a multiple of 64"; return MXQ_ERR_SHAPE; }
+        if ((kba && in.A.ld != 64) || (kbb && in.B.ld != 64)) { err = "a K-blocked operand has ld = 64"; return MXQ_ERR_SHAPE; }
+        if ((kba && in.A.kblock_plane % 16 != 0) || (kbb && in.B.kblock_plane % 16 != 0)) {
+            err = "kblock_plane must be a multiple of 16 bytes";
+            return MXQ_ERR_ALIGN;
+        }
+        if (kba && in.A.kblock_plane < in.M * 64) { err = "A kblock_plane is smaller than its M rows of 64 bytes"; return MXQ_ERR_SHAPE; }
+        if (kbb && (in.B.kblock_plane < (in.G - 1) * in.B.gstride + in.N * 64 || (in.G > 1 && in.B.gstride < in.N * 64))) {
+            err = "B kblock_plane or group stride too small for G groups of N rows of 64 bytes";
+            return MXQ_ERR_SHAPE;
+        }
+        const int64_t planes = in.K / 64;
+        if ((kba && in.A.kblock_plane > kMaxPlaneExtent / planes) || (kbb && in.B.kblock_plane > kMaxPlaneExtent / planes)) {
+            err = "K-blocked operand extent too large";
+            return MXQ_ERR_OVERFLOW;
+        }
+    }
     // operand extents
     if (in.mode == MXQ_GEMM_NT) {
-        if (in.A.ld < in.K || in.B.ld < in.K || in.ld_out < in.N) { err = "ld too small"; return MXQ_ERR_SHAPE; }
-        if (in.B.gstride < (in.N - 1) * in.B.ld + in.K && in.G > 1) { err = "B group stride too small"; return MXQ_ERR_SHAPE; }
+        if ((!kba && in.A.ld < in.K) || (!kbb && in.B.ld < in.K) || in.ld_out < in.N) { err = "ld too small"; return MXQ_ERR_SHAPE; }
+        if (!kbb && in.B.gstride < (in.N - 1) * in.B.ld + in.K && in.G > 1) { err = "B group stride too small"; return MXQ_ERR_SHAPE; }
         if (f8 && (in.A.ld_scales < (in.K + 31) / 32 || in.B.ld_scales < (in.K + 31) / 32)) { err = "ld_scales too small"; return MXQ_ERR_SHAPE; }
     } else if (in.mode == MXQ_GEMM_NN) {
-        if (in.A.ld < in.K || in.B.ld < in.N || in.ld_out < in.N) { err = "ld too small"; return MXQ_ERR_SHAPE; }
+        if ((!kba && in.A.ld < in.K) || in.B.ld < in.N || in.ld_out < in.N) { err = "ld too small"; return MXQ_ERR_SHAPE; }
         if (in.B.gstride < (in.K - 1) * in.B.ld + in.N && in.G > 1) { err = "B group stride too small"; return MXQ_ERR_SHAPE; }
         if (f8 && (in.A.ld_scales < (in.K + 31) / 32 || in.B.ld_scales < in.N)) { err = "ld_scales too small"; return MXQ_ERR_SHAPE; }
     } else {

@@ -14,6 +14,7 @@ struct MxOut {
     int64_t ld_codes;
     uint8_t *scales;
     int64_t ld_scales;
+    int64_t plane;      // rowwise only: 0 row-major; > 0 codes K-blocked by 64 (ld_codes 64), plane stride in bytes
 };
 
 // Row groups as seen by the kernels.  G == 0 means one implicit group of M rows.

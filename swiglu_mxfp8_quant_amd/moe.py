@@ -45,10 +45,18 @@ def weight_offsets(G, rows, device):
 class Layer:
     """One grouped expert layer; `forward` keeps what `backward` needs."""
 
-    def __init__(self, splits, w13, w2, clamped=False, limit=7.0, fused_fc1=False, recipe="mxfp8"):
+    def __init__(self, splits, w13, w2, clamped=False, limit=7.0, fused_fc1=False, recipe="mxfp8", kblock=True):
         if recipe not in ("mxfp8", "bf16_wgrad"):
             raise ValueError(f"unknown recipe {recipe!r}")
         self.recipe = recipe
+        # kblock: the rowwise codes that feed a GEMM along the contraction
+        # (the activation for FC2, dY and dact for the dgrads) are written
+        # K-blocked by 64 (KBlocked), so that the GEMM's stage loads cover
+        # whole cache lines; the results are the same bits either way
+        self.kblock = kblock
+        I_, H_ = w13.shape[1] // 2, w13.shape[2]
+        self.kb_a, self.kb_dy, self.kb_dq = (kblock and I_ % 64 == 0, kblock and H_ % 64 == 0,
+                                             kblock and (2 * I_) % 64 == 0)
         self.splits = splits
         self.G, self.I2, self.H = w13.shape
         self.I = self.I2 // 2
@@ -110,7 +118,7 @@ class Layer:
             grouped_gemm(GEMM_NT, ro, x_perm, self.w13, h13)
             a_r, a_c, as_r, as_c = swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, rowwise=True, colwise=col,
                                                        row_off=ro, block_off=bo, clamped=self.clamped,
-                                                       limit=self.limit)
+                                                       limit=self.limit, kblock=self.kb_a)
         # W2 in both directions from one read (the colwise copy is kept for
         # the backward's FC2 dgrad)
         self._quantize_w2()
@@ -126,7 +134,8 @@ class Layer:
         dev = dy.device
         ro, bo = self.row_off, self.block_off
         mx = self.recipe == "mxfp8"
-        dy_r, dy_c, dys_r, dys_c = quantize(dy, rowwise=True, colwise=mx, row_off=ro, block_off=bo)
+        dy_r, dy_c, dys_r, dys_c = quantize(dy, rowwise=True, colwise=mx, row_off=ro, block_off=bo,
+                                            kblock=self.kb_dy)
         w2c, w2cs = s["w2c"], s["w2cs"]
         da = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
         grouped_gemm(GEMM_NN, ro, dy_r, w2c, da, dys_r, w2cs)
@@ -144,7 +153,7 @@ class Layer:
             grouped_gemm(GEMM_TN, ro, dy, a_bf16, dw2)
         dq_r, dq_c, dqs_r, dqs_c, dd, dscale = swiglu_quantize_bwd(
             da, gate, up, s["scale"], rowwise=True, colwise=mx, row_off=ro, block_off=bo,
-            clamped=self.clamped, limit=self.limit, interleave=self.il)
+            clamped=self.clamped, limit=self.limit, interleave=self.il, kblock=self.kb_dq)
         self._quantize_w13()
         w13c, w13cs = self.w13c, self.w13cs
         dx = torch.empty((R, H), dtype=torch.bfloat16, device=dev)

@@ -102,3 +102,9 @@ def rowblock_of(M, row_off=None):
 def close_h(close_flags):
     """Forward closeness: either rounding (silu or h) may flip h."""
     return close_flags != 0
+
+
+def rowmajor(x):
+    """Row-major codes of a tensor the layer may hold K-blocked (a KBlocked of
+    the package): the same bytes in (rows, K) order, for comparisons."""
+    return x.to_rowmajor() if hasattr(x, "to_rowmajor") else x

@@ -319,3 +319,85 @@ def test_gemm_bf16_every_mode_validates(m):
         ws = fake(6 << 28) if mode == m.GEMM_TN else None
         assert lib.mxq_grouped_gemm(ctypes.byref(a), ws, 256 if ws else 0, None) == 5, mode
         assert "overlaps" in m.last_error()
+
+
+def test_kblock_gemm_validation(m):
+    """K-blocked MXFP8 operands (kblock_plane > 0): only the operands read
+    along the contraction (A of NT / NN, B of NT), with ld 64, K a multiple
+    of 64, the plane a multiple of 16 holding every row; their footprint
+    (planes x plane) counts in the overlap check."""
+    lib = m.lib
+
+    def args(mode=m.GEMM_NT, ka=True, kb=False, K=256):
+        a = gemm_args(m, mode, K=K)
+        if mode == m.GEMM_NN:
+            a.B.ld, a.B.ld_scales, a.B.scale_gstride = 256, 256, 8 * 256
+        if ka:
+            a.A.ld, a.A.kblock_plane = 64, 256 * 64
+        if kb:
+            a.B.ld, a.B.gstride, a.B.kblock_plane = 64, 256 * 64, 4 * 256 * 64
+        return a
+
+    def call(a):
+        return lib.mxq_grouped_gemm(ctypes.byref(a), None, 0, None)
+    bad = args()
+    bad.A.ld = 256                      # a K-blocked operand has ld 64
+    assert call(bad) == 2
+    bad = args(K=96)                    # K a multiple of 64
+    bad.A.ld_scales = bad.B.ld_scales = 3
+    assert call(bad) == 2
+    bad = args()
+    bad.A.kblock_plane = 255 * 64       # the plane must hold all M rows
+    assert call(bad) == 2
+    bad = args()
+    bad.A.kblock_plane = 256 * 64 + 8   # 16-byte multiple
+    assert call(bad) == 3
+    bad = args(kb=True)
+    bad.B.kblock_plane = 4 * 256 * 64 - 16   # the plane must hold all G x N rows
+    assert call(bad) == 2
+    bad = args(kb=True)
+    bad.B.gstride = 255 * 64            # groups of N rows do not overlap
+    assert call(bad) == 2
+    nn = args(m.GEMM_NN, ka=False)
+    nn.B.kblock_plane = 1 << 20         # B of NN runs along N: not K-blocked
+    assert call(nn) == 6
+    tn = gemm_args(m, m.GEMM_TN)
+    tn.A.kblock_plane = 1 << 20
+    assert lib.mxq_grouped_gemm(ctypes.byref(tn), fake(6 << 28), 256, None) == 6
+    bf = args()
+    bf.A.dtype = bf.B.dtype = m.DTYPE_BF16
+    assert call(bf) == 6                # bf16 operands are never K-blocked
+    # the output just inside the last plane of A (plane 3 starts at 3 x 16384)
+    a = args()
+    a.out = BASE + (1 << 28) + 3 * 256 * 64 + 256 * 64 - 16
+    assert call(a) == 5
+
+
+def test_kblock_mx_out_validation(m):
+    """K-blocked rowwise codes (mxq_mx_out.kblock_plane): ld_codes 64, a
+    multiple of 64 columns, the plane a 16-byte multiple holding every row,
+    under 2^31 bytes in all; colwise codes and the fused FC1 epilogue stay
+    row-major; the blocked footprint counts in the overlap check."""
+    lib = m.lib
+
+    def q(M=64, K=128, ld_codes=64, plane=64 * 64, dirs=1, col_plane=0, x=0):
+        row = m.mxq_mx_out(BASE + (4 << 24), ld_codes, BASE + (5 << 24), K // 32, plane)
+        col = m.mxq_mx_out(BASE + (6 << 24), K, BASE + (7 << 24), K, col_plane)
+        return lib.mxq_quantize(M, K, fake(x), K, None, dirs, ctypes.byref(row) if dirs & 1 else None,
+                                ctypes.byref(col) if dirs & 2 else None, None)
+    assert q(ld_codes=128) == 2              # blocked codes have ld_codes 64
+    assert q(K=96) == 2                      # a multiple of 64 columns
+    assert q(plane=63 * 64) == 2             # the plane holds all M rows
+    assert q(plane=64 * 64 + 4) == 3         # 16-byte multiple
+    assert q(M=1 << 22, K=1 << 13, plane=(1 << 22) * 64) == 4   # 128 planes of 256 MiB: past 2^31 bytes
+    assert q(dirs=2, col_plane=64 * 64) == 6  # colwise codes are row-major
+    # an input inside the last plane of the blocked codes (plane 1 of 2)
+    assert q(x=(4 << 24) + 64 * 64 + 32) == 5
+    # the fused FC1 epilogue writes row-major codes
+    a = gemm_args(m, m.GEMM_NT, N=256)
+    a.A.dtype = a.B.dtype = m.DTYPE_BF16
+    a.A.scales = a.B.scales = None
+    a.A.ld, a.B.ld, a.B.gstride, a.ld_out = 256, 256, 256 * 256, 256
+    row = m.mxq_mx_out(BASE + (6 << 28), 64, BASE + (7 << 28), 4, 64 * 256)
+    assert lib.mxq_grouped_gemm_swiglu(ctypes.byref(a), ctypes.byref(m.mxq_act(0, 7.0, 128)), None, 1,
+                                       ctypes.byref(row), None, None) == 6

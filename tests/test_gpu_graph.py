@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import workloads as W
+from parity import rowmajor
 
 pytestmark = pytest.mark.gpu
 
@@ -30,9 +31,9 @@ KEYS = ("da", "dd", "dq_r", "dqs_r", "dq_c", "dx", "dw2", "dw13", "dscale")
 def snapshot(layer, y):
     out = {"y": y.clone()}
     for k in KEYS:
-        out[k] = layer.grads[k].clone()
+        out[k] = rowmajor(layer.grads[k]).clone()
     for k in ("h13", "a_r", "as_r"):
-        out[k] = layer.saved[k].clone()
+        out[k] = rowmajor(layer.saved[k]).clone()
     return out
 
 

@@ -18,6 +18,7 @@ import torch
 
 import oracle as O
 import workloads as W
+from parity import rowmajor
 
 pytestmark = pytest.mark.gpu
 
@@ -85,7 +86,7 @@ def test_layer_forward_backward(mxq, skewed, clamped):
     # fused activation forward on the GPU's H13: rowwise + per-expert colwise
     rc, cc, rs, cs, _h = O.swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale, 3, ro, kind, 7.0)
     nb = cs.shape[0]
-    same(u8(s["a_r"]), rc, "act fwd row codes")
+    same(u8(rowmajor(s["a_r"])), rc, "act fwd row codes")
     same(u8(s["as_r"]), rs, "act fwd row scales")
     same(u8(s["a_c"]), cc, "act fwd col codes")
     same(u8(s["as_c"])[:nb], cs, "act fwd col scales")
@@ -102,7 +103,7 @@ def test_layer_forward_backward(mxq, skewed, clamped):
     # backward: dY quantized both ways (colwise per expert)
     dyb = bits(dy)
     q = O.mx_quantize(dyb, 3, ro)
-    same(u8(gr["dy_r"]), q[0], "dY row codes")
+    same(u8(rowmajor(gr["dy_r"])), q[0], "dY row codes")
     same(u8(gr["dys_r"]), q[2], "dY row scales")
     same(u8(gr["dy_c"]), q[1], "dY col codes")
     same(u8(gr["dys_c"])[:q[3].shape[0]], q[3], "dY col scales")
@@ -125,7 +126,7 @@ def test_layer_forward_backward(mxq, skewed, clamped):
     da = bits(gr["da"])
     b = O.swiglu_quantize_bwd(da, h13[:, :I], h13[:, I:], scale, 3, ro, kind, 7.0, want_close=True)
     brc, bcc, brs, bcs, dg, du, ds, _close, tol = b
-    same(u8(gr["dq_r"]), brc, "act bwd row codes")
+    same(u8(rowmajor(gr["dq_r"])), brc, "act bwd row codes")
     same(u8(gr["dqs_r"]), brs, "act bwd row scales")
     same(u8(gr["dq_c"]), bcc, "act bwd col codes")
     same(u8(gr["dqs_c"])[:bcs.shape[0]], bcs, "act bwd col scales")
@@ -224,20 +225,20 @@ def test_full_size_layer_sampled(mxq, routing):
                              "bf16")
         close(_host(s["h13"], S)[:, cs], ref, f"FC1 expert {g}")
         # FC2 (MXFP8 NT): columns 224..287 of (R, H)
-        A, As = _host(s["a_r"], S), _host(s["as_r"], S)
+        A, As = _host(rowmajor(s["a_r"]), S), _host(s["as_r"], S)
         B, Bs = u8(s["w2q"][g, cs, :]), u8(s["w2s"][g, cs, :])
         ref = O.grouped_gemm("m", one, 0, 64, I, O.Operand("mxfp8", A, 0, I, 1, As, 0, I // 32, 1),
                              O.Operand("mxfp8", B, 0, I, 1, Bs, 0, I // 32, 1), "bf16")
         close(_host(y, S)[:, cs], ref, f"FC2 expert {g}")
         # FC2 dgrad (MXFP8 NN): columns 224..287 of (R, I)
-        A, As = _host(gr["dy_r"], S), _host(gr["dys_r"], S)
+        A, As = _host(rowmajor(gr["dy_r"]), S), _host(gr["dys_r"], S)
         B = np.ascontiguousarray(u8(gr["w2c"][g])[:, cs])
         Bs = np.ascontiguousarray(u8(gr["w2cs"][g])[:, cs])
         ref = O.grouped_gemm("m", one, 0, 64, H, O.Operand("mxfp8", A, 0, H, 1, As, 0, H // 32, 1),
                              O.Operand("mxfp8", B, 0, 1, 64, Bs, 0, 1, 64), "bf16")
         close(_host(gr["da"], S)[:, cs], ref, f"FC2 dgrad expert {g}")
         # FC1 dgrad (MXFP8 NN): columns 224..287 of (R, H)
-        A, As = _host(gr["dq_r"], S), _host(gr["dqs_r"], S)
+        A, As = _host(rowmajor(gr["dq_r"]), S), _host(gr["dqs_r"], S)
         B = np.ascontiguousarray(u8(gr["w13c"][g])[:, cs])
         Bs = np.ascontiguousarray(u8(gr["w13cs"][g])[:, cs])
         ref = O.grouped_gemm("m", one, 0, 64, 2 * I, O.Operand("mxfp8", A, 0, 2 * I, 1, As, 0, 2 * I // 32, 1),
@@ -260,14 +261,14 @@ def test_full_size_layer_sampled(mxq, routing):
         # colwise blocks restart at the expert's first row)
         h13 = _host(s["h13"], allr)
         rc, cc, rs, cs_, _h = O.swiglu_quantize_fwd(h13[:, :I], h13[:, I:], scale[r0:r1], 3, None, kind, 7.0)
-        same(u8(s["a_r"][r0:r1]), rc, "act fwd row codes")
+        same(u8(rowmajor(s["a_r"])[r0:r1]), rc, "act fwd row codes")
         same(u8(s["as_r"][r0:r1]), rs, "act fwd row scales")
         same(u8(s["a_c"][r0:r1]), cc, "act fwd col codes")
         same(u8(s["as_c"][b0:b1]), cs_, "act fwd col scales")
         # activation backward on the expert's rows of the GPU's dA and H13
         da = _host(gr["da"], allr)
         b = O.swiglu_quantize_bwd(da, h13[:, :I], h13[:, I:], scale[r0:r1], 3, None, kind, 7.0, want_close=True)
-        same(u8(gr["dq_r"][r0:r1]), b[0], "act bwd row codes")
+        same(u8(rowmajor(gr["dq_r"])[r0:r1]), b[0], "act bwd row codes")
         same(u8(gr["dqs_r"][r0:r1]), b[2], "act bwd row scales")
         same(u8(gr["dq_c"][r0:r1]), b[1], "act bwd col codes")
         same(u8(gr["dqs_c"][b0:b1]), b[3], "act bwd col scales")
@@ -278,7 +279,7 @@ def test_full_size_layer_sampled(mxq, routing):
         assert np.all(err <= b[8] + 1e-30), f"dscale off by {err.max()}"
         # dY (both directions) and X (colwise) over the expert's rows
         q = O.mx_quantize(bits(dy[r0:r1]), 3)
-        same(u8(gr["dy_r"][r0:r1]), q[0], "dY row codes")
+        same(u8(rowmajor(gr["dy_r"])[r0:r1]), q[0], "dY row codes")
         same(u8(gr["dys_r"][r0:r1]), q[2], "dY row scales")
         same(u8(gr["dy_c"][r0:r1]), q[1], "dY col codes")
         same(u8(gr["dys_c"][b0:b1]), q[3], "dY col scales")
@@ -339,6 +340,7 @@ def test_full_size_layer_modes_sampled(mxq, routing):
     sp, gp = lp.saved, lp.grads
 
     def eq(a, b, what):
+        a, b = rowmajor(a), rowmajor(b)
         assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
                            b.view(torch.uint8) if b.dtype != torch.uint8 else b), what
 
@@ -356,7 +358,7 @@ def test_full_size_layer_modes_sampled(mxq, routing):
     for k in ("da", "dw2", "dscale"):
         eq(gp[k], gf[k], f"fused: {k}")
     eq(gp["dd"], gf["dd"][:, perm], "fused: [dgate | dup]")
-    eq(gp["dq_r"], gf["dq_r"][:, perm], "fused: dact rowwise codes")
+    eq(gp["dq_r"], rowmajor(gf["dq_r"])[:, perm], "fused: dact rowwise codes")
     eq(gp["dq_c"], gf["dq_c"][:, perm], "fused: dact colwise codes")
     eq(gp["dqs_c"][:ncb], gf["dqs_c"][:ncb][:, perm], "fused: dact colwise scales")
     eq(gp["dw13"], gf["dw13"][:, perm, :], "fused: dW13")
@@ -396,5 +398,5 @@ def test_full_size_layer_modes_sampled(mxq, routing):
     for k in ("da", "dscale", "dw2", "a_bf16"):
         eq(gr_[k], gfr[k], f"fused recipe: {k}")
     eq(gr_["dd"], gfr["dd"][:, perm], "fused recipe: [dgate | dup]")
-    eq(gr_["dq_r"], gfr["dq_r"][:, perm], "fused recipe: dact rowwise codes")
+    eq(gr_["dq_r"], rowmajor(gfr["dq_r"])[:, perm], "fused recipe: dact rowwise codes")
     eq(gr_["dw13"], gfr["dw13"][:, perm, :], "fused recipe: dW13")
