@@ -266,7 +266,7 @@ def moe_section(m, torch, W, reps=5):
             fn()
             us, = timed_alt(torch, [fn], reps)
             tf = flops[k] / us / 1e6
-            peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP8_PEAK_TFLOPS
+            peak = BF16_PEAK_TFLOPS if dt.startswith("bf16") else FP8_PEAK_TFLOPS
             per[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": dt, "frac_peak": round(tf / peak, 4)}
             tot_fl += flops[k]
             tot_us += us
@@ -349,9 +349,11 @@ def graph_section(torch, W, reps=10):
 def supplementary_gemm(m, torch, reps=5):
     """A compute-bound grouped shape, outside the workload's configurations
     (labelled as such): 8 equal groups of 4096 rows, N = K = 8192, NT, in
-    MXFP8 (random finite E4M3 codes, unit-range E8M0 scales) and in bf16.
-    It shows the matrix-core rate the kernel reaches when the contraction is
-    long and the output small against the flops."""
+    MXFP8 (random finite E4M3 codes, unit-range E8M0 scales) and in bf16,
+    each with row-major operands and with the same operands K-blocked by 64
+    bytes (the layout change itself is not timed).  It shows the
+    matrix-core rate the kernel reaches when the contraction is long and the
+    output small against the flops."""
     G, rows, N, K = 8, 4096, 8192, 8192
     dev = "cuda"
     sp = torch.full((G,), rows, dtype=torch.int64, device=dev)
@@ -363,7 +365,7 @@ def supplementary_gemm(m, torch, reps=5):
     res = {"shape": f"{G} groups x {rows} rows, N = K = {N}, NT", "configuration": "supplementary, not a workload config"}
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for dt in ("fp8", "fp8_kblock", "bf16"):
+    for dt in ("fp8", "fp8_kblock", "bf16", "bf16_kblock"):
         if dt == "fp8":
             A = torch.randint(0, 0x70, (R, K), dtype=torch.uint8, device=dev, generator=g)
             B = torch.randint(0, 0x70, (G, N, K), dtype=torch.uint8, device=dev, generator=g)
@@ -376,10 +378,14 @@ def supplementary_gemm(m, torch, reps=5):
             Ak, Bk = m.KBlocked.from_rowmajor(A), m.KBlocked.from_rowmajor(B)
             A = B = None
             fn = lambda: m.grouped_gemm(m.GEMM_NT, ro, Ak, Bk, out, As, Bs)
-        else:
+        elif dt == "bf16":
             A = torch.randn((R, K), device=dev, generator=g).to(torch.bfloat16)
             B = torch.randn((G, N, K), device=dev, generator=g).to(torch.bfloat16)
             fn = lambda: m.grouped_gemm(m.GEMM_NT, ro, A, B, out)
+        else:
+            Ak, Bk = m.KBlocked.from_rowmajor(A), m.KBlocked.from_rowmajor(B)
+            A = B = None
+            fn = lambda: m.grouped_gemm(m.GEMM_NT, ro, Ak, Bk, out)
         fn()
         fn()
         ts = []
@@ -391,13 +397,13 @@ def supplementary_gemm(m, torch, reps=5):
             ts.append(e0.elapsed_time(e1) * 1e3)
         us = sorted(ts)[len(ts) // 2]
         tf = 2.0 * R * N * K / us / 1e6
-        peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP8_PEAK_TFLOPS
+        peak = BF16_PEAK_TFLOPS if dt.startswith("bf16") else FP8_PEAK_TFLOPS
         res[dt] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "frac_peak": round(tf / peak, 4)}
         fn = None
         if dt == "fp8_kblock":
             del Ak, Bk, As, Bs
-        elif dt == "bf16":
-            del A, B
+        elif dt == "bf16_kblock":
+            del Ak, Bk
     del out
     torch.cuda.empty_cache()
     return res

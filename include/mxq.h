@@ -334,18 +334,20 @@ typedef enum { MXQ_DTYPE_BF16 = 0, MXQ_DTYPE_MXFP8_E4M3 = 1, MXQ_DTYPE_F32 = 2 }
  * block_off.
  * Every product is accumulated in fp32 and rounded once to the output dtype.
  *
- * K-blocked MXFP8 codes (an operand read along the contraction: A of NT and
- * NN, B of NT).  With kblock_plane = P > 0 the codes are stored in planes of
- * 64 contraction bytes: code (r, k) of row r lies at byte
- * (k / 64) * P + r * 64 + k % 64 of data (for B of NT, r = g * gstride / 64
- * + n, i.e. gstride is the byte distance of group g's rows within a plane).
- * ld must then be 64, K a multiple of 64, P a multiple of 16 and at least
- * the rows' extent within a plane.  The values and results are those of the
- * row-major layout; what changes is that a 64-byte stage of 16 rows is one
- * contiguous kilobyte, so every load of the GEMM covers whole cache lines.
- * The fused activation kernels and the quantizer write their rowwise codes in
- * this layout when their mxq_mx_out asks for it (mxq_mx_out.kblock_plane).
- * Scales keep their row-major layout.
+ * K-blocked operands (an operand read along the contraction: A of NT and
+ * NN, B of NT; MXFP8 codes or bf16).  With kblock_plane = P > 0 the operand
+ * is stored in planes of 64 contraction bytes (e = 64 codes or 32 bf16 per
+ * plane row): element (r, k) of row r lies at byte
+ * (k / e) * P + r * 64 + (k % e) * element size of data (for B of NT,
+ * r = g * gstride / e + n: gstride, in elements, is the distance of group
+ * g's rows within a plane).  ld must then be e, K a multiple of e, P a
+ * multiple of 16 and at least the rows' extent within a plane (else
+ * MXQ_ERR_SHAPE / _ALIGN; MXQ_ERR_UNSUPPORTED for B of NN and for TN).  The
+ * values and results are those of the row-major layout; what changes is that
+ * a 64-byte stage of 16 rows is one contiguous kilobyte, so every load of the
+ * GEMM covers whole cache lines.  The fused activation kernels and the
+ * quantizer write their rowwise codes in this layout when their mxq_mx_out
+ * asks for it (mxq_mx_out.kblock_plane).  Scales keep their row-major layout.
  */
 typedef enum { MXQ_GEMM_NT = 0, MXQ_GEMM_NN = 1, MXQ_GEMM_TN = 2 } mxq_gemm_mode;
 
@@ -357,8 +359,8 @@ typedef struct {
     const uint8_t *scales;  /* E8M0 bytes (MXFP8 only) */
     int64_t ld_scales;      /* scale row pitch, bytes */
     int64_t scale_gstride;  /* scale group stride, bytes (B of NT/NN only) */
-    int64_t kblock_plane;   /* 0: row-major codes; P > 0: K-blocked MXFP8 codes
-                               with plane stride P bytes (see above) */
+    int64_t kblock_plane;   /* 0: row-major; P > 0: K-blocked, plane stride P
+                               bytes (see above) */
 } mxq_operand;
 
 typedef struct {

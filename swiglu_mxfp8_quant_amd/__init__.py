@@ -432,45 +432,55 @@ def srelu_quantize_bwd(grad, x, scale=None, rowwise=True, colwise=False, row_off
 
 
 class KBlocked:
-    """MXFP8 codes K-blocked by 64 (the layout of mxq_operand.kblock_plane):
-    code (r, k) of a (rows, K) matrix sits at [k // 64, r, k % 64] of `data`,
-    a (K/64, rows, 64) uint8 tensor whose plane stride is data.stride(0); a
-    (G, N, K) stack of per-group matrices is blocked over its G * N rows.
-    `shape` is the logical (row-major) shape."""
+    """An operand K-blocked by 64 bytes (the layout of mxq_operand.kblock_plane
+    and mxq_mx_out.kblock_plane): with e = 64 / element size elements per
+    plane row, element (r, k) of a (rows, K) matrix sits at [k // e, r, k % e]
+    of `data`, a (K / e, rows, e) tensor (uint8 MXFP8 codes or bf16) whose
+    plane stride is data.stride(0) elements; a (G, N, K) stack of per-group
+    matrices is blocked over its G * N rows.  `shape` is the logical
+    (row-major) shape."""
 
     def __init__(self, data, shape):
-        if shape[-1] % 64 != 0:
-            raise ValueError("K-blocked codes need a multiple of 64 columns")
         self.data = data
         self.shape = tuple(shape)
+        if (self.shape[-1] * data.element_size()) % 64 != 0:
+            raise ValueError("K-blocked operands need rows of a multiple of 64 bytes")
+
+    @property
+    def epp(self):
+        """Elements per 64-byte plane row."""
+        return 64 // self.data.element_size()
 
     @property
     def plane(self):
         """Bytes between planes (at least 64, so that an empty matrix still
         reads as K-blocked)."""
-        return max(self.data.stride(0), 64)
+        return max(self.data.stride(0) * self.data.element_size(), 64)
 
     @classmethod
     def from_rowmajor(cls, t):
-        """Blocked copy of row-major codes (R, K) or (G, N, K): a layout
-        change done by torch, for tests and for codes that were not written
-        blocked by the kernels."""
+        """Blocked copy of a row-major (R, K) or (G, N, K) tensor: a layout
+        change done by torch, for tests, benchmarks and operands that were not
+        written blocked by the kernels."""
         K = t.shape[-1]
+        e = 64 // t.element_size()
         rows = t.numel() // K
-        d = t.reshape(rows, K // 64, 64).transpose(0, 1).contiguous()
+        d = t.reshape(rows, K // e, e).transpose(0, 1).contiguous()
         return cls(d, t.shape)
 
     def to_rowmajor(self):
-        K = self.shape[-1]
         return self.data.transpose(0, 1).reshape(self.shape).contiguous()
 
     @classmethod
-    def empty(cls, shape, device):
+    def empty(cls, shape, device, dtype=None):
+        torch = _torch()
+        dtype = torch.uint8 if dtype is None else dtype
+        e = 64 // torch.empty((), dtype=dtype).element_size()
         K = shape[-1]
         rows = 1
         for d in shape[:-1]:
             rows *= d
-        return cls(_torch().empty((K // 64, rows, 64), dtype=_torch().uint8, device=device), shape)
+        return cls(torch.empty((K // e, rows, e), dtype=dtype, device=device), shape)
 
 
 def rowmajor(codes):
@@ -484,8 +494,10 @@ def _operand(data, scales=None, group_dim=False):
     KBlocked codes, and its E8M0 scale tensor (same rank as the logical
     shape)."""
     if isinstance(data, KBlocked):
-        gs = data.shape[1] * 64 if group_dim else 0
-        op = mxq_operand(DTYPE_MXFP8, data.data.data_ptr(), 64, gs, None, 0, 0, data.plane)
+        f8 = data.data.dtype == _torch().uint8
+        gs = data.shape[1] * data.epp if group_dim else 0
+        op = mxq_operand(DTYPE_MXFP8 if f8 else DTYPE_BF16, data.data.data_ptr(), data.epp, gs, None, 0, 0,
+                         data.plane)
     else:
         f8 = data.dtype == _torch().uint8
         if group_dim:

@@ -322,12 +322,13 @@ mxq_status check_gemm_alias(const mxq_gemm_args &a) {
         out = range_groups(a.out, a.G, a.out_gstride, a.M, a.N, a.ld_out, osz, "out");
     } else {
         const int64_t kb = (a.K + 31) / 32;
-        if (a.A.kblock_plane > 0) ins.push_back(range_kblock(a.A.data, a.K / 64, a.A.kblock_plane, a.M * 64, "A"));
+        if (a.A.kblock_plane > 0) ins.push_back(range_kblock(a.A.data, a.K * esz / 64, a.A.kblock_plane, a.M * 64, "A"));
         else ins.push_back(range2d(a.A.data, a.M, a.K, a.A.ld, esz, "A"));
         if (f8) ins.push_back(range2d(a.A.scales, a.M, kb, a.A.ld_scales, 1, "A scales"));
         if (a.mode == MXQ_GEMM_NT) {
             if (a.B.kblock_plane > 0)
-                ins.push_back(range_kblock(a.B.data, a.K / 64, a.B.kblock_plane, (a.G - 1) * a.B.gstride + a.N * 64, "B"));
+                ins.push_back(range_kblock(a.B.data, a.K * esz / 64, a.B.kblock_plane,
+                                           (a.G - 1) * a.B.gstride * esz + a.N * 64, "B"));
             else ins.push_back(range_groups(a.B.data, a.G, a.B.gstride, a.N, a.K, a.B.ld, esz, "B"));
             if (f8) ins.push_back(range_groups(a.B.scales, a.G, a.B.scale_gstride, a.N, kb, a.B.ld_scales, 1, "B scales"));
         } else {

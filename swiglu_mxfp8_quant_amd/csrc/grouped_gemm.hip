@@ -1610,27 +1610,32 @@ int gemm_prepare(const mxq_gemm_args &in, GemmArgs &g, std::string &err) {
         err = "out pointer and pitches must be 16-byte aligned";
         return MXQ_ERR_ALIGN;
     }
-    // K-blocked codes: MXFP8 operands read along the contraction only
+    // K-blocked operands (64-byte contraction planes; either dtype): only the
+    // operands read along the contraction.  A plane row is 64 bytes, i.e. ld
+    // = 64 / element size, and the group stride counts elements too.
     const bool kba = in.A.kblock_plane != 0, kbb = in.B.kblock_plane != 0;
     if (kba || kbb) {
         if (in.A.kblock_plane < 0 || in.B.kblock_plane < 0) { err = "kblock_plane must be >= 0"; return MXQ_ERR_SHAPE; }
-        if (!f8) { err = "K-blocked operands are MXFP8 codes"; return MXQ_ERR_UNSUPPORTED; }
         if (in.mode == MXQ_GEMM_TN || (in.mode == MXQ_GEMM_NN && kbb)) {
             err = "only operands contiguous along the contraction (A of NT / NN, B of NT) can be K-blocked";
             return MXQ_ERR_UNSUPPORTED;
         }
-        if (in.K % 64 != 0) { err = "K-blocked operands need K a multiple of 64"; return MXQ_ERR_SHAPE; }
-        if ((kba && in.A.ld != 64) || (kbb && in.B.ld != 64)) { err = "a K-blocked operand has ld = 64"; return MXQ_ERR_SHAPE; }
+        if ((in.K * esz) % 64 != 0) { err = "K-blocked operands need K a multiple of 64 bytes"; return MXQ_ERR_SHAPE; }
+        if ((kba && in.A.ld * esz != 64) || (kbb && in.B.ld * esz != 64)) {
+            err = "a K-blocked operand has ld = 64 bytes";
+            return MXQ_ERR_SHAPE;
+        }
         if ((kba && in.A.kblock_plane % 16 != 0) || (kbb && in.B.kblock_plane % 16 != 0)) {
             err = "kblock_plane must be a multiple of 16 bytes";
             return MXQ_ERR_ALIGN;
         }
         if (kba && in.A.kblock_plane < in.M * 64) { err = "A kblock_plane is smaller than its M rows of 64 bytes"; return MXQ_ERR_SHAPE; }
-        if (kbb && (in.B.kblock_plane < (in.G - 1) * in.B.gstride + in.N * 64 || (in.G > 1 && in.B.gstride < in.N * 64))) {
+        if (kbb && (in.B.kblock_plane < (in.G - 1) * in.B.gstride * esz + in.N * 64 ||
+                    (in.G > 1 && in.B.gstride * esz < in.N * 64))) {
             err = "B kblock_plane or group stride too small for G groups of N rows of 64 bytes";
             return MXQ_ERR_SHAPE;
         }
-        const int64_t planes = in.K / 64;
+        const int64_t planes = in.K * esz / 64;
         if ((kba && in.A.kblock_plane > kMaxPlaneExtent / planes) || (kbb && in.B.kblock_plane > kMaxPlaneExtent / planes)) {
             err = "K-blocked operand extent too large";
             return MXQ_ERR_OVERFLOW;

@@ -322,10 +322,11 @@ def test_gemm_bf16_every_mode_validates(m):
 
 
 def test_kblock_gemm_validation(m):
-    """K-blocked MXFP8 operands (kblock_plane > 0): only the operands read
-    along the contraction (A of NT / NN, B of NT), with ld 64, K a multiple
-    of 64, the plane a multiple of 16 holding every row; their footprint
-    (planes x plane) counts in the overlap check."""
+    """K-blocked operands (kblock_plane > 0): only the operands read along
+    the contraction (A of NT / NN, B of NT), with 64-byte plane rows (ld 64
+    codes or 32 bf16), K a multiple of 64 bytes, the plane a multiple of 16
+    holding every row; their footprint (planes x plane) counts in the overlap
+    check."""
     lib = m.lib
 
     def args(mode=m.GEMM_NT, ka=True, kb=False, K=256):
@@ -366,7 +367,9 @@ def test_kblock_gemm_validation(m):
     assert lib.mxq_grouped_gemm(ctypes.byref(tn), fake(6 << 28), 256, None) == 6
     bf = args()
     bf.A.dtype = bf.B.dtype = m.DTYPE_BF16
-    assert call(bf) == 6                # bf16 operands are never K-blocked
+    bf.A.scales = bf.B.scales = None
+    bf.A.ld = 64                        # a bf16 plane row is 32 elements (64 bytes)
+    assert call(bf) == 2
     # the output just inside the last plane of A (plane 3 starts at 3 x 16384)
     a = args()
     a.out = BASE + (1 << 28) + 3 * 256 * 64 + 256 * 64 - 16

@@ -262,3 +262,38 @@ def test_layer_kblock_equals_rowmajor(mxq, recipe, fused):
             assert isinstance(layer.grads["dy_r"], mxq.KBlocked)
     for a, b, what in zip(outs[0], outs[1], ("Y", "dX", "dW13", "dW2", "dscale")):
         eq(a, b, what)
+
+
+@pytest.mark.parametrize("mode", ["NT", "NN"])
+def test_gemm_bf16_kblock(mxq, mode):
+    """bf16 operands K-blocked by 64 bytes (32 elements per plane row): NT
+    with A, B or both blocked, NN with A blocked, against the row-major run
+    bit for bit and against the oracle."""
+    rng = np.random.default_rng(51 if mode == "NT" else 52)
+    ro, _ = offsets(mxq, SPLITS)
+    ro_np = O.splits_to_offsets(SPLITS)[0]
+    R, N, K, G = sum(SPLITS), 208, 320, len(SPLITS)
+
+    def bf(shape, std):
+        return W.bf16_bits(torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(torch.bfloat16))
+    A = bf((R, K), 1.0)
+    Ad = W.from_bits(A, "cuda")
+    if mode == "NT":
+        B = bf((G, N, K), 0.05)
+        opB = O.Operand("bf16", B, N * K, K, 1)
+    else:
+        B = bf((G, K, N), 0.05)
+        opB = O.Operand("bf16", B, K * N, 1, N)
+    Bd = W.from_bits(B, "cuda")
+    ref = O.grouped_gemm("m", ro_np, 0, N, K, O.Operand("bf16", A, 0, K, 1), opB, "f32")
+    gm = mxq.GEMM_NT if mode == "NT" else mxq.GEMM_NN
+    rm = torch.empty((R, N), dtype=torch.float32, device="cuda")
+    mxq.grouped_gemm(gm, ro, Ad, Bd, rm)
+    combos = ((True, True), (True, False), (False, True)) if mode == "NT" else ((True, False),)
+    for a_kb, b_kb in combos:
+        out = torch.full((R, N), 7.0, dtype=torch.float32, device="cuda")
+        mxq.grouped_gemm(gm, ro, mxq.KBlocked.from_rowmajor(Ad) if a_kb else Ad,
+                         mxq.KBlocked.from_rowmajor(Bd) if b_kb else Bd, out)
+        torch.cuda.synchronize()
+        eq(out, rm, f"{mode} bf16 K-blocked A={a_kb} B={b_kb} against row-major")
+    check_close(out.cpu().numpy().astype(np.float64), ref.astype(np.float64))
