@@ -346,14 +346,14 @@ def swiglu_bf16(gate, up, scale=None, rowwise=False, colwise=False, row_off=None
 
 
 def srelu_quantize_fwd(x, scale=None, rowwise=True, colwise=False, row_off=None, block_off=None,
-                       n_col_blocks=None, stream=None):
+                       n_col_blocks=None, kblock=False, stream=None):
     """The row-scaled SReLU forward, MXFP8 out: (codes_row, codes_col,
     scales_row, scales_col) as swiglu_quantize_fwd."""
     M, K = x.shape
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if n_col_blocks is None:
         n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
-    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device, kblock)
     ro, co = _outs(rc, cc, rs, cs, dirs)
     check(mxq_swiglu_quantize_fwd(make_act(ACT_SRELU), x, None, scale, make_groups(row_off, block_off), dirs, ro,
                                   co, stream))
@@ -411,7 +411,7 @@ def swiglu_quantize_bwd(grad, gate, up, scale=None, rowwise=True, colwise=False,
 
 
 def srelu_quantize_bwd(grad, x, scale=None, rowwise=True, colwise=False, row_off=None, block_off=None,
-                       n_col_blocks=None, dense=True, want_dscale=True, stream=None):
+                       n_col_blocks=None, dense=True, want_dscale=True, kblock=False, stream=None):
     """The row-scaled SReLU backward: (codes_row, codes_col, scales_row,
     scales_col, dx, dscale), the codes covering the (M, K) dx."""
     import torch
@@ -419,7 +419,7 @@ def srelu_quantize_bwd(grad, x, scale=None, rowwise=True, colwise=False, row_off
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if n_col_blocks is None:
         n_col_blocks = (M + 31) // 32 if row_off is None else colwise_scale_rows_bound(M, row_off.numel() - 1)
-    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device)
+    rc, cc, rs, cs = _alloc_mx(M, K, dirs, n_col_blocks, x.device, kblock)
     ro, co = _outs(rc, cc, rs, cs, dirs)
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if dense else None
     ds = torch.empty(M, dtype=torch.float32, device=x.device) if want_dscale else None

@@ -297,3 +297,23 @@ def test_gemm_bf16_kblock(mxq, mode):
         torch.cuda.synchronize()
         eq(out, rm, f"{mode} bf16 K-blocked A={a_kb} B={b_kb} against row-major")
     check_close(out.cpu().numpy().astype(np.float64), ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("M,K", [(96, 768), (64, 1024)])
+def test_srelu_kblock_equals_rowmajor(mxq, M, K):
+    """The row-scaled SReLU (unary) through the same stores: forward codes and
+    the backward's dx codes K-blocked against row-major."""
+    x = W._normal((M, K), 1.0, 9, 44, "cuda")
+    sc = W.row_scale(M, seed=9).cuda()
+    dy = W.grad_out(M, K, seed=9).cuda()
+    ref = mxq.srelu_quantize_fwd(x, sc, rowwise=True, colwise=True)
+    got = mxq.srelu_quantize_fwd(x, sc, rowwise=True, colwise=True, kblock=True)
+    rb = mxq.srelu_quantize_bwd(dy, x, sc, rowwise=True, colwise=True)
+    gb = mxq.srelu_quantize_bwd(dy, x, sc, rowwise=True, colwise=True, kblock=True)
+    torch.cuda.synchronize()
+    eq(got[0].to_rowmajor(), ref[0], "forward rowwise codes")
+    eq(gb[0].to_rowmajor(), rb[0], "backward rowwise codes")
+    for i in (1, 2, 3):
+        eq(got[i], ref[i], f"forward output {i}")
+        eq(gb[i], rb[i], f"backward output {i}")
+    eq(gb[4], rb[4], "dx")
