@@ -174,22 +174,27 @@ def gpu_clocks():
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 MOE_VARIANTS = (("uniform_plain", False, False), ("zipf_plain", True, False), ("zipf_clamped", True, True))
+GEMM_INNER = 4   # back-to-back calls per timing of a single GEMM (timed_alt)
 
 
-def timed_alt(torch, fns, reps):
-    """Medians (us) of `reps` rounds that time each of fns once, in turn, on
-    the current stream (alternating, so that clock drift over the run falls
-    on every variant alike)."""
+def timed_alt(torch, fns, reps, inner=1):
+    """Medians (us) of `reps` rounds that time each of fns, in turn, on the
+    current stream (alternating, so that clock drift over the run falls on
+    every variant alike).  Each timing covers `inner` calls back to back and
+    reports the time per call: the host's time to issue the first call lies
+    between the events, and over several calls it is a small share (the
+    later calls are issued while the GPU runs the earlier ones)."""
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ts = [[] for _ in fns]
     for _ in range(reps):
         for i, fn in enumerate(fns):
             e0.record(stream)
-            fn()
+            for _ in range(inner):
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            ts[i].append(e0.elapsed_time(e1) * 1e3)
+            ts[i].append(e0.elapsed_time(e1) * 1e3 / inner)
     return [sorted(t)[len(t) // 2] for t in ts]
 
 
@@ -264,7 +269,7 @@ def moe_section(m, torch, W, reps=5):
         per, tot_fl, tot_us = {}, 0.0, 0.0
         for k, (fn, dt) in calls.items():
             fn()
-            us, = timed_alt(torch, [fn], reps)
+            us, = timed_alt(torch, [fn], reps, inner=GEMM_INNER)
             tf = flops[k] / us / 1e6
             peak = BF16_PEAK_TFLOPS if dt.startswith("bf16") else FP8_PEAK_TFLOPS
             per[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": dt, "frac_peak": round(tf / peak, 4)}
@@ -279,7 +284,7 @@ def moe_section(m, torch, W, reps=5):
         per_bf16 = {}
         for k, fn in bcalls.items():
             fn()
-            us, = timed_alt(torch, [fn], reps)
+            us, = timed_alt(torch, [fn], reps, inner=GEMM_INNER)
             tf = flops[k[:-5]] / us / 1e6
             per_bf16[k] = {"us": round(us, 1), "TFLOPs": round(tf, 1), "dtype": "bf16",
                            "frac_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
@@ -542,15 +547,16 @@ def _expected_gemm_sequence():
     MOE_ONLY_REPS times timed (each the six GEMMs in layer order), the plain
     layer MOE_ONLY_REPS times with the weight cache valid, each GEMM of the
     plain layer and then each bf16 wgrad once untimed and MOE_ONLY_REPS times
-    timed, then FC1 + the activation unfused and fused, both directions and
-    rowwise only, in turn, once untimed and MOE_ONLY_REPS times."""
+    timed (GEMM_INNER calls each), then FC1 + the activation unfused and
+    fused, both directions and rowwise only, in turn, once untimed and
+    MOE_ONLY_REPS times."""
     one = []
     for _ in range(1 + MOE_ONLY_REPS):
         one += GP_ORDER + GP_FUSED_ORDER + GP_BF16_ORDER + GP_BF16_FUSED_ORDER
     for _ in range(MOE_ONLY_REPS):
         one += GP_ORDER
     for g in GP_ORDER + GP_BF16_WGRADS:
-        one += [g] * (1 + MOE_ONLY_REPS)
+        one += [g] * (1 + MOE_ONLY_REPS * GEMM_INNER)
     one += ["FC1 forward", GP_FUSED, "FC1 forward", GP_FUSED_ROW] * (1 + MOE_ONLY_REPS)
     return one * len(MOE_VARIANTS)
 
