@@ -647,6 +647,8 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip the expert-layer (grouped GEMM) section")
     ap.add_argument("--no-cells", action="store_true", help="skip the per-cell record")
     ap.add_argument("--cell-reps", type=int, default=10)
+    ap.add_argument("--supp-only", action="store_true",
+                    help="run only the compute-bound supplementary GEMM shape (for profiling) and print it")
     ap.add_argument("--moe-only", action="store_true",
                     help="only run the expert-layer section once and print its record (for profiling the GEMMs)")
     ap.add_argument("--summarize-gemm-profile", metavar="DIR",
@@ -669,6 +671,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     if args.moe_only:
         print(json.dumps({"gemm": moe_section(m, torch, W, reps=MOE_ONLY_REPS)}), flush=True)
+        return
+    if args.supp_only:
+        print(json.dumps({"gemm_supplementary": supplementary_gemm(m, torch)}), flush=True)
         return
     data = make_data(torch, W, [STRESS])
     cells = [Cell(m, torch, data, k, dn, dict(DIRS)[dn], sh, mo) for (k, dn, sh, mo) in STEP_CELLS]
