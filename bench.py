@@ -414,6 +414,38 @@ def supplementary_gemm(m, torch, reps=5):
     return res
 
 
+def fused_expert_section(m, torch, W, reps=3):
+    """The fused forward and backward (plain SwiGLU, both directions) at the
+    expert layer's width K = 768: 65,536 rows in 128 equal groups (the
+    layer's shape) and 65,536 / 131,072 / 262,144 rows in one group, each
+    twice untimed and `reps` times timed (three calls back to back per
+    timing).  Shows how the launch's fixed cost spreads as M grows."""
+    K, out = 768, {}
+    for M, G in ((65536, 128), (65536, 0), (131072, 0), (262144, 0)):
+        gu = W.packed_gate_up(M, K, seed=0, device="cuda")
+        sc = W.row_scale(M, seed=0, device="cuda")
+        dy = W.grad_out(M, K, seed=0, device="cuda")
+        kw = {}
+        if G:
+            ro, bo, _ = m.splits_to_offsets(torch.full((G,), M // G, dtype=torch.int64, device="cuda"))
+            kw = dict(row_off=ro, block_off=bo)
+        g, u = gu[:, :K], gu[:, K:]
+        fwd = lambda: m.swiglu_quantize_fwd(g, u, sc, rowwise=True, colwise=True, **kw)
+        bwd = lambda: m.swiglu_quantize_bwd(dy, g, u, sc, rowwise=True, colwise=True, **kw)
+        for fn in (fwd, bwd, fwd, bwd):
+            fn()
+        torch.cuda.synchronize()
+        tf, tb = timed_alt(torch, [fwd, bwd], reps, inner=3)
+        bf = M * K * (4 + 2 * (1 + 1 / 32)) + 4 * M
+        bb = M * K * (10 + 4 * (1 + 1 / 32)) + 8 * M
+        out[f"{M}x{K}" + (f"_G{G}" if G else "")] = {
+            "fwd_both_us": round(tf, 1), "fwd_pct_hbm": round(bf / tf / 1e3 / HBM_PEAK_GBS * 100, 1),
+            "bwd_both_us": round(tb, 1), "bwd_pct_hbm": round(bb / tb / 1e3 / HBM_PEAK_GBS * 100, 1)}
+        del gu, dy
+        torch.cuda.empty_cache()
+    return out
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -647,6 +679,8 @@ def main():
     ap.add_argument("--no-moe", action="store_true", help="skip the expert-layer (grouped GEMM) section")
     ap.add_argument("--no-cells", action="store_true", help="skip the per-cell record")
     ap.add_argument("--cell-reps", type=int, default=10)
+    ap.add_argument("--fused-expert-only", action="store_true",
+                    help="run only the fused forward/backward at the expert layer's width (for profiling)")
     ap.add_argument("--supp-only", action="store_true",
                     help="run only the compute-bound supplementary GEMM shape (for profiling) and print it")
     ap.add_argument("--moe-only", action="store_true",
@@ -674,6 +708,9 @@ def main():
         return
     if args.supp_only:
         print(json.dumps({"gemm_supplementary": supplementary_gemm(m, torch)}), flush=True)
+        return
+    if args.fused_expert_only:
+        print(json.dumps({"fused_expert": fused_expert_section(m, torch, W)}), flush=True)
         return
     data = make_data(torch, W, [STRESS])
     cells = [Cell(m, torch, data, k, dn, dict(DIRS)[dn], sh, mo) for (k, dn, sh, mo) in STEP_CELLS]
