@@ -447,6 +447,10 @@ class KBlocked:
             raise ValueError("K-blocked operands need rows of a multiple of 64 bytes")
 
     @property
+    def device(self):
+        return self.data.device
+
+    @property
     def epp(self):
         """Elements per 64-byte plane row."""
         return 64 // self.data.element_size()
@@ -565,7 +569,7 @@ def grouped_gemm_swiglu(row_off, x, w13, out, scale=None, rowwise=True, colwise=
     dirs = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
     if n_col_blocks is None:
         n_col_blocks = colwise_scale_rows_bound(R, G)
-    rc, cc, rs, cs = _alloc_mx(R, I, dirs, n_col_blocks, x.device)
+    rc, cc, rs, cs = _alloc_mx(R, I, dirs, n_col_blocks, out.device)
     ro, co = _outs(rc, cc, rs, cs, dirs)
     args = mxq_gemm_args(GEMM_NT, G, row_off.data_ptr(), None if block_off is None else block_off.data_ptr(),
                          R, N, H, R, _operand(x), _operand(w13, None, group_dim=True), DTYPE_BF16, out.data_ptr(),

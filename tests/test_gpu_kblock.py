@@ -317,3 +317,46 @@ def test_srelu_kblock_equals_rowmajor(mxq, M, K):
         eq(got[i], ref[i], f"forward output {i}")
         eq(gb[i], rb[i], f"backward output {i}")
     eq(gb[4], rb[4], "dx")
+
+
+def test_gemm_fc1_shape_bf16_kblock(mxq):
+    """The expert layer's FC1 in bf16 (65,536 rows over 128 experts, N 1536,
+    K 2048) with the tokens and the weight K-blocked (32 elements per plane
+    row): the row-major bits."""
+    R, G, N, K = 65536, 128, 1536, 2048
+    ro, _ = offsets(mxq, [R // G] * G)
+    x = W._normal((R, K), 1.0, 10, 45, "cuda")
+    w = W._normal((G * N, K), 0.02, 11, 46, "cuda").view(G, N, K)
+    y1 = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    mxq.grouped_gemm(mxq.GEMM_NT, ro, x, w, y1)
+    mxq.grouped_gemm(mxq.GEMM_NT, ro, mxq.KBlocked.from_rowmajor(x), mxq.KBlocked.from_rowmajor(w), y2)
+    torch.cuda.synchronize()
+    eq(y2, y1, "FC1 bf16 K-blocked against row-major")
+
+
+@pytest.mark.parametrize("dirs", [1, 3])
+def test_fused_fc1_kblock_operands(mxq, dirs):
+    """FC1 with the SwiGLU + MXFP8 epilogue over K-blocked bf16 operands (the
+    epilogue's own outputs stay row-major): every output equals the
+    row-major launch's."""
+    splits = [33, 0, 260, 1, 96, 0, 300, 64]
+    G, H, I = len(splits), 256, 256
+    R = sum(splits)
+    ro, bo = offsets(mxq, splits)
+    x = W._normal((R, H), 1.0, 12, 47, "cuda")
+    w13 = mxq.interleave_rows(W._normal((G * 2 * I, H), 0.05, 13, 48, "cuda").view(G, 2 * I, H))
+    sc = W.row_scale(R, seed=12).cuda()
+    kw = dict(scale=sc, rowwise=True, colwise=bool(dirs & 2), block_off=bo)
+    h1 = torch.empty((R, 2 * I), dtype=torch.bfloat16, device="cuda")
+    h2 = torch.empty_like(h1)
+    ref = mxq.grouped_gemm_swiglu(ro, x, w13, h1, **kw)
+    got = mxq.grouped_gemm_swiglu(ro, mxq.KBlocked.from_rowmajor(x), mxq.KBlocked.from_rowmajor(w13), h2, **kw)
+    torch.cuda.synchronize()
+    eq(h2, h1, "bf16 product")
+    ncb = col_scale_rows(R, splits)
+    for i, what in ((0, "rowwise codes"), (2, "rowwise scales")):
+        eq(got[i], ref[i], what)
+    if dirs & 2:
+        eq(got[1], ref[1], "colwise codes")
+        eq(got[3][:ncb], ref[3][:ncb], "colwise scales")
