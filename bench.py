@@ -30,7 +30,10 @@ Outside the timed region, for the record:
     FC1 + activation unfused against fused; and (gemm.graph) the plain layer
     eager against a HIP-graph replay of the same step;
   * gemm_supplementary: a compute-bound grouped GEMM outside the workload
-    configurations, labelled as such;
+    configurations, labelled as such (row-major and K-blocked operands);
+  * fused_expert: the fused forward and backward at the expert layer's width
+    (65,536 rows of 768 columns in 128 groups, and 65,536 / 131,072 /
+    262,144 rows in one group), timed like per_cell;
   * clocks: the GPU's current sclk / mclk as rocm-smi reports them;
   * cpu_baseline: the CPU oracle on a bounded sample of the step's workload,
     on one host thread and on all of the process's host cores, and the
@@ -414,35 +417,66 @@ def supplementary_gemm(m, torch, reps=5):
     return res
 
 
-def fused_expert_section(m, torch, W, reps=3):
-    """The fused forward and backward (plain SwiGLU, both directions) at the
-    expert layer's width K = 768: 65,536 rows in 128 equal groups (the
-    layer's shape) and 65,536 / 131,072 / 262,144 rows in one group, each
-    twice untimed and `reps` times timed (three calls back to back per
-    timing).  Shows how the launch's fixed cost spreads as M grows."""
+def fused_expert_section(m, torch, W, reps=9):
+    """The fused forward and backward (plain SwiGLU, both directions, outputs
+    preallocated) at the expert layer's width K = 768: 65,536 rows in 128
+    equal groups (the layer's shape: the fused kernels of the configurations'
+    expert layer) and 65,536 / 131,072 / 262,144 rows in one group; each
+    call once untimed, then `reps` single calls timed like the per-cell
+    record (caches flushed before each; the flush also covers the host's
+    time to issue the call); medians and p10 / p90.  Shows how the launch's
+    fixed cost spreads as M grows."""
     K, out = 768, {}
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            e0.record(stream)
+            m.check(fn())
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return percentiles(ts)
+
+    act = m.make_act()
     for M, G in ((65536, 128), (65536, 0), (131072, 0), (262144, 0)):
         gu = W.packed_gate_up(M, K, seed=0, device="cuda")
         sc = W.row_scale(M, seed=0, device="cuda")
         dy = W.grad_out(M, K, seed=0, device="cuda")
-        kw = {}
+        g, u = gu[:, :K], gu[:, K:]
+        groups, ncb = None, (M + 31) // 32
         if G:
             ro, bo, _ = m.splits_to_offsets(torch.full((G,), M // G, dtype=torch.int64, device="cuda"))
-            kw = dict(row_off=ro, block_off=bo)
-        g, u = gu[:, :K], gu[:, K:]
-        fwd = lambda: m.swiglu_quantize_fwd(g, u, sc, rowwise=True, colwise=True, **kw)
-        bwd = lambda: m.swiglu_quantize_bwd(dy, g, u, sc, rowwise=True, colwise=True, **kw)
-        for fn in (fwd, bwd, fwd, bwd):
-            fn()
+            groups, ncb = m.make_groups(ro, bo), m.colwise_scale_rows_bound(M, G)
+        fo = m._alloc_mx(M, K, 3, ncb, "cuda")
+        f_row, f_col = m._outs(*fo, 3)
+        bo_ = m._alloc_mx(M, 2 * K, 3, ncb, "cuda")
+        b_row, b_col = m._outs(*bo_, 3)
+        dd = torch.empty((M, 2 * K), dtype=torch.bfloat16, device="cuda")
+        ds = torch.empty(M, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(m.mxq_swiglu_quantize_bwd_workspace(M, K, 3), 1), dtype=torch.uint8, device="cuda")
+        fwd = lambda: m.mxq_swiglu_quantize_fwd(act, g, u, sc, groups, 3, f_row, f_col)
+        bwd = lambda: m.mxq_swiglu_quantize_bwd(act, dy, g, u, sc, groups, dd[:, :K], dd[:, K:], ds, 3, b_row, b_col,
+                                                ws)
+        m.check(fwd())
+        m.check(bwd())
         torch.cuda.synchronize()
-        tf, tb = timed_alt(torch, [fwd, bwd], reps, inner=3)
+        (f10, f50, f90), (b10, b50, b90) = timed(fwd), timed(bwd)
         bf = M * K * (4 + 2 * (1 + 1 / 32)) + 4 * M
         bb = M * K * (10 + 4 * (1 + 1 / 32)) + 8 * M
         out[f"{M}x{K}" + (f"_G{G}" if G else "")] = {
-            "fwd_both_us": round(tf, 1), "fwd_pct_hbm": round(bf / tf / 1e3 / HBM_PEAK_GBS * 100, 1),
-            "bwd_both_us": round(tb, 1), "bwd_pct_hbm": round(bb / tb / 1e3 / HBM_PEAK_GBS * 100, 1)}
-        del gu, dy
+            "fwd_both_us": round(f50, 1), "fwd_p10_us": round(f10, 1), "fwd_p90_us": round(f90, 1),
+            "fwd_pct_hbm": round(bf / f50 / 1e3 / HBM_PEAK_GBS * 100, 1),
+            "bwd_both_us": round(b50, 1), "bwd_p10_us": round(b10, 1), "bwd_p90_us": round(b90, 1),
+            "bwd_pct_hbm": round(bb / b50 / 1e3 / HBM_PEAK_GBS * 100, 1)}
+        del gu, dy, fo, bo_, dd, ds, ws
         torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
     return out
 
 
@@ -807,6 +841,7 @@ def main():
         out["gemm"] = moe_section(m, torch, W)
         out["gemm"]["graph"] = graph_section(torch, W)
         out["gemm_supplementary"] = supplementary_gemm(m, torch)
+        out["fused_expert"] = fused_expert_section(m, torch, W)
         print("bench: grouped GEMM record done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

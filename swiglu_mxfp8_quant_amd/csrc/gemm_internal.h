@@ -17,7 +17,7 @@ struct GemmOperand {
     int64_t ld, gstride;
     const uint8_t *scales;
     int64_t ld_scales, scale_gstride;
-    int64_t plane;          // 0: row-major; > 0: K-blocked MXFP8 codes, bytes between 64-byte planes
+    int64_t plane;          // 0: row-major; > 0: K-blocked (either dtype), bytes between 64-byte planes
 };
 
 struct GemmArgs {
