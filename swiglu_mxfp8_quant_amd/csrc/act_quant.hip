@@ -156,6 +156,25 @@ __device__ __forceinline__ int64_t xcd_item(int64_t bid, int64_t grid) {
 
 inline int64_t xcd_grid(int64_t nwork) { return (nwork + kXCD - 1) / kXCD * kXCD; }
 
+// The work item of block `bid`, or -1 for none.  A grouped colwise launch is
+// sized for the bound on its 32-row blocks (one partial block per group on top
+// of M / 32), but only block_off[G] of them exist: the items are spread over
+// the XCDs by that count, so that the blocks left over are a few on every XCD
+// rather than all on the last one, which would otherwise run the longest.
+__device__ __forceinline__ int64_t work_item(int64_t bid, int64_t grid, int64_t nwork, int64_t nslabs,
+                                             const Groups &gr, bool grouped) {
+    if (!grouped) {
+        const int64_t it = xcd_item(bid, grid);
+        return it < nwork ? it : -1;
+    }
+    int64_t tiles = gr.block_off[gr.G];
+    const int64_t bound = nwork / nslabs;
+    tiles = tiles < 0 ? 0 : (tiles > bound ? bound : tiles);
+    const int64_t n = tiles * nslabs, share = (n + kXCD - 1) / kXCD, i = bid / kXCD;
+    const int64_t it = (bid % kXCD) * share + i;
+    return (i < share && it < n) ? it : -1;
+}
+
 struct Tile {
     int64_t r0;    // first row
     int n;         // rows present (0 => nothing to do)
@@ -364,8 +383,9 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
     constexpr int SLAB = 64 * CPT, NWORDS = risk_words<RPW, CPT>();
     __shared__ uint2 fq[kQ + 1][FNT];  // slot kQ takes the writes of lanes whose queue is full
     __shared__ uint32_t cmx[NWAVE][64][CPT / 2];
-    const int64_t item = xcd_item(blockIdx.x, gridDim.x);
-    if (item >= nwork) return;  // grid padding (uniform over the workgroup)
+    const bool grouped = (DIRS & 2) && a.groups.G > 0;
+    const int64_t item = work_item(blockIdx.x, gridDim.x, nwork, nslabs, a.groups, grouped);
+    if (item < 0) return;  // grid padding (uniform over the workgroup)
     if (a.noop != nullptr && *a.noop != 0) return;  // a cached output that is still valid (uniform)
     const int64_t t = item / nslabs;
     const int64_t slab = item - t * nslabs;
@@ -377,7 +397,7 @@ __global__ void __launch_bounds__(FNT) fwd_kernel(FwdArgs a, int64_t nslabs, int
     // interleaved in blocks of il columns (il a multiple of 32, so a lane's 8
     // columns stay in one block), logical column j sits at 2 il (j / il) + j % il
     const int gco = a.il ? (co / a.il) * 2 * a.il + co % a.il : co;
-    const Tile T = tile_rows<TROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
+    const Tile T = tile_rows<TROWS>(t, a.M, a.groups, grouped);
     if (T.n == 0) return;  // uniform over the workgroup
     const int nrow = min(max(T.n - wave * RPW, 0), RPW);  // rows of this wave (uniform per wave)
     const int64_t rbase = T.r0 + wave * RPW;
@@ -725,8 +745,9 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
     __shared__ uint32_t cmx[2][BNWAVE][64][CPT / 2];
     __shared__ float red[TROWS][65];
     __shared__ float red2[TROWS][9];
-    const int64_t item = xcd_item(blockIdx.x, gridDim.x);
-    if (item >= nwork) return;  // grid padding (uniform over the workgroup)
+    const bool grouped = (DIRS & 2) && a.groups.G > 0;
+    const int64_t item = work_item(blockIdx.x, gridDim.x, nwork, nslabs, a.groups, grouped);
+    if (item < 0) return;  // grid padding (uniform over the workgroup)
     const int64_t t = item / nslabs;
     const int64_t slab = item - t * nslabs;
     const int tid = threadIdx.x;
@@ -735,7 +756,7 @@ __global__ void __launch_bounds__(BNT) bwd_kernel(BwdArgs a, int64_t nslabs, int
     const bool active = co < a.K;
     const int gco = a.il ? (co / a.il) * 2 * a.il + co % a.il : co;   // gate / up / dgate / dup column
     const int uoff = a.il ? a.il : (int)a.K;   // dup's columns of the MXFP8 [dgate | dup] lie this far on
-    const Tile T = tile_rows<TROWS>(t, a.M, a.groups, (DIRS & 2) && a.groups.G > 0);
+    const Tile T = tile_rows<TROWS>(t, a.M, a.groups, grouped);
     if (T.n == 0) return;
     const int nrow = min(max(T.n - wave * BRPW, 0), BRPW);
     const int64_t rbase = T.r0 + wave * BRPW;
