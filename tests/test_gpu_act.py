@@ -376,6 +376,28 @@ def test_backward_grouped_both(mxq):
     run_bwd_and_compare(mxq, gu, sc, dy, 128, 3, False, splits=splits)
 
 
+@pytest.mark.parametrize("kind", ["whole_blocks", "ragged"])
+def test_grouped_many_groups_three_slabs(mxq, kind):
+    """A grouped launch is sized for the bound M / 32 + G on its 32-row blocks,
+    and only block_off[G] of them exist; its work items are spread over the
+    XCDs by that count.  96 groups of 64 rows (96 of the 288 bound blocks
+    idle, 3 column slabs each at K = 768) and a ragged mix with empty groups:
+    every block must be computed once, forward and backward."""
+    rng = np.random.default_rng(21)
+    if kind == "whole_blocks":
+        splits = [64] * 96
+    else:
+        splits = [int(v) for v in rng.integers(0, 100, 96)]
+        for i in rng.integers(0, 96, 12):
+            splits[int(i)] = 0
+    M, K = sum(splits), 768
+    gu = W.packed_gate_up(M, K, seed=21)
+    sc = W.row_scale(M, seed=21)
+    dy = W.grad_out(M, K, seed=21)
+    run_fwd_and_compare(mxq, gu, sc, K, 3, False, splits=splits)
+    run_bwd_and_compare(mxq, gu, sc, dy, K, 3, False, splits=splits)
+
+
 def test_backward_dscale_only_and_quant_only(mxq):
     gu = W.packed_gate_up(64, 128, seed=16)
     sc = W.row_scale(64, seed=16)
